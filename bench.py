@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of multi-row verify attention over a paged E4M3 KV cache.
+
+One step = one verify call (split partials) + one combine call on the
+headline workload: q8 rows, 6 query heads over 1 KV head, head dim 256,
+E4M3 pages, context 262144 in 3456-token pages, rows 5-7 zero-length, NaN
+null page padding the table (the largest configuration of the 8K-256K range
+the metric is quoted on).  The KV pool is replicated in device memory and the
+steps rotate through the copies, so every call reads K/V from HBM rather than
+from the 256 MB Infinity Cache ("cold"); the same loop on one copy ("hot",
+identical inputs back to back) is reported beside it, with the other contexts
+of the range (8K, 64K, 128K).
+
+Throughput counts algorithmic bytes only: the longest visible prefix x 512 B
+(K and V, one KV head, D = 256, one byte per element).  The verify kernel's own
+duration comes from HIP events around each verify launch on the stream it runs
+on; roofline.achieved = algorithmic bytes / that duration.  The FP64 CPU oracle
+is timed on the host's cores on the same workload as a reported baseline.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and KV-read GB/s (% HBM peak), q8 H6/Hkv1/D256 E4M3, 8K–256K ctx"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 << 20         # Infinity Cache
+PMC_FILE = os.path.join(ROOT, "profiles", "verify_kernel_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "fp8_kv_paged_attn_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class DenseBench:
+    """A dense workload resident on the device, with n_copies of its KV pool."""
+
+    def __init__(self, w, n_copies: int, kernel: str, splits: int):
+        import numpy as np
+        import torch
+
+        import fp8_kv_paged_attn_amd as pa
+
+        self.w, self.pa, self.torch = w, pa, torch
+        dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(np.ascontiguousarray(w.q_bits).view(np.int16)).view(
+            torch.float16).to(dev)
+        k = torch.from_numpy(w.k_pool).to(dev)
+        v = torch.from_numpy(w.v_pool).to(dev)
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
+        self.table = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
+        self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
+        G = w.num_heads // w.num_kv_heads
+        s = splits if splits else w.num_splits
+        self.plan = pa.plan(w.max_tokens, w.q_rows * G, w.num_kv_heads, w.head_dim, splits=s,
+                            kernel=kernel)
+        self.rows = w.q_rows * w.num_heads
+        self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
+        self.out = torch.empty((w.q_rows, w.num_heads, w.head_dim), dtype=torch.float16,
+                               device=dev)
+        self.kv_bytes = w.kv_bytes()
+        self.pool_bytes = 2 * k.numel()
+
+    def verify(self, i: int):
+        k, v = self.pools[i % len(self.pools)]
+        w = self.w
+        self.pa.paged_attn_verify_e4m3(self.q, k, v, self.table, self.lens, w.max_tokens,
+                                       w.sm_scale, w.k_scale, self.plan, self.ws)
+
+    def combine(self):
+        self.pa.paged_attn_combine_fp32(self.ws, self.plan.num_splits, self.rows,
+                                        self.w.head_dim, self.w.v_scale, self.out)
+
+    def run(self, steps: int, warmup: int, rotate: bool):
+        """Time `steps` calls; returns (ms per call, mean verify-kernel ms)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.verify(i if rotate else 0)
+            self.combine()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            ev[i][0].record()
+            self.verify(i if rotate else 0)
+            ev[i][1].record()
+            self.combine()
+        t1.record()
+        torch.cuda.synchronize()
+        total_ms = t0.elapsed_time(t1)
+        vk = [a.elapsed_time(b) for a, b in ev]
+        return total_ms / steps, statistics.fmean(vk), statistics.median(vk)
+
+
+def copies_for(pool_bytes: int) -> int:
+    """Enough pool copies that one rotation exceeds twice the Infinity Cache."""
+    return max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
+
+
+def cpu_baseline(w, max_seconds: float = 20.0):
+    import oracle
+
+    orc = oracle.get()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 and (time.perf_counter() - t_start) < max_seconds:
+        t0 = time.perf_counter()
+        orc.dense_workload(w, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(w.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {w.name} workload (all {w.q_rows} rows x {w.num_heads} heads), "
+                      f"FP64 oracle on {threads} threads, median of {len(times)} runs, "
+                      f"{t * 1e3:.1f} ms per call"}
+
+
+def traffic_from_profile(src_hash: str, workload: str):
+    """HBM bytes per verify launch from the committed rocprofv3 counter runs,
+    or None when they were taken on another kernel source or workload."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != src_hash or d.get("workload") != workload:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the verify path is "
+                                   "measured on a single MI355X (--gpus 1)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import fp8_kv_paged_attn_amd as pa
+    from fp8_kv_paged_attn_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a ROCm GPU (cuda:0)")
+    pa.lib()
+    src_hash = kernel_source_hash()
+
+    log(f"[bench] generating {args.workload}")
+    w = wl.cached(args.workload)
+    n_copies = copies_for(2 * w.k_pool.size)
+    log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
+    b = DenseBench(w, n_copies, args.kernel, args.splits)
+    ms, vk_mean, vk_med = b.run(args.steps, args.warmup, rotate=True)
+    log(f"[bench] cold: {ms * 1e3:.2f} us/call, verify {vk_mean * 1e3:.2f} us")
+    ms_hot, vk_hot, _ = b.run(args.steps, args.warmup, rotate=False)
+    log(f"[bench] hot: {ms_hot * 1e3:.2f} us/call, verify {vk_hot * 1e3:.2f} us")
+    gbs = b.kv_bytes / (ms * 1e-3) / 1e9
+    achieved = b.kv_bytes / (vk_mean * 1e-3) / 1e9
+    plan = b.plan
+    del b
+    torch.cuda.empty_cache()
+
+    sweep = []
+    if not args.no_sweep:
+        for name in ["c1", "c2_64k", "c2_128k"]:
+            log(f"[bench] sweep {name}")
+            ws = wl.cached(name)
+            bs = DenseBench(ws, copies_for(2 * ws.k_pool.size), args.kernel, 0)
+            steps = max(20, args.steps // 2)
+            c_ms, c_vk, _ = bs.run(steps, args.warmup, rotate=True)
+            h_ms, h_vk, _ = bs.run(steps, args.warmup, rotate=False)
+            sweep.append({"workload": ws.name, "ctx": ws.max_tokens, "kv_bytes": bs.kv_bytes,
+                          "splits": bs.plan.num_splits, "us_per_call": round(c_ms * 1e3, 3),
+                          "verify_us": round(c_vk * 1e3, 3),
+                          "gbs": round(bs.kv_bytes / (c_ms * 1e-3) / 1e9, 1),
+                          "verify_gbs": round(bs.kv_bytes / (c_vk * 1e-3) / 1e9, 1),
+                          "hot_us_per_call": round(h_ms * 1e3, 3),
+                          "hot_gbs": round(bs.kv_bytes / (h_ms * 1e-3) / 1e9, 1)})
+            del bs
+            torch.cuda.empty_cache()
+        sweep.append({"workload": w.name, "ctx": w.max_tokens, "kv_bytes": w.kv_bytes(),
+                      "splits": plan.num_splits, "us_per_call": round(ms * 1e3, 3),
+                      "verify_us": round(vk_mean * 1e3, 3), "gbs": round(gbs, 1),
+                      "verify_gbs": round(achieved, 1),
+                      "hot_us_per_call": round(ms_hot * 1e3, 3),
+                      "hot_gbs": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 1)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(w)
+
+    kernel_name = {0: "auto", 1: "simple", 2: "mfma"}[plan.kernel]
+    traffic = traffic_from_profile(src_hash, w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if kernel_name != "simple" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "q_rows": w.q_rows, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "ctx": w.max_tokens, "page_size": w.page_size, "kv_bytes": w.kv_bytes(),
+                   "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
+                   "kernel": kernel_name, "cache": f"cold: {n_copies} rotating pool copies",
+                   "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "hot": {"us_per_call": round(ms_hot * 1e3, 3),
+                "value": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 2),
+                "verify_us": round(vk_hot * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "verify", "verify_us": round(vk_mean * 1e3, 3),
+                     "verify_us_median": round(vk_med * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "source_hash": src_hash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

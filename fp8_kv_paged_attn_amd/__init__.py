@@ -1,0 +1,294 @@
+"""Multi-row verify attention over a paged FP8-E4M3 KV cache, for MI355X.
+
+Thin ctypes binding over ``libpaged_attn_e4m3.so`` (HIP, gfx950), whose C ABI
+is ``include/paged_attn_e4m3.h``.  This module only checks devices and dtypes
+and marshals pointers; every step of the computation runs in the library's
+kernels.  PyTorch provides device memory and the current stream.  There is no
+CPU fallback: without the built library every call raises.
+
+Entry points (same names as the C ABI):
+  plan(...)                      split planner (pure host)
+  paged_attn_verify_e4m3(...)    dense verify, writes FP32 split partials
+  paged_attn_combine_fp32(...)   merges partials into FP16 rows
+  qsa_sparse_verify_e4m3(...)    sparse verify over selected blocks
+and the conveniences ``verify`` and ``qsa_verify`` (verify + combine).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn_e4m3.so")
+ABI_VERSION = 1
+
+PA_KERNEL = {"auto": 0, "simple": 1, "mfma": 2}
+LOG2E = 1.4426950408889634
+
+
+class PaKvPool(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("page_stride", ctypes.c_int64), ("token_stride", ctypes.c_int64),
+                ("head_stride", ctypes.c_int64), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32)]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("tokens_per_split", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("rows_per_kv_unit", ctypes.c_int32), ("num_kv_units", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ws_acc_bytes", ctypes.c_int64),
+                ("ws_stat_bytes", ctypes.c_int64)]
+
+    def __repr__(self):
+        return (f"PaPlan(splits={self.num_splits}, tokens_per_split={self.tokens_per_split}, "
+                f"kernel={self.kernel}, max_tokens={self.max_tokens}, "
+                f"rows={self.rows_per_kv_unit}, units={self.num_kv_units})")
+
+
+class PaWorkspace(ctypes.Structure):
+    _fields_ = [("acc", ctypes.c_void_p), ("max", ctypes.c_void_p), ("sum", ctypes.c_void_p),
+                ("acc_bytes", ctypes.c_int64), ("stat_bytes", ctypes.c_int64)]
+
+
+EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
+           "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3")
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it was not built or has another ABI revision."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m fp8_kv_paged_attn_amd.build` (there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, p, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    L.paged_attn_abi_version.argtypes = []
+    L.paged_attn_abi_version.restype = i32
+    L.paged_attn_status_string.argtypes = [i32]
+    L.paged_attn_status_string.restype = ctypes.c_char_p
+    L.paged_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PaPlan)]
+    L.paged_attn_plan.restype = i32
+    L.paged_attn_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, i32, i32,
+                                         i32, i32, f32, f32, ctypes.POINTER(PaPlan),
+                                         ctypes.POINTER(PaWorkspace), p]
+    L.paged_attn_verify_e4m3.restype = i32
+    L.paged_attn_combine_fp32.argtypes = [p, p, p, i32, i32, i32, f32, p, p]
+    L.paged_attn_combine_fp32.restype = i32
+    L.qsa_sparse_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, p, i32,
+                                         i32, i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
+                                         ctypes.POINTER(PaWorkspace), p]
+    L.qsa_sparse_verify_e4m3.restype = i32
+    ver = L.paged_attn_abi_version()
+    if ver != ABI_VERSION:
+        raise RuntimeError(f"libpaged_attn_e4m3 ABI revision {ver}, this binding needs "
+                           f"{ABI_VERSION}: rebuild the library")
+    _LIB = L
+    return L
+
+
+def status_string(rc: int) -> str:
+    return lib().paged_attn_status_string(int(rc)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what} failed: {status_string(rc)} ({rc})")
+
+
+def plan(max_tokens: int, rows_per_kv_unit: int, num_kv_units: int, head_dim: int,
+         num_cus: int = 0, splits: int = 0, kernel: str = "auto") -> PaPlan:
+    """Split plan (pure host integer arithmetic in the library)."""
+    out = PaPlan()
+    _check(lib().paged_attn_plan(int(max_tokens), int(rows_per_kv_unit), int(num_kv_units),
+                                 int(head_dim), int(num_cus), int(splits), ctypes.byref(out)),
+           "paged_attn_plan")
+    out.kernel = PA_KERNEL[kernel]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Tensor marshalling
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _scale(x, device, name: str) -> float:
+    """Scales are host scalars.  A one-element tensor is accepted only on the
+    query's device (vLLM PR "Qwen4Exp: fp8_e4m3 main KV cache on the QSA path",
+    CodeRabbit finding) and is read once on the host."""
+    torch = _torch()
+    if isinstance(x, torch.Tensor):
+        if x.numel() != 1:
+            raise ValueError(f"{name} must have one element")
+        if x.device != device:
+            raise ValueError(f"{name} is on {x.device}, the query is on {device}")
+        x = x.item()
+    x = float(x)
+    if not math.isfinite(x):
+        raise ValueError(f"{name} must be finite")
+    return x
+
+
+def _pool(k_pool, v_pool, device) -> PaKvPool:
+    torch = _torch()
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must hold E4M3 bytes (uint8 or float8_e4m3fn)")
+        if t.device != device:
+            raise ValueError(f"{n} is on {t.device}, the query is on {device}")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{n} must be [pages][page_size][kv_heads][head_dim], head_dim contiguous")
+    if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same shape and strides")
+    return PaKvPool(k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.stride(1),
+                    k_pool.stride(2), k_pool.shape[0], k_pool.shape[1])
+
+
+def _i32(t, name: str, device):
+    torch = _torch()
+    if t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor on {device}")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def make_workspace(p: PaPlan, total_rows: int, head_dim: int, device):
+    torch = _torch()
+    acc = torch.empty((p.num_splits, total_rows, head_dim), dtype=torch.float32, device=device)
+    mx = torch.empty((p.num_splits, total_rows), dtype=torch.float32, device=device)
+    sm = torch.empty((p.num_splits, total_rows), dtype=torch.float32, device=device)
+    return acc, mx, sm
+
+
+def _ws(acc, mx, sm) -> PaWorkspace:
+    torch = _torch()
+    for t in (acc, mx, sm):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("workspace buffers must be contiguous float32")
+    return PaWorkspace(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
+                       acc.numel() * 4, min(mx.numel(), sm.numel()) * 4)
+
+
+def paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens: int,
+                           sm_scale, k_scale, p: PaPlan, ws) -> None:
+    """Dense verify of one request into the FP32 split workspace ws = (acc, max, sum)."""
+    torch = _torch()
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous float16 tensor [q_rows][heads][head_dim]")
+    dev = q.device
+    pool = _pool(k_pool, v_pool, dev)
+    qr, H, D = q.shape
+    if k_pool.shape[3] != D:
+        raise ValueError("head_dim of q and the pool differ")
+    rc = lib().paged_attn_verify_e4m3(
+        q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
+        block_table.numel(), _i32(row_lens, "row_lens", dev), int(max_tokens), qr, H,
+        k_pool.shape[2], D, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
+    _check(rc, "paged_attn_verify_e4m3")
+
+
+def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,
+                            out) -> None:
+    """FP32 combine of split partials into out (float16, [num_rows][head_dim] elements)."""
+    torch = _torch()
+    acc, mx, sm = ws
+    if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() < num_rows * head_dim:
+        raise ValueError("out must be a contiguous float16 tensor of num_rows*head_dim elements")
+    for t in (acc, mx, sm):
+        if t.device != out.device or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("workspace must be contiguous float32 on the output's device")
+    if acc.numel() < num_splits * num_rows * head_dim or min(mx.numel(), sm.numel()) < num_splits * num_rows:
+        raise ValueError("workspace smaller than num_splits x num_rows")
+    rc = lib().paged_attn_combine_fp32(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
+                                       int(num_splits), int(num_rows), int(head_dim),
+                                       _scale(out_scale, out.device, "out_scale"),
+                                       out.data_ptr(), _stream(out.device))
+    _check(rc, "paged_attn_combine_fp32")
+
+
+def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,
+                           k_scale, p: PaPlan, ws) -> None:
+    """Sparse verify of a batch over selected blocks into the FP32 split workspace."""
+    torch = _torch()
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous bfloat16 tensor [batch][q_rows][heads][head_dim]")
+    dev = q.device
+    pool = _pool(k_pool, v_pool, dev)
+    B, qr, H, D = q.shape
+    if k_pool.shape[3] != D:
+        raise ValueError("head_dim of q and the pool differ")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch][max_blocks]")
+    Hkv = k_pool.shape[2]
+    if sel_blocks.dim() != 3 or tuple(sel_blocks.shape[:2]) != (B, Hkv):
+        raise ValueError("sel_blocks must be [batch][kv_heads][topk]")
+    if tuple(row_lens.shape) != (B, qr):
+        raise ValueError("row_lens must be [batch][q_rows]")
+    rc = lib().qsa_sparse_verify_e4m3(
+        q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
+        block_table.shape[1], _i32(sel_blocks, "sel_blocks", dev), sel_blocks.shape[2],
+        _i32(row_lens, "row_lens", dev), B, qr, H, Hkv, D, _scale(sm_scale, dev, "sm_scale"),
+        _scale(k_scale, dev, "k_scale"), ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
+    _check(rc, "qsa_sparse_verify_e4m3")
+
+
+# ---------------------------------------------------------------------------
+# Conveniences: verify + combine
+# ---------------------------------------------------------------------------
+
+
+def verify(q, k_pool, v_pool, block_table, row_lens, max_tokens: int, *, sm_scale, k_scale,
+           v_scale, splits: int = 0, kernel: str = "auto", p: Optional[PaPlan] = None,
+           ws: Optional[Tuple] = None, out=None):
+    """Dense verify of one request; returns FP16 [q_rows][heads][head_dim]."""
+    torch = _torch()
+    qr, H, D = q.shape
+    Hkv = k_pool.shape[2]
+    if p is None:
+        p = plan(max_tokens, qr * (H // Hkv), Hkv, D, splits=splits, kernel=kernel)
+    if ws is None:
+        ws = make_workspace(p, qr * H, D, q.device)
+    if out is None:
+        out = torch.empty((qr, H, D), dtype=torch.float16, device=q.device)
+    paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens, sm_scale,
+                           k_scale, p, ws)
+    paged_attn_combine_fp32(ws, p.num_splits, qr * H, D, v_scale, out)
+    return out
+
+
+def qsa_verify(q, k_pool, v_pool, block_table, sel_blocks, row_lens, *, sm_scale, k_scale,
+               v_scale, splits: int = 0, kernel: str = "auto", p: Optional[PaPlan] = None,
+               ws: Optional[Tuple] = None, out=None):
+    """Sparse verify of a batch; returns FP16 [batch][q_rows][heads][head_dim]."""
+    torch = _torch()
+    B, qr, H, D = q.shape
+    Hkv = k_pool.shape[2]
+    page = k_pool.shape[1]
+    if p is None:
+        p = plan(sel_blocks.shape[2] * page, qr * (H // Hkv), B * Hkv, D, splits=splits,
+                 kernel=kernel)
+    if ws is None:
+        ws = make_workspace(p, B * qr * H, D, q.device)
+    if out is None:
+        out = torch.empty((B, qr, H, D), dtype=torch.float16, device=q.device)
+    qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,
+                           k_scale, p, ws)
+    paged_attn_combine_fp32(ws, p.num_splits, B * qr * H, D, v_scale, out)
+    return out

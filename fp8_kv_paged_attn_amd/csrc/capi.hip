@@ -1,0 +1,356 @@
+// capi.hip - the C ABI of libpaged_attn_e4m3: argument checks, the split
+// planner and kernel dispatch.  Host code only; the kernels live in the other
+// sources of this directory.
+//
+// Every check here runs before anything is enqueued, so a rejected call
+// leaves the stream untouched (design note "DFlash2 E4M3 attention with FP32
+// state": an incompatible call raises instead of silently using another
+// precision; vLLM PR "Qwen4Exp: fp8_e4m3 main KV cache on the QSA path",
+// CodeRabbit finding: scales are validated before the launch).
+#include "paged_attn_e4m3.h"
+#include "pa_internal.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+namespace {
+
+constexpr int kTileTokens = 64;
+constexpr int kMaxRowsPerUnit = 48;
+constexpr int kMaxQRows = 8;
+constexpr int kDefaultCUs = 256;
+// Fewest tokens a split should read, so that the FP32 partial it writes
+// (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.
+constexpr int kMinTokensPerSplit = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned16(int64_t v) { return (v & 15) == 0; }
+
+// Per-device record: 0 unknown, 1 gfx950, -1 something else.
+std::atomic<int> g_device_ok[64];
+
+int32_t check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return PA_EDEVICE;
+    if (dev < 64) {
+        int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0)
+            return known > 0 ? PA_OK : PA_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return PA_EDEVICE;
+    bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64)
+        g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? PA_OK : PA_EDEVICE;
+}
+
+int32_t check_pool(const pa_kv_pool *kv)
+{
+    if (!kv || !kv->k_pool || !kv->v_pool)
+        return PA_EINVAL;
+    if (kv->page_size < 1 || kv->num_pages < 1 || kv->page_stride < 0 || kv->token_stride < 0 ||
+        kv->head_stride < 0)
+        return PA_EINVAL;
+    if (!aligned16(kv->k_pool) || !aligned16(kv->v_pool) || !aligned16(kv->page_stride) ||
+        !aligned16(kv->token_stride) || !aligned16(kv->head_stride))
+        return PA_EALIGN;
+    return PA_OK;
+}
+
+int32_t check_shape(int32_t q_rows, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t *rows_per_unit)
+{
+    if (q_rows < 1 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0)
+        return PA_EINVAL;
+    if (q_rows > kMaxQRows)
+        return PA_EUNSUPPORTED;
+    if (head_dim != 128 && head_dim != 256)
+        return PA_EUNSUPPORTED;
+    int64_t rows = (int64_t)q_rows * (num_heads / num_kv_heads);
+    if (rows > kMaxRowsPerUnit)
+        return PA_EUNSUPPORTED;
+    *rows_per_unit = (int32_t)rows;
+    return PA_OK;
+}
+
+int32_t check_scales(float sm_scale, float k_scale)
+{
+    if (!std::isfinite(sm_scale) || !std::isfinite(k_scale) || !(k_scale > 0.0f))
+        return PA_EINVAL;
+    return PA_OK;
+}
+
+int32_t check_plan(const pa_plan *plan, int32_t list_len, int32_t rows_per_unit,
+                   int32_t units, int32_t head_dim)
+{
+    if (!plan)
+        return PA_EINVAL;
+    if (plan->max_tokens != list_len || plan->rows_per_kv_unit != rows_per_unit ||
+        plan->num_kv_units != units || plan->head_dim != head_dim)
+        return PA_EPLAN;
+    if (plan->num_splits < 1 || plan->tokens_per_split < kTileTokens ||
+        plan->tokens_per_split % kTileTokens != 0 || plan->num_splits > 65535)
+        return PA_EPLAN;
+    if ((int64_t)plan->num_splits * plan->tokens_per_split < (int64_t)list_len)
+        return PA_EPLAN;
+    if (plan->kernel < PA_KERNEL_AUTO || plan->kernel > PA_KERNEL_MFMA)
+        return PA_EPLAN;
+    return PA_OK;
+}
+
+int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows,
+                 int32_t head_dim)
+{
+    if (!ws || !ws->acc || !ws->max || !ws->sum)
+        return PA_EINVAL;
+    int64_t need_acc = (int64_t)plan->num_splits * total_rows * head_dim * 4;
+    int64_t need_stat = (int64_t)plan->num_splits * total_rows * 4;
+    if (ws->acc_bytes < need_acc || ws->stat_bytes < need_stat)
+        return PA_EWORKSPACE;
+    return PA_OK;
+}
+
+int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim, bool sparse,
+                 hipStream_t stream)
+{
+    int32_t rc = check_device();
+    if (rc != PA_OK)
+        return rc;
+    hipError_t err;
+    switch (plan->kernel) {
+    case PA_KERNEL_SIMPLE:
+        err = pa::launch_verify_simple(a, head_dim, sparse, stream);
+        break;
+    case PA_KERNEL_MFMA:
+        err = pa::launch_verify_mfma(a, head_dim, sparse, stream);
+        if (err == hipErrorNotSupported)
+            return PA_EUNSUPPORTED;
+        break;
+    default:
+        err = pa::launch_verify_mfma(a, head_dim, sparse, stream);
+        if (err == hipErrorNotSupported)
+            err = pa::launch_verify_simple(a, head_dim, sparse, stream);
+        break;
+    }
+    return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t paged_attn_abi_version(void) { return PA_ABI_VERSION; }
+
+const char *paged_attn_status_string(int32_t status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument (null pointer, shape, count or scale)";
+    case PA_EUNSUPPORTED: return "unsupported shape (head_dim, query rows or rows per KV head)";
+    case PA_EWORKSPACE: return "workspace smaller than the plan requires";
+    case PA_EALIGN: return "pointer or stride not 16-byte aligned";
+    case PA_EDEVICE: return "no usable gfx950 device";
+    case PA_EHIP: return "HIP launch failed";
+    case PA_EPLAN: return "plan does not match this call";
+    default: return "unknown status";
+    }
+}
+
+int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
+                        int32_t head_dim, int32_t num_cus, int32_t requested_splits,
+                        pa_plan *out)
+{
+    if (!out || max_tokens < 0 || rows_per_kv_unit < 1 || num_kv_units < 1 || head_dim < 1 ||
+        requested_splits < 0)
+        return PA_EINVAL;
+    const int64_t cus = num_cus > 0 ? num_cus : kDefaultCUs;
+    const int64_t tiles = max_tokens > 0 ? (max_tokens + kTileTokens - 1) / kTileTokens : 1;
+    int64_t splits;
+    if (requested_splits > 0) {
+        splits = requested_splits;
+    } else {
+        // one workgroup per compute unit over all units ...
+        splits = (cus + num_kv_units - 1) / num_kv_units;
+        // ... but no split shorter than kMinTokensPerSplit tokens
+        int64_t cap = ((int64_t)max_tokens + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
+        if (cap < 1)
+            cap = 1;
+        if (splits > cap)
+            splits = cap;
+    }
+    if (splits > tiles)
+        splits = tiles;
+    if (splits > 65535)
+        splits = 65535;
+    const int64_t tiles_per_split = (tiles + splits - 1) / splits;
+    const int64_t tps = tiles_per_split * kTileTokens;
+    splits = max_tokens > 0 ? ((int64_t)max_tokens + tps - 1) / tps : 1;
+    const int64_t rows = (int64_t)rows_per_kv_unit * num_kv_units;
+    std::memset(out, 0, sizeof *out);
+    out->num_splits = (int32_t)splits;
+    out->tokens_per_split = (int32_t)tps;
+    out->kernel = PA_KERNEL_AUTO;
+    out->max_tokens = max_tokens;
+    out->rows_per_kv_unit = rows_per_kv_unit;
+    out->num_kv_units = num_kv_units;
+    out->head_dim = head_dim;
+    out->ws_acc_bytes = splits * rows * head_dim * 4;
+    out->ws_stat_bytes = splits * rows * 4;
+    return PA_OK;
+}
+
+int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                               const int32_t *block_table, int32_t num_table_entries,
+                               const int32_t *row_lens, int32_t max_tokens, int32_t q_rows,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float sm_scale, float k_scale, const pa_plan *plan,
+                               const pa_workspace *ws, void *stream)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!q_fp16 || !block_table || !row_lens)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
+        return rc;
+    if (!aligned16(q_fp16))
+        return PA_EALIGN;
+    if (num_table_entries < 0 || max_tokens < 0 ||
+        (int64_t)max_tokens > (int64_t)num_table_entries * kv->page_size)
+        return PA_EINVAL;
+    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
+        return rc;
+    if ((rc = check_plan(plan, max_tokens, rows_per_unit, num_kv_heads, head_dim)) != PA_OK)
+        return rc;
+    const int64_t total_rows = (int64_t)q_rows * num_heads;
+    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
+        return rc;
+
+    pa::VerifyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q_fp16);
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.page_stride = kv->page_stride;
+    a.token_stride = kv->token_stride;
+    a.head_stride = kv->head_stride;
+    a.page_size = kv->page_size;
+    a.block_table = block_table;
+    a.table_stride = 0;
+    a.sel = nullptr;
+    a.topk = 0;
+    a.row_lens = row_lens;
+    a.len_cap = max_tokens;
+    a.list_len = max_tokens;
+    a.batch = 1;
+    a.q_rows = q_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.rows = rows_per_unit;
+    a.num_splits = plan->num_splits;
+    a.tokens_per_split = plan->tokens_per_split;
+    a.total_rows = (int32_t)total_rows;
+    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    a.ws_acc = ws->acc;
+    a.ws_max = ws->max;
+    a.ws_sum = ws->sum;
+    (void)kLog2e;
+    return dispatch(a, plan, head_dim, false, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,
+                                int32_t num_splits, int32_t num_rows, int32_t head_dim,
+                                float out_scale, void *out_fp16, void *stream)
+{
+    if (!ws_acc || !ws_max || !ws_sum || !out_fp16)
+        return PA_EINVAL;
+    if (num_splits < 1 || num_rows < 0 || head_dim < 1 || head_dim > 4096 ||
+        !std::isfinite(out_scale))
+        return PA_EINVAL;
+    if (num_rows > 0x7FFFFFFF / 2)
+        return PA_EINVAL;
+    int32_t rc = check_device();
+    if (rc != PA_OK)
+        return rc;
+    hipError_t err = pa::launch_combine(ws_acc, ws_max, ws_sum, num_splits, num_rows, head_dim,
+                                        out_scale, static_cast<uint16_t *>(out_fp16),
+                                        static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
+                               const int32_t *block_table, int32_t max_blocks_per_req,
+                               const int32_t *sel_blocks, int32_t topk,
+                               const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float sm_scale, float k_scale, const pa_plan *plan,
+                               const pa_workspace *ws, void *stream)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!q_bf16 || !block_table || !sel_blocks || !row_lens)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
+        return rc;
+    if (!aligned16(q_bf16))
+        return PA_EALIGN;
+    if (batch < 1 || max_blocks_per_req < 1 || topk < 1)
+        return PA_EINVAL;
+    const int64_t list_len = (int64_t)topk * kv->page_size;
+    const int64_t cap = (int64_t)max_blocks_per_req * kv->page_size;
+    if (list_len > 0x7FFFFFFF || cap > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((int64_t)batch * num_kv_heads > 65535)
+        return PA_EUNSUPPORTED;
+    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
+        return rc;
+    if ((rc = check_plan(plan, (int32_t)list_len, rows_per_unit, batch * num_kv_heads,
+                         head_dim)) != PA_OK)
+        return rc;
+    const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
+    if (total_rows > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
+        return rc;
+
+    pa::VerifyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q_bf16);
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.page_stride = kv->page_stride;
+    a.token_stride = kv->token_stride;
+    a.head_stride = kv->head_stride;
+    a.page_size = kv->page_size;
+    a.block_table = block_table;
+    a.table_stride = max_blocks_per_req;
+    a.sel = sel_blocks;
+    a.topk = topk;
+    a.row_lens = row_lens;
+    a.len_cap = (int32_t)cap;
+    a.list_len = (int32_t)list_len;
+    a.batch = batch;
+    a.q_rows = q_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.rows = rows_per_unit;
+    a.num_splits = plan->num_splits;
+    a.tokens_per_split = plan->tokens_per_split;
+    a.total_rows = (int32_t)total_rows;
+    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    a.ws_acc = ws->acc;
+    a.ws_max = ws->max;
+    a.ws_sum = ws->sum;
+    return dispatch(a, plan, head_dim, true, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -272,10 +272,13 @@ def make_dense(name: str, seed: int, *, q_rows: int, num_heads: int,
     k_pool = np.zeros(shape, np.uint8)
     v_pool = np.zeros(shape, np.uint8)
     if poison_unused:
-        junk = (uniform_u64(sj, 0, 2 * int(np.prod(shape))) >> np.uint64(56)).astype(np.uint8)
-        junk[::7] = E4M3_NAN
-        k_pool[...] = junk[: k_pool.size].reshape(shape)
-        v_pool[...] = junk[k_pool.size:].reshape(shape)
+        # random bytes (NaN codes included) in every page; real pages are
+        # overwritten below.  numpy's seeded PCG64 is enough for filler.
+        rng = np.random.Generator(np.random.PCG64(sj))
+        k_pool[...] = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        v_pool[...] = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        k_pool.reshape(-1)[::7] = E4M3_NAN
+        v_pool.reshape(-1)[::7] = E4M3_NAN
     outl = None
     if outlier_channels:
         outl = np.sort(permutation(so, head_dim)[:outlier_channels])
@@ -426,6 +429,16 @@ def tiny_dense(seed: int, **kw) -> DenseWorkload:
                 page_size=48, pool_pages=9, sigma=1.0, k_scale=0.75, v_scale=1.25)
     args.update(kw)
     return make_dense(f"tiny_dense_{seed:x}", seed, **args)
+
+
+_CACHE: Dict[str, object] = {}
+
+
+def cached(name: str):
+    """The named configuration, generated once per process."""
+    if name not in _CACHE:
+        _CACHE[name] = CONFIGS[name]()
+    return _CACHE[name]
 
 
 CONFIGS: Dict[str, object] = {

@@ -1,0 +1,208 @@
+/* paged_attn_e4m3.h - multi-row verify attention over a paged FP8-E4M3 KV
+ * cache, for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the library computes.  For a query row i of head h, whose KV head is
+ * g = h / (num_heads / num_kv_heads), and the tokens t that row sees:
+ *
+ *     s_t = sm_scale * k_scale * sum_d q[i][h][d] * K_t[g][d]
+ *     o[i][h][:] = v_scale * sum_t softmax(s)_t * V_t[g][:]
+ *
+ * with K_t and V_t the exact values of the E4M3 bytes stored for token t.
+ * Sources:
+ *   [DN]  1Cat-vLLM design note "DFlash2 E4M3 attention with FP32 state",
+ *         first section: single-request verification of q2-8 draft rows with
+ *         H6/Hkv1/D256 grouped heads over E4M3 pages, live per-query lengths
+ *         including zero padding, FP32 unnormalised partition numerators,
+ *         separate FP32 max/sum, FP32 combination, FP16 activations; page
+ *         size is a runtime stride, not a template ("revision 4" paragraph).
+ *   [QSA] vLLM PR "[Model] Qwen4Exp: fp8_e4m3 main KV cache on the QSA path":
+ *         the sparse split-K paged GQA kernel over selected blocks, which
+ *         dequantises E4M3 on load; k_scale folded into the softmax scale on
+ *         the host and v_scale used as the kernel's output scale (review
+ *         thread on host-side KV scales); scale validation before launch
+ *         (CodeRabbit finding).
+ *   [NB]  1Cat-vLLM PR "[Model] Qualify calibrated E4M3 and disk PLE with QSA
+ *         DCP2": rows that no query attends must not reach P.V even when the
+ *         null block decodes to NaN (commit fixing the grouped-page4 NaN);
+ *         strided (packed) page views read like unpacked ones.
+ *
+ * Conventions for every entry point:
+ *   - Buffers are device pointers unless marked (host).  The caller owns all
+ *     memory; the library never allocates, never frees, keeps no state
+ *     between calls except a per-device record of whether it is a gfx950,
+ *     never synchronises and never copies host memory to the device.  Work
+ *     is enqueued on `stream` (a hipStream_t; NULL = the null stream), so
+ *     calls can be captured into a HIP graph.
+ *   - A problem the host can see (null pointer, bad shape, misalignment, a
+ *     plan that does not fit the call, a workspace that is too small)
+ *     returns a negative status and enqueues nothing.  A failed kernel
+ *     launch returns PA_EHIP.  There is no fallback to another precision.
+ *   - Device-resident data is not inspected on the host.  Row lengths are
+ *     clamped on the device; block-table and selection entries must name
+ *     pages inside the pool (precondition; reading outside is undefined).
+ *   - Workspace buffers are reused by successive calls on one stream only.
+ *   - Calls are thread-safe.
+ */
+#ifndef PAGED_ATTN_E4M3_H
+#define PAGED_ATTN_E4M3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Revision of this interface.  A caller built against another revision must
+ * refuse the library rather than run it ([DN] revision gate: the wrapper
+ * requires the revision it was written for, so new workspace layouts never
+ * reach an older binary). */
+#define PA_ABI_VERSION 1
+
+enum pa_status {
+    PA_OK = 0,
+    PA_EINVAL = -1,        /* null pointer, bad shape or count, bad scale */
+    PA_EUNSUPPORTED = -2,  /* valid but not built: head_dim, rows per KV head */
+    PA_EWORKSPACE = -3,    /* workspace smaller than the plan needs */
+    PA_EALIGN = -4,        /* pointer or stride not 16-byte aligned */
+    PA_EDEVICE = -5,       /* no HIP device, or not gfx950 */
+    PA_EHIP = -6,          /* a HIP call or kernel launch failed */
+    PA_EPLAN = -7          /* plan does not cover this call */
+};
+
+/* PA_ABI_VERSION of the built library. */
+int32_t paged_attn_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *paged_attn_status_string(int32_t status);
+
+/* (host) Paged K/V pool.  Byte (page p, token u, KV head g, element d) of the
+ * K plane is k_pool[p*page_stride + u*token_stride + g*head_stride + d]; the
+ * V plane uses the same strides.  Elements of one head are contiguous.
+ * page_stride, token_stride, head_stride and both base pointers must be
+ * multiples of 16 bytes; any page_size >= 1 is accepted.  Strided views of a
+ * larger interleaved allocation ("packed pages") are ordinary pools here. */
+typedef struct pa_kv_pool {
+    const uint8_t *k_pool;
+    const uint8_t *v_pool;
+    int64_t page_stride;
+    int64_t token_stride;
+    int64_t head_stride;
+    int32_t num_pages;
+    int32_t page_size;
+} pa_kv_pool;
+
+/* Kernel choice carried by a plan (an A/B switch; both compute the same
+ * function, with different FP32 rounding). */
+enum pa_kernel {
+    PA_KERNEL_AUTO = 0,            /* MFMA kernel where it applies, else simple */
+    PA_KERNEL_SIMPLE = 1,          /* plain FP32 kernel (A/B baseline) */
+    PA_KERNEL_MFMA = 2             /* MFMA kernel; PA_EUNSUPPORTED where it does not apply */
+};
+
+/* (host) Split plan: the token axis of each KV unit (one KV head of one
+ * request) is cut into num_splits ranges of tokens_per_split tokens; range s
+ * is one workgroup.  Filled by paged_attn_plan; the other fields record what
+ * the plan was made for and are checked by the compute entry points. */
+typedef struct pa_plan {
+    int32_t num_splits;
+    int32_t tokens_per_split;      /* multiple of 64 */
+    int32_t kernel;                /* enum pa_kernel; paged_attn_plan sets PA_KERNEL_AUTO */
+    int32_t max_tokens;            /* tokens per KV unit the plan covers */
+    int32_t rows_per_kv_unit;      /* query rows x heads sharing one KV head */
+    int32_t num_kv_units;          /* KV heads x requests */
+    int32_t head_dim;
+    int64_t ws_acc_bytes;          /* FP32 [num_splits][rows][head_dim] */
+    int64_t ws_stat_bytes;         /* FP32 [num_splits][rows], each of max and sum */
+} pa_plan;
+
+/* (host) FP32 split workspace written by the verify entry points and read by
+ * paged_attn_combine_fp32.  Row r of split s holds, for the tokens of that
+ * split that the row sees ([DN]: FP32 unnormalised partition numerators with
+ * a separate FP32 max and sum), with y_t = s_t * log2(e):
+ *     max[s][r]    = m = max_t y_t            (-inf when the split is empty)
+ *     sum[s][r]    = l = sum_t 2^(y_t - m)    (0 when empty)
+ *     acc[s][r][d] = sum_t 2^(y_t - m) * V_t[g][d]   (0 when empty; no v_scale)
+ * Rows are numbered like the output, so the combine works row by row. */
+typedef struct pa_workspace {
+    float *acc;
+    float *max;
+    float *sum;
+    int64_t acc_bytes;             /* capacity of acc */
+    int64_t stat_bytes;            /* capacity of each of max and sum */
+} pa_workspace;
+
+/* (host, pure integer) Choose the split of max_tokens tokens for
+ * num_kv_units units of rows_per_kv_unit rows.  num_cus = compute units to
+ * fill (<= 0: 256, the MI355X count).  requested_splits > 0 forces the split
+ * count (clamped to what the token count allows); 0 picks one: enough
+ * workgroups to fill the device, balanced against the FP32 workspace each
+ * split writes (the pages tune split counts per device and region, [QSA]
+ * sm_120 retune commit).  Returns PA_EINVAL for non-positive sizes. */
+int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
+                        int32_t head_dim, int32_t num_cus, int32_t requested_splits,
+                        pa_plan *out);
+
+/* Dense verify of one request ([DN] first section), writing split partials.
+ *   q_fp16       [q_rows][num_heads][head_dim] FP16, contiguous, 16-byte aligned
+ *   kv           (host) the pool; head_dim bytes per token and head
+ *   block_table  [num_table_entries] int32: logical page -> physical page
+ *   row_lens     [q_rows] int32: row i sees tokens t < clamp(len_i, 0, max_tokens);
+ *                zero is allowed and gives an empty row
+ *   max_tokens   (host) bound on the lengths, <= num_table_entries*page_size;
+ *                must equal plan->max_tokens
+ *   q_rows 1..8; num_heads % num_kv_heads == 0; q_rows*num_heads/num_kv_heads
+ *   <= 48 rows per KV head; head_dim 128 or 256
+ *   sm_scale, k_scale (host) finite, k_scale > 0: the logit scale is
+ *                sm_scale*k_scale*log2(e), folded on the host ([QSA])
+ *   plan         (host) from paged_attn_plan(max_tokens, q_rows*num_heads/num_kv_heads,
+ *                num_kv_heads, head_dim, ...)
+ *   ws           (host) workspace of at least plan->ws_*_bytes
+ * Tokens a row does not see never reach P.V: their scores are replaced by
+ * -inf and their V rows by zero with selects, so NaN bytes in padding pages
+ * or page tails have no effect ([NB] null-block fix). */
+int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                               const int32_t *block_table, int32_t num_table_entries,
+                               const int32_t *row_lens, int32_t max_tokens, int32_t q_rows,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float sm_scale, float k_scale, const pa_plan *plan,
+                               const pa_workspace *ws, void *stream);
+
+/* FP32 combination of split partials into FP16 rows ([DN] first section):
+ *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),
+ *   out[r][d] = fp16_rne(out_scale * sum_s w_s acc[s][r][d] / sum_s w_s sum[s][r]),
+ * and out[r][:] = 0 when every split of row r is empty.  out_scale is the
+ * V dequantisation scale ([QSA] output scale).  ws_* as written by a verify
+ * call with num_splits splits and num_rows rows; out_fp16 [num_rows][head_dim]
+ * (= [q_rows][num_heads][head_dim], or [batch][q_rows][num_heads][head_dim]). */
+int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,
+                                int32_t num_splits, int32_t num_rows, int32_t head_dim,
+                                float out_scale, void *out_fp16, void *stream);
+
+/* Sparse (QSA) verify of a batch over selected blocks ([QSA] sparse split-K
+ * paged GQA kernel), writing split partials.  A block is one page.
+ *   q_bf16       [batch][q_rows][num_heads][head_dim] BF16, contiguous
+ *   block_table  [batch][max_blocks_per_req] int32: logical block -> physical page
+ *   sel_blocks   [batch][num_kv_heads][topk] int32 logical block ids; -1 = empty
+ *                slot (skipped); repeated ids are attended as often as listed
+ *   row_lens     [batch][q_rows] int32: row i of request b sees logical tokens
+ *                t < clamp(len, 0, max_blocks_per_req*page_size), which masks
+ *                the newest block causally
+ *   plan         (host) from paged_attn_plan(topk*page_size, q_rows*num_heads/num_kv_heads,
+ *                batch*num_kv_heads, head_dim, ...); split s covers selection
+ *                list positions [s*T, (s+1)*T), position p naming slot
+ *                p / page_size and in-block token p % page_size
+ *   rows of the workspace and of the combined output: (b, i, h).
+ * Other arguments as for paged_attn_verify_e4m3. */
+int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
+                               const int32_t *block_table, int32_t max_blocks_per_req,
+                               const int32_t *sel_blocks, int32_t topk,
+                               const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float sm_scale, float k_scale, const pa_plan *plan,
+                               const pa_workspace *ws, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_E4M3_H */

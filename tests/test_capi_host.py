@@ -1,0 +1,187 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, reports its ABI revision, plans splits by its documented rules and
+rejects bad arguments before anything reaches a device.  No compute calls."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_kv_paged_attn_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn_e4m3.h")
+
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP, PA_EPLAN = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.LIB_PATH):
+        from fp8_kv_paged_attn_amd import build
+
+        build.build()
+    return pa.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == set(pa.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_abi_and_status(L):
+    assert L.paged_attn_abi_version() == pa.ABI_VERSION == 1
+    for rc in (PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP,
+               PA_EPLAN, 12345):
+        s = L.paged_attn_status_string(rc)
+        assert s and len(s) > 1
+
+
+@pytest.mark.parametrize("max_tokens,rows,units,D,cus,req", [
+    (2048, 12, 1, 256, 256, 4), (8192, 48, 1, 256, 0, 0), (65536, 48, 1, 256, 0, 0),
+    (131072, 48, 1, 256, 0, 0), (262144, 48, 1, 256, 0, 0), (2048, 48, 32, 128, 0, 0),
+    (1, 6, 1, 256, 0, 0), (0, 6, 1, 256, 0, 0), (300, 4, 2, 128, 0, 7), (64, 48, 1, 256, 0, 9),
+    (100000, 48, 3, 256, 80, 0), (262144, 48, 1, 256, 0, 100000),
+])
+def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
+    p = pa.plan(max_tokens, rows, units, D, num_cus=cus, splits=req)
+    S, T = p.num_splits, p.tokens_per_split
+    tiles = max(1, -(-max_tokens // 64))
+    assert T % 64 == 0 and T >= 64 and 1 <= S <= 65535
+    assert S * T >= max_tokens
+    if max_tokens > 0:
+        assert (S - 1) * T < max_tokens, "no split may lie wholly past max_tokens"
+    if req:
+        assert S <= min(req, tiles)
+    else:
+        c = cus if cus > 0 else 256
+        assert S <= max(1, -(-c // units))
+        assert S <= max(1, -(-max_tokens // 256))
+    assert (p.max_tokens, p.rows_per_kv_unit, p.num_kv_units, p.head_dim) == (max_tokens, rows, units, D)
+    assert p.ws_acc_bytes == S * rows * units * D * 4
+    assert p.ws_stat_bytes == S * rows * units * 4
+    assert p.kernel == 0
+
+
+def test_plan_rejects(L):
+    out = pa.PaPlan()
+    assert L.paged_attn_plan(-1, 48, 1, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert L.paged_attn_plan(10, 0, 1, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert L.paged_attn_plan(10, 4, 0, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert L.paged_attn_plan(10, 4, 1, 256, 0, -2, ctypes.byref(out)) == PA_EINVAL
+    assert L.paged_attn_plan(10, 4, 1, 256, 0, 0, None) == PA_EINVAL
+
+
+# Fake, 16-byte-aligned addresses: every call below is rejected by a host check
+# before any HIP call, so they are never dereferenced.  The tests still stay
+# off machines with a GPU, where a wrongly accepted call could reach it.
+A = 0x10000
+no_device = pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="fake pointers; CPU only")
+
+
+class Call:
+    """A valid-looking dense verify call whose fields the tests spoil one at a time."""
+
+    def __init__(self):
+        self.q = A
+        self.pool = pa.PaKvPool(A * 2, A * 3, 3296 * 256, 256, 256, 64, 3296)
+        self.table, self.entries = A * 4, 3
+        self.lens, self.max_tokens = A * 5, 8192
+        self.q_rows, self.H, self.Hkv, self.D = 8, 6, 1, 256
+        self.sm, self.ks = 0.0625, 0.37
+        self.plan = pa.plan(8192, 48, 1, 256)
+        S = self.plan.num_splits
+        self.ws = pa.PaWorkspace(A * 6, A * 7, A * 8, S * 48 * 256 * 4, S * 48 * 4)
+
+    def __call__(self, L):
+        return L.paged_attn_verify_e4m3(self.q, ctypes.byref(self.pool), self.table, self.entries,
+                                        self.lens, self.max_tokens, self.q_rows, self.H, self.Hkv,
+                                        self.D, self.sm, self.ks, ctypes.byref(self.plan),
+                                        ctypes.byref(self.ws), None)
+
+
+def _spoil(L, attr, value, expect, sub=None):
+    c = Call()
+    tgt = getattr(c, sub) if sub else c
+    setattr(tgt, attr, value)
+    assert c(L) == expect, (attr, value)
+
+
+@no_device
+def test_verify_rejects_bad_arguments(L):
+    _spoil(L, "q", None, PA_EINVAL)
+    _spoil(L, "table", None, PA_EINVAL)
+    _spoil(L, "lens", None, PA_EINVAL)
+    _spoil(L, "k_pool", None, PA_EINVAL, sub="pool")
+    _spoil(L, "D", 64, PA_EUNSUPPORTED)
+    _spoil(L, "q_rows", 9, PA_EUNSUPPORTED)
+    _spoil(L, "q_rows", 0, PA_EINVAL)
+    _spoil(L, "Hkv", 4, PA_EINVAL)                 # 6 % 4 != 0
+    _spoil(L, "H", 12, PA_EUNSUPPORTED)            # 8 x 12 rows per KV head > 48
+    _spoil(L, "q", A + 8, PA_EALIGN)
+    _spoil(L, "k_pool", A * 2 + 4, PA_EALIGN, sub="pool")
+    _spoil(L, "token_stride", 264 - 4, PA_EALIGN, sub="pool")
+    _spoil(L, "page_size", 0, PA_EINVAL, sub="pool")
+    _spoil(L, "entries", 2, PA_EINVAL)             # 2 x 3296 < 8192
+    _spoil(L, "max_tokens", -1, PA_EINVAL)
+    _spoil(L, "ks", 0.0, PA_EINVAL)
+    _spoil(L, "ks", float("nan"), PA_EINVAL)
+    _spoil(L, "sm", float("inf"), PA_EINVAL)
+    _spoil(L, "max_tokens", 8000, PA_EPLAN)        # plan made for 8192
+    _spoil(L, "tokens_per_split", 100, PA_EPLAN, sub="plan")
+    _spoil(L, "num_splits", 1, PA_EPLAN, sub="plan")
+    _spoil(L, "kernel", 7, PA_EPLAN, sub="plan")
+    _spoil(L, "acc_bytes", 1024, PA_EWORKSPACE, sub="ws")
+    _spoil(L, "stat_bytes", 4, PA_EWORKSPACE, sub="ws")
+    _spoil(L, "sum", None, PA_EINVAL, sub="ws")
+
+
+@no_device
+def test_qsa_and_combine_reject_bad_arguments(L):
+    pool = pa.PaKvPool(A * 2, A * 3, 64 * 256, 256, 128, 8192, 64)
+    p = pa.plan(32 * 64, 48, 32, 128)
+    ws = pa.PaWorkspace(A * 6, A * 7, A * 8, p.ws_acc_bytes, p.ws_stat_bytes)
+
+    def qsa(**kw):
+        a = dict(q=A, table=A * 4, maxb=512, sel=A * 9, topk=32, lens=A * 5, B=16, qr=4, H=24,
+                 Hkv=2, D=128, sm=0.088, ks=0.5)
+        a.update(kw)
+        return L.qsa_sparse_verify_e4m3(a["q"], ctypes.byref(pool), a["table"], a["maxb"],
+                                        a["sel"], a["topk"], a["lens"], a["B"], a["qr"], a["H"],
+                                        a["Hkv"], a["D"], a["sm"], a["ks"], ctypes.byref(p),
+                                        ctypes.byref(ws), None)
+
+    assert qsa(sel=None) == PA_EINVAL
+    assert qsa(topk=0) == PA_EINVAL
+    assert qsa(B=0) == PA_EINVAL
+    assert qsa(topk=31) == PA_EPLAN
+    assert qsa(B=8) == PA_EPLAN
+    assert qsa(ks=-0.5) == PA_EINVAL
+    assert qsa(H=96) == PA_EUNSUPPORTED
+    assert L.paged_attn_combine_fp32(A, A, A, 0, 48, 256, 1.0, A, None) == PA_EINVAL
+    assert L.paged_attn_combine_fp32(A, A, A, 4, 48, 256, float("nan"), A, None) == PA_EINVAL
+    assert L.paged_attn_combine_fp32(None, A, A, 4, 48, 256, 1.0, A, None) == PA_EINVAL
+    assert L.paged_attn_combine_fp32(A, A, A, 4, 48, 256, 1.0, None, None) == PA_EINVAL
+
+
+@no_device
+def test_valid_call_without_device_reports_edevice(L):
+    assert Call()(L) == PA_EDEVICE
+
+
+def test_python_binding_rejects_cpu_fallback(monkeypatch, tmp_path):
+    """Without the built library every op raises: there is no CPU path."""
+    monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(pa, "_LIB", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        pa.lib()

@@ -1,0 +1,318 @@
+"""GPU parity: the HIP path through its C ABI against the FP64 oracle.
+
+Every case prints a line naming itself before it touches the GPU.  Full-size
+cases are the five named configurations in the split plan the benchmark
+uses; small cases span several 64-token tiles with a ragged tail, odd page
+sizes, grouped heads with more than one KV head, and forced split counts."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_paged_attn_amd as pa
+from fp8_kv_paged_attn_amd import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["simple"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    gu.require_gpu()
+    pa.lib()
+
+
+def announce(*what):
+    print("[case]", *what, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the five named configurations
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("name", ["c0", "c1", "c2_64k", "c2_128k", "c3"])
+def test_dense_config(orc, name, kernel):
+    w = wl.cached(name)
+    announce(name, kernel)
+    got = gu.run_dense(w, kernel)
+    ref = orc.dense_workload(w, nthreads=8)
+    gu.assert_parity(got, ref, f"{name}/{kernel}")
+    if name == "c3":
+        assert not got[5:].any(), "zero-length rows must be exactly zero"
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_config(orc, kernel):
+    w = wl.cached("c4")
+    announce("c4", kernel)
+    got = gu.run_qsa(w, kernel)
+    ref = orc.qsa_workload(w, nthreads=8)
+    gu.assert_parity(got, ref, f"c4/{kernel}")
+
+
+# ---------------------------------------------------------------------------
+# small cases: tiles, ragged tails, page sizes, grouped heads, forced splits
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # (q_rows, H, Hkv, D, ctx, page, lens, splits)
+    (2, 6, 1, 256, 300, 48, None, 3),
+    (8, 6, 1, 256, 1000, 800, None, 0),
+    (3, 4, 2, 128, 517, 16, [0, 200, 517], 5),
+    (1, 6, 1, 256, 70, 7, None, 1),
+    (4, 12, 1, 128, 640, 64, [637, 638, 639, 640], 10),
+    (8, 6, 1, 256, 2500, 848, [2493, 2494, 2495, 2496, 2497, 0, 0, 0], 0),
+    (2, 24, 1, 256, 200, 16, None, 2),
+    (5, 8, 4, 256, 333, 1, None, 4),
+    (8, 6, 1, 256, 4100, 1728, None, 64),
+]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_dense_small(orc, case, kernel):
+    qr, H, Hkv, D, ctx, page, lens, splits = SMALL[case]
+    npages = -(-ctx // page)
+    w = wl.make_dense(f"small{case}", 0x5EED00 + case, q_rows=qr, num_heads=H, num_kv_heads=Hkv,
+                      head_dim=D, ctx=ctx, page_size=page, pool_pages=npages + 3, sigma=1.2,
+                      k_scale=0.45, v_scale=1.6, row_lens=lens, num_splits=splits,
+                      poison_tail=True)
+    announce("small", case, SMALL[case], kernel)
+    got = gu.run_dense(w, kernel)
+    ref = orc.dense_workload(w)
+    gu.assert_parity(got, ref, f"small{case}/{kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_small_edges(orc, kernel):
+    w = wl.make_qsa("qsa_small", 0x5EED50, batch=3, q_rows=4, num_heads=12, num_kv_heads=2,
+                    head_dim=128, ctx=1024, page_size=64, topk=6, k_scale=0.5, v_scale=2.0,
+                    num_splits=3)
+    sel = w.sel_blocks.copy()
+    sel[0, 0, 2] = -1                       # empty slot
+    sel[1, 1, 0] = sel[1, 1, 3]             # a block listed twice
+    sel[2, 0, :] = -1                       # nothing selected
+    lens = w.row_lens.copy()
+    lens[0, 1] = 0
+    lens[1, :] = [1000, 1001, 1002, 5000]   # the last is clamped to 1024
+    w = dataclasses.replace(w, sel_blocks=sel, row_lens=lens)
+    announce("qsa_small_edges", kernel)
+    got = gu.run_qsa(w, kernel)
+    ref = orc.qsa_workload(w)
+    gu.assert_parity(got, ref, f"qsa_small/{kernel}")
+    assert not got[2, :, :6].any(), "unit with an empty selection must give zeros"
+    assert not got[0, 1].any()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_d256(orc, kernel):
+    w = wl.make_qsa("qsa_d256", 0x5EED51, batch=2, q_rows=8, num_heads=6, num_kv_heads=1,
+                    head_dim=256, ctx=640, page_size=32, topk=5, k_scale=0.37, v_scale=1.9)
+    announce("qsa_d256", kernel)
+    gu.assert_parity(gu.run_qsa(w, kernel), orc.qsa_workload(w), f"qsa_d256/{kernel}")
+
+
+# ---------------------------------------------------------------------------
+# workspace and combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_workspace_partials_c0(orc, kernel):
+    """The FP32 split workspace is part of the interface: compare it with the
+    oracle's split partials, and the combine kernel with the oracle's combine
+    of the same FP32 workspace (within one FP16 ulp)."""
+    w = wl.cached("c0")
+    announce("workspace c0", kernel)
+    got, p, (acc, mx, sm) = gu.run_dense(w, kernel, return_ws=True)
+    assert p.num_splits == 4
+    oacc, omx, osm = orc.verify_dense_split(w.q_bits, w.k_pool, w.v_pool, w.block_table,
+                                            w.row_lens, w.max_tokens, w.num_kv_heads,
+                                            w.sm_scale, w.k_scale, p.num_splits,
+                                            p.tokens_per_split)
+    assert np.allclose(mx, omx, rtol=2e-6, atol=2e-5), np.abs(mx - omx).max()
+    assert np.allclose(sm, osm, rtol=2e-5, atol=0), np.abs(sm / osm - 1).max()
+    nz = osm > 0
+    norm_gpu = acc[nz] / sm[nz][:, None]
+    norm_orc = oacc[nz] / osm[nz][:, None]
+    rel = np.linalg.norm(norm_gpu - norm_orc) / np.linalg.norm(norm_orc)
+    assert rel < 1e-4, rel
+    comb = orc.combine(acc, mx, sm, w.v_scale).reshape(got.shape)
+    ulp = np.spacing(np.abs(comb).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got.astype(np.float64) - comb) <= ulp), "combine off by > 1 fp16 ulp"
+
+
+def test_combine_empty_and_single_split():
+    """Combine edge cases fed directly: every split empty -> 0; one split ->
+    out_scale * acc / sum."""
+    S, R, D = 3, 5, 256
+    acc = torch.zeros((S, R, D), dtype=torch.float32, device=gu.DEV)
+    mx = torch.full((S, R), float("-inf"), device=gu.DEV)
+    sm = torch.zeros((S, R), device=gu.DEV)
+    acc[1, 2] = torch.arange(D, dtype=torch.float32, device=gu.DEV)
+    mx[1, 2] = 3.0
+    sm[1, 2] = 2.0
+    out = torch.full((R, D), 7.0, dtype=torch.float16, device=gu.DEV)
+    announce("combine edges")
+    pa.paged_attn_combine_fp32((acc, mx, sm), S, R, D, 1.5, out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    exp = np.zeros((R, D))
+    exp[2] = (np.arange(D) / 2.0 * 1.5).astype(np.float16)
+    assert np.array_equal(o, exp)
+
+
+# ---------------------------------------------------------------------------
+# index handling: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_one_hot_probe_bit_exact(orc, kernel):
+    """K = 448 on one token, zero elsewhere, q = 1: the softmax is one-hot in
+    FP32 too, so every row returns fp16(v_scale * V[probe]) exactly, for probes
+    at page starts and ends, in the partial last page and past a split edge."""
+    base = wl.make_dense("probe", 0x9B0BE, q_rows=2, num_heads=6, num_kv_heads=1, head_dim=256,
+                         ctx=2048, page_size=800, pool_pages=6, sigma=1.0, k_scale=1.0,
+                         v_scale=1.5, num_splits=4)
+    ones = np.full(base.q_bits.shape, np.float16(1.0)).view(np.uint16)
+    tab = orc.e4m3_table()
+    for probe in [0, 511, 512, 799, 800, 1599, 1600, 2046, 2047]:
+        k = np.zeros_like(base.k_pool)
+        lp, u = divmod(probe, base.page_size)
+        phys = int(base.block_table[lp])
+        k[phys, u, 0, :] = 0x7E
+        w = dataclasses.replace(base, k_pool=k, q_bits=ones,
+                                row_lens=np.array([2048, 2048], np.int32))
+        announce("probe", probe, kernel)
+        got = gu.run_dense(w, kernel)
+        exp = (np.float32(w.v_scale) * tab[base.v_pool[phys, u, 0]].astype(np.float32)
+               ).astype(np.float16)
+        assert np.array_equal(got[0, 0], exp) and np.array_equal(got[1, 5], exp), probe
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_relocation_and_strided_view_bit_identical(kernel):
+    """Pages moved to other physical slots, and the pool read as a strided view
+    of a packed allocation (two members interleaved per page), give
+    bit-identical output under the same plan."""
+    w = wl.make_dense("reloc", 0x7E10C, q_rows=8, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=3000, page_size=848, pool_pages=8, sigma=1.5, k_scale=0.37,
+                      v_scale=1.9)
+    announce("relocation", kernel)
+    base = gu.run_dense(w, kernel)
+    P = w.k_pool.shape[0]
+    perm = np.roll(np.arange(P), 3)
+    k = np.empty_like(w.k_pool)
+    v = np.empty_like(w.v_pool)
+    k[perm] = w.k_pool
+    v[perm] = w.v_pool
+    w2 = dataclasses.replace(w, k_pool=k, v_pool=v,
+                             block_table=perm[w.block_table].astype(np.int32))
+    assert np.array_equal(gu.run_dense(w2, kernel), base), "relocated pages"
+    # packed: [P][page][2 members][Hkv][D]; this pool is member 1
+    packed_k = torch.zeros((P, w.page_size, 2, 1, 256), dtype=torch.uint8, device=gu.DEV)
+    packed_v = torch.full((P, w.page_size, 2, 1, 256), 0x7F, dtype=torch.uint8, device=gu.DEV)
+    packed_k[:, :, 1] = torch.from_numpy(w.k_pool).to(gu.DEV)
+    packed_v[:, :, 1] = torch.from_numpy(w.v_pool).to(gu.DEV)
+    kview, vview = packed_k[:, :, 1], packed_v[:, :, 1]
+    assert kview.stride(1) == 512
+    got = gu.run_dense(w, kernel, k=kview, v=vview)
+    assert np.array_equal(got, base), "strided view"
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_nan_poison_bit_identical(kernel):
+    """NaN bytes in the null page that pads the table, in page tails past the
+    longest row and in unused pages leave the output bit-identical."""
+    kw = dict(q_rows=8, num_heads=6, num_kv_heads=1, head_dim=256, ctx=3000, page_size=848,
+              pool_pages=6, sigma=1.0, k_scale=0.5, v_scale=2.25,
+              row_lens=[2996, 2997, 2998, 2999, 3000, 0, 0, 0], pad_table_to=8)
+    clean = wl.make_dense("clean", 0x4A4, null_page_nan=True, poison_tail=False,
+                          poison_unused=False, **kw)
+    dirty = wl.make_dense("dirty", 0x4A4, null_page_nan=True, poison_tail=True,
+                          poison_unused=True, **kw)
+    clean = dataclasses.replace(clean, k_pool=clean.k_pool.copy(), v_pool=clean.v_pool.copy())
+    clean.k_pool[0] = 0
+    clean.v_pool[0] = 0
+    assert (dirty.k_pool[0] == 0x7F).all()
+    announce("nan poison", kernel)
+    a = gu.run_dense(clean, kernel)
+    b = gu.run_dense(dirty, kernel)
+    assert np.all(np.isfinite(b.astype(np.float64)))
+    assert np.array_equal(a, b)
+    assert not b[5:].any()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_zero_lengths(kernel):
+    w = wl.make_dense("zeros", 0x2E0, q_rows=4, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=700, page_size=96, pool_pages=9, sigma=1.0, k_scale=1.0, v_scale=1.0,
+                      row_lens=[0, 0, 0, 0])
+    announce("all rows empty", kernel)
+    assert not gu.run_dense(w, kernel).any()
+    w0 = dataclasses.replace(w, max_tokens=0)
+    announce("max_tokens 0", kernel)
+    assert not gu.run_dense(w0, kernel).any()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_length_clamp(orc, kernel):
+    w = wl.make_dense("clamp", 0xC1A, q_rows=3, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=500, page_size=64, pool_pages=10, sigma=1.0, k_scale=0.8,
+                      v_scale=1.1, row_lens=[-5, 10**6, 250])
+    announce("clamp", kernel)
+    got = gu.run_dense(w, kernel)
+    gu.assert_parity(got, orc.dense_workload(w), f"clamp/{kernel}")
+    assert not got[0].any()
+
+
+# ---------------------------------------------------------------------------
+# graph replay with changed lengths
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_graph_replay_changed_lengths(kernel):
+    """verify + combine captured once, replayed with new device lengths
+    (including zeros) between eager work: each replay equals the eager call."""
+    w = wl.make_dense("graph", 0x62A9, q_rows=8, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=5000, page_size=1648, pool_pages=6, sigma=1.0, k_scale=0.6,
+                      v_scale=1.3)
+    d = gu.dense_to_dev(w)
+    p = gu.dense_plan(w, kernel)
+    ws = pa.make_workspace(p, 48, 256, gu.DEV)
+    out = torch.empty((8, 6, 256), dtype=torch.float16, device=gu.DEV)
+    lens = d.lens.clone()
+
+    def step():
+        pa.verify(d.q, d.k, d.v, d.table, lens, w.max_tokens, sm_scale=w.sm_scale,
+                  k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws, out=out)
+
+    announce("graph capture", kernel)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    trials = [[4993, 4994, 4995, 4996, 4997, 4998, 4999, 5000], [0] * 8,
+              [100, 0, 3000, 0, 5000, 1, 64, 65], [4993, 4994, 4995, 4996, 4997, 0, 0, 0]]
+    for lv in trials:
+        lens.copy_(torch.tensor(lv, dtype=torch.int32))
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.cpu().numpy().copy()
+        out.fill_(0)
+        step()                              # eager, same buffers
+        torch.cuda.synchronize()
+        eager = out.cpu().numpy().copy()
+        assert np.array_equal(replayed, eager), lv
+        zero_rows = [i for i, x in enumerate(lv) if x == 0]
+        assert not replayed[zero_rows].any()
