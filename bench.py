@@ -161,7 +161,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "simple", "mfma"])
+    ap.add_argument("--kernel", default="mfma", choices=["auto", "simple", "mfma"])
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")

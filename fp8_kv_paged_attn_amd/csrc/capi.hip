@@ -271,9 +271,11 @@ int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const 
 {
     if (!ws_acc || !ws_max || !ws_sum || !out_fp16)
         return PA_EINVAL;
-    if (num_splits < 1 || num_rows < 0 || head_dim < 1 || head_dim > 4096 ||
-        !std::isfinite(out_scale))
+    if (num_splits < 1 || num_rows < 0 || head_dim < 4 || head_dim > 4096 ||
+        head_dim % 4 != 0 || !std::isfinite(out_scale))
         return PA_EINVAL;
+    if (!aligned16(ws_acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0)
+        return PA_EALIGN;
     if (num_rows > 0x7FFFFFFF / 2)
         return PA_EINVAL;
     int32_t rc = check_device();

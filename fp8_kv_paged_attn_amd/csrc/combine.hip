@@ -7,9 +7,14 @@
 // "Qwen4Exp: fp8_e4m3 main KV cache on the QSA path", review thread on
 // host-side KV scales).
 //
-// One workgroup per output row; thread d owns column d.  Split weights are
-// w_s = 2^(m_s - M) with M the largest max among non-empty splits, so an
-// empty split (m = -inf, l = 0) is skipped and -inf - -inf never forms.
+// Split weights are w_s = 2^(m_s - M) with M the largest max among non-empty
+// splits (l_s > 0); empty splits get weight 0 and are skipped, so -inf - -inf
+// never forms, and a row whose splits are all empty is written as 0.
+//
+// One workgroup per (row, 64-column chunk): 16 column lanes x 16 split groups.
+// The weights of 256 splits at a time are computed once into LDS, each thread
+// accumulates float4 columns over its splits, and the 16 split groups are
+// summed through LDS.  The split sums are plain FP32 sums in a fixed order.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -18,6 +23,10 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kLanes = 16;                 // float4 column lanes: 64 columns
+constexpr int kGroups = kThreads / kLanes; // split groups
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ acc,
                                                            const float *__restrict__ mx,
@@ -26,27 +35,80 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                                                            float out_scale,
                                                            uint16_t *__restrict__ out)
 {
+    __shared__ float red[kThreads];
+    __shared__ float wts[kThreads];
+    __shared__ f32x4 part[kGroups][kLanes];
+
     const int r = blockIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) {
-        float l = sm[(int64_t)s * R + r];
-        float m = mx[(int64_t)s * R + r];
-        if (l > 0.0f && m > M)
-            M = m;
+    const int tid = threadIdx.x;
+    const int lane = tid % kLanes, grp = tid / kLanes;
+    const int d0 = blockIdx.y * (4 * kLanes) + 4 * lane;
+
+    // M = max over non-empty splits
+    float m = -INFINITY;
+    for (int s = tid; s < S; s += kThreads) {
+        const int64_t k = (int64_t)s * R + r;
+        if (sm[k] > 0.0f)
+            m = fmaxf(m, mx[k]);
     }
-    for (int d = threadIdx.x; d < D; d += kThreads) {
-        float num = 0.0f, den = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            int64_t k = (int64_t)s * R + r;
-            float l = sm[k];
-            if (!(l > 0.0f))
-                continue;
-            float w = exp2f(mx[k] - M);
-            den += w * l;
-            num += w * acc[k * D + d];
+    red[tid] = m;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (tid < off)
+            red[tid] = fmaxf(red[tid], red[tid + off]);
+        __syncthreads();
+    }
+    const float M = red[0];
+    __syncthreads();
+
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den_part = 0.0f;
+    const bool col_ok = d0 < D;          // D is a multiple of 4
+    for (int s0 = 0; s0 < S; s0 += kThreads) {
+        const int s = s0 + tid;
+        float w = 0.0f;
+        if (s < S) {
+            const int64_t k = (int64_t)s * R + r;
+            const float l = sm[k];
+            if (l > 0.0f) {
+                w = exp2f(mx[k] - M);
+                den_part += w * l;
+            }
         }
-        float o = den > 0.0f ? (num / den) * out_scale : 0.0f;
-        out[(int64_t)r * D + d] = __builtin_bit_cast(uint16_t, (_Float16)o);
+        wts[tid] = w;
+        __syncthreads();
+        const int cnt = min(kThreads, S - s0);
+        if (col_ok) {
+            for (int j = grp; j < cnt; j += kGroups) {
+                const float wj = wts[j];
+                if (wj != 0.0f) {
+                    const f32x4 v = *(const f32x4 *)(acc + ((int64_t)(s0 + j) * R + r) * D + d0);
+                    num += wj * v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    red[tid] = den_part;
+    part[grp][lane] = num;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (tid < off)
+            red[tid] += red[tid + off];
+        __syncthreads();
+    }
+    if (grp == 0 && col_ok) {
+        f32x4 tot = part[0][lane];
+        for (int gq = 1; gq < kGroups; ++gq)
+            tot += part[gq][lane];
+        const float den = red[0];
+        uint16_t h[4];
+        for (int k = 0; k < 4; ++k) {
+            const float o = den > 0.0f ? (tot[k] / den) * out_scale : 0.0f;
+            h[k] = __builtin_bit_cast(uint16_t, (_Float16)o);
+        }
+        uint2 packed = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+        *(uint2 *)(out + (int64_t)r * D + d0) = packed;
     }
 }
 
@@ -58,8 +120,11 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
 {
     if (num_rows == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(num_rows), dim3(kThreads), 0, stream, acc, mx, sm,
-                       num_splits, num_rows, head_dim, out_scale, out);
+    if (head_dim % 4 != 0)
+        return hipErrorInvalidValue;
+    dim3 grid(num_rows, (head_dim + 4 * kLanes - 1) / (4 * kLanes));
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, acc, mx, sm, num_splits,
+                       num_rows, head_dim, out_scale, out);
     return hipGetLastError();
 }
 

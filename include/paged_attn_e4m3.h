@@ -173,7 +173,9 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
  * and out[r][:] = 0 when every split of row r is empty.  out_scale is the
  * V dequantisation scale ([QSA] output scale).  ws_* as written by a verify
  * call with num_splits splits and num_rows rows; out_fp16 [num_rows][head_dim]
- * (= [q_rows][num_heads][head_dim], or [batch][q_rows][num_heads][head_dim]). */
+ * (= [q_rows][num_heads][head_dim], or [batch][q_rows][num_heads][head_dim]).
+ * head_dim is a multiple of 4 (<= 4096); ws_acc is 16-byte aligned and
+ * out_fp16 8-byte aligned (PA_EALIGN otherwise). */
 int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,
                                 int32_t num_splits, int32_t num_rows, int32_t head_dim,
                                 float out_scale, void *out_fp16, void *stream);

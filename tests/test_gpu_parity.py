@@ -17,7 +17,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["simple"]
+KERNELS = ["simple", "mfma"]
 
 
 @pytest.fixture(scope="module", autouse=True)
