@@ -165,6 +165,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run one plain device-to-device copy of MIB MiB (a known-size "
+                         "kernel for calibrating hardware traffic counters) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -183,6 +186,15 @@ def main():
         raise SystemExit("bench.py needs a ROCm GPU (cuda:0)")
     pa.lib()
     src_hash = kernel_source_hash()
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
 
     log(f"[bench] generating {args.workload}")
     w = wl.cached(args.workload)

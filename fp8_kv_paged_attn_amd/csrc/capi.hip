@@ -79,9 +79,15 @@ int32_t check_shape(int32_t q_rows, int32_t num_heads, int32_t num_kv_heads, int
     return PA_OK;
 }
 
+// The folded logit scale sm_scale * k_scale * log2(e) must be a positive normal
+// FP32 number: the kernels take row maxima on raw scores and scale afterwards.
 int32_t check_scales(float sm_scale, float k_scale)
 {
-    if (!std::isfinite(sm_scale) || !std::isfinite(k_scale) || !(k_scale > 0.0f))
+    if (!std::isfinite(sm_scale) || !std::isfinite(k_scale) || !(sm_scale > 0.0f) ||
+        !(k_scale > 0.0f))
+        return PA_EINVAL;
+    const float c = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    if (!std::isnormal(c))
         return PA_EINVAL;
     return PA_OK;
 }

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // P^T fragments: [token block kk][row block][hi, lo][64 lanes] x 16 bytes
     __shared__ __attribute__((aligned(16))) int4v p_s[kWaves][kRowBlocks][2][64];
     __shared__ int2v slots[kSlots];                 // (physical page, first token) per slot
-    __shared__ int32_t tok_s[2][kMacro];            // sparse: token of each position
+    __shared__ __attribute__((aligned(16))) int32_t tok_s[2][kMacro];   // sparse: token per position
     __shared__ float xmax[kWaves][16 * kRowBlocks];
     __shared__ float xl[kWaves][16 * kRowBlocks];
 
@@ -308,23 +308,66 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     };
 
     // Direct-to-LDS loads of this wave's 32 rows of macro-step j into one plane.
+    // Lane l loads, in load i, row r_i = i*ROWS_PER_DMA + l/LANES_PER_ROW, swizzled
+    // chunk position l%LANES_PER_ROW.  With pages of at least 32 tokens a wave's
+    // block spans at most two page slots, so the page lookup is done once per
+    // block (wave-uniform) and a lane only adds its precomputed row offset; small
+    // pages or very large token strides take the per-row resolve.
+    const int cp = lane % C::LANES_PER_ROW;
+    const bool two_slot = ps >= kSub && a.token_stride < (1 << 25);
+    int32_t loff[C::DMA];
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+        const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
+        loff[i] = two_slot ? r * (int32_t)a.token_stride + 16 * (cp ^ swz<D>(r)) : 0;
+    }
     auto issue_plane = [&](int j, const uint8_t *pool, uint8_t *plane, int32_t *tokst)
         __attribute__((always_inline)) {
         const int pos0 = lo + j * kMacro + w * kSub;
-        const int cp = lane % C::LANES_PER_ROW;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(plane + w * C::BLOCK));
         // the stage being refilled was read by this wave's previous step
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        if (two_slot) {
+            const int sa = divp(pos0, dm);
+            const int ua = pos0 - sa * ps;
+            const int na = min(kSub, ps - ua);            // rows in the first slot
+            const int2v ea = slots[min(max(sa - slot0, 0), kSlots - 1)];
+            const int2v eb = slots[min(max(sa + 1 - slot0, 0), kSlots - 1)];
+            const int phys_a = __builtin_amdgcn_readfirstlane(ea.x);
+            const int tb_a = __builtin_amdgcn_readfirstlane(ea.y);
+            const int phys_b = __builtin_amdgcn_readfirstlane(eb.x);
+            const int tb_b = __builtin_amdgcn_readfirstlane(eb.y);
+            const int hip = hi - pos0;
+            // valid rows: [0, end_a) in the first slot, [na, end_b) in the second
+            int end_a = min(na, hip), end_b = hip;
+            if (SPARSE) {
+                end_a = phys_a >= 0 ? min(end_a, lmax - (tb_a + ua)) : 0;
+                end_b = phys_b >= 0 ? min(end_b, na + lmax - tb_b) : 0;
+            }
+            const int64_t base_a = (int64_t)phys_a * a.page_stride + (int64_t)ua * a.token_stride + head_off;
+            const int64_t base_b = (int64_t)phys_b * a.page_stride - (int64_t)na * a.token_stride + head_off;
 #pragma unroll
-        for (int i = 0; i < C::DMA; ++i) {
-            const int row = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
-            int64_t off;
-            int t;
-            const bool ok = resolve(pos0 + row, off, t);
-            const int64_t src = ok ? off + 16 * (cp ^ swz<D>(row)) : 0;
-            dma16(pool + src, dst + i * 1024);
-            if (SPARSE && tokst != nullptr && cp == 0)
-                tokst[w * kSub + row] = ok ? t : INT32_MAX;
+            for (int i = 0; i < C::DMA; ++i) {
+                const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
+                const bool in_b = r >= na;
+                const bool ok = in_b ? (r < end_b) : (r < end_a);
+                const int64_t src = ok ? (in_b ? base_b : base_a) + loff[i] : 0;
+                dma16(pool + src, dst + i * 1024);
+                if (SPARSE && tokst != nullptr && cp == 0)
+                    tokst[w * kSub + r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::DMA; ++i) {
+                const int row = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
+                int64_t off;
+                int t;
+                const bool ok = resolve(pos0 + row, off, t);
+                const int64_t src = ok ? off + 16 * (cp ^ swz<D>(row)) : 0;
+                dma16(pool + src, dst + i * 1024);
+                if (SPARSE && tokst != nullptr && cp == 0)
+                    tokst[w * kSub + row] = ok ? t : INT32_MAX;
+            }
         }
     };
 
@@ -386,29 +429,45 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         }
         issue_plane(j + 2, a.k_pool, kst_next2, nullptr);
 
-        // ---- tokens of this lane's 8 scores: 32w + 8g + jj -------------------
+        // ---- visibility of this lane's 8 scores (tokens 32w + 8g + jj) ---------
+        // vis[rb] bit jj: row 16rb + n sees token jj.  Row blocks that see the
+        // whole block skip the selects; blocks that see none of it skip P.
         int tok[8];
-        bool valid[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            if (!SPARSE) {
-                tok[jj] = pos0 + w * kSub + 8 * g + jj;
-                valid[jj] = tok[jj] < hi;
-            } else {
-                tok[jj] = tok_cur[w * kSub + 8 * g + jj];
-                valid[jj] = tok[jj] != INT32_MAX;
-            }
+        if (SPARSE) {
+            const int4v t0 = *(const int4v *)&tok_cur[w * kSub + 8 * g];
+            const int4v t1 = *(const int4v *)&tok_cur[w * kSub + 8 * g + 4];
+            tok[0] = t0.x; tok[1] = t0.y; tok[2] = t0.z; tok[3] = t0.w;
+            tok[4] = t1.x; tok[5] = t1.y; tok[6] = t1.z; tok[7] = t1.w;
         }
+        const int tfirst = pos0 + w * kSub + 8 * g;
+        uint32_t vis[kRowBlocks];
         float y[kRowBlocks][8];
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) {
-            float mloc = -INFINITY;
+            if (!SPARSE) {
+                const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
+                vis[rb] = (1u << nv) - 1u;
+            } else {
+                uint32_t m = 0;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float v = s[rb][jj >> 2][jj & 3] * c;
-                const bool vis = valid[jj] && tok[jj] < lrow[rb];
-                y[rb][jj] = vis ? v : -INFINITY;
-                mloc = fmaxf(mloc, y[rb][jj]);
+                for (int jj = 0; jj < 8; ++jj)
+                    m |= (tok[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid tok = INT32_MAX
+                vis[rb] = m;
+            }
+            float mloc = -INFINITY;
+            if (__all(vis[rb] == 0xFFu)) {
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    y[rb][jj] = s[rb][jj >> 2][jj & 3] * c;
+                    mloc = fmaxf(mloc, y[rb][jj]);
+                }
+            } else if (!__all(vis[rb] == 0u)) {
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float v = s[rb][jj >> 2][jj & 3] * c;
+                    y[rb][jj] = ((vis[rb] >> jj) & 1u) ? v : -INFINITY;
+                    mloc = fmaxf(mloc, y[rb][jj]);
+                }
             }
             mloc = max_over_groups(mloc);
             if (g == 0)
@@ -436,24 +495,26 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 m_ref[rb] = mt;
             }
             const float mu = (m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb];
-            float lsum = 0.0f;
-            half8 ph, pl;
+            half8 ph = {}, pl = {};
+            if (!__all(vis[rb] == 0u)) {
+                float lsum = 0.0f;
 #pragma unroll
-            for (int jj = 0; jj < 8; jj += 2) {
-                const float p0 = exp2f(y[rb][jj] - mu);
-                const float p1 = exp2f(y[rb][jj + 1] - mu);
-                lsum += p0 + p1;
-                const float s0 = p0 * kPScale, s1 = p1 * kPScale;
-                const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s0) & 0xFFFFE000u);
-                const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s1) & 0xFFFFE000u);
-                const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
-                const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(s0 - h0, s1 - h1));
-                ph[jj] = hh.x;
-                ph[jj + 1] = hh.y;
-                pl[jj] = ll.x;
-                pl[jj + 1] = ll.y;
+                for (int jj = 0; jj < 8; jj += 2) {
+                    const float p0 = exp2f(y[rb][jj] - mu);
+                    const float p1 = exp2f(y[rb][jj + 1] - mu);
+                    lsum += p0 + p1;
+                    const float s0 = p0 * kPScale, s1 = p1 * kPScale;
+                    const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s0) & 0xFFFFE000u);
+                    const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s1) & 0xFFFFE000u);
+                    const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
+                    const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(s0 - h0, s1 - h1));
+                    ph[jj] = hh.x;
+                    ph[jj + 1] = hh.y;
+                    pl[jj] = ll.x;
+                    pl[jj + 1] = ll.y;
+                }
+                l_part[rb] += lsum;
             }
-            l_part[rb] += lsum;
             p_s[w][rb][0][lane] = __builtin_bit_cast(int4v, ph);
             p_s[w][rb][1][lane] = __builtin_bit_cast(int4v, pl);
         }

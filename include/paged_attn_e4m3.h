@@ -152,8 +152,9 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
  *                must equal plan->max_tokens
  *   q_rows 1..8; num_heads % num_kv_heads == 0; q_rows*num_heads/num_kv_heads
  *   <= 48 rows per KV head; head_dim 128 or 256
- *   sm_scale, k_scale (host) finite, k_scale > 0: the logit scale is
- *                sm_scale*k_scale*log2(e), folded on the host ([QSA])
+ *   sm_scale, k_scale (host) both > 0 and finite; the logit scale
+ *                sm_scale*k_scale*log2(e) is folded on the host ([QSA]) and must
+ *                be a positive normal FP32 number (PA_EINVAL otherwise)
  *   plan         (host) from paged_attn_plan(max_tokens, q_rows*num_heads/num_kv_heads,
  *                num_kv_heads, head_dim, ...)
  *   ws           (host) workspace of at least plan->ws_*_bytes

@@ -137,6 +137,9 @@ def test_verify_rejects_bad_arguments(L):
     _spoil(L, "ks", 0.0, PA_EINVAL)
     _spoil(L, "ks", float("nan"), PA_EINVAL)
     _spoil(L, "sm", float("inf"), PA_EINVAL)
+    _spoil(L, "sm", -0.0625, PA_EINVAL)
+    _spoil(L, "sm", 0.0, PA_EINVAL)
+    _spoil(L, "sm", 1e-40, PA_EINVAL)            # folded scale underflows
     _spoil(L, "max_tokens", 8000, PA_EPLAN)        # plan made for 8192
     _spoil(L, "tokens_per_split", 100, PA_EPLAN, sub="plan")
     _spoil(L, "num_splits", 1, PA_EPLAN, sub="plan")
