@@ -167,7 +167,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (a known-size "
-                         "kernel for calibrating hardware traffic counters) and exit")
+                         "kernel for calibrating hardware traffic counters) before the benchmark")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -30,6 +30,9 @@ def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Werror", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the
+           # (rare) accumulator rescale in the verify kernel
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra_flags, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -47,7 +47,7 @@ constexpr int kSub = 32;                  // tokens per wave per macro-step
 constexpr int kMacro = kSub * kWaves;     // tokens per macro-step
 constexpr int kRowBlocks = 3;             // 48 rows
 constexpr float kLazy = 8.0f;             // reference-max slack (log2 units)
-constexpr float kPScale = 64.0f;          // P is scaled by 2^6 before FP16 rounding
+constexpr float kPLog2 = 6.0f;            // P is carried as 2^6 * p (FP16 normal range)
 constexpr float kPUnscale = 1.0f / 64.0f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -83,13 +83,14 @@ __device__ __forceinline__ int swz(int r)
     return ((r >> 1) + 2 * (r >> 4)) & 7;
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+// Wait until at most N vector-memory loads of this wave are in flight.  Inline
+// asm on purpose: the compiler does not see the direct-to-LDS loads (also asm),
+// so it would consider a builtin s_waitcnt redundant and may delete it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // Workgroup barrier for LDS data.  __syncthreads() (and any release fence on
@@ -109,9 +110,34 @@ __device__ __forceinline__ void barrier_lds()
 // track it: its own tracking of these loads is conservative (it drains every
 // load in flight before LDS reads it cannot disambiguate).  Completion is
 // waited for explicitly with wait_vmcnt, on a fixed per-step issue schedule.
+//
+// The compiler's hazard recognizer does not see into inline asm, so the asm
+// carries the wait states gfx9 requires before these loads itself: one after
+// an SALU write of M0 (the LDS destination) and five after a VALU write of an
+// SGPR that the load reads (the readfirstlane that forms an SGPR base).
 __device__ __forceinline__ void dma16(const void *gaddr, uint32_t lds_base)
 {
-    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gaddr), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 : : "v"(gaddr), "{m0}"(lds_base) : "memory");
+}
+
+// The same load addressed as a wave-uniform SGPR base plus a per-lane 32-bit
+// offset, which needs no per-lane address arithmetic.  The base goes through
+// readfirstlane so that it is held in SGPRs; FIRST marks the first load after
+// the base was formed, which must wait out the VALU-to-SGPR hazard.
+template <bool FIRST>
+__device__ __forceinline__ void dma16_s(const void *base, uint32_t voff, uint32_t lds_base)
+{
+    const uint64_t u = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    const void *sbase = (const void *)(((uint64_t)hi << 32) | lo);
+    if (FIRST)
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                     : : "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     : : "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -160,19 +186,43 @@ __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Lanes n, n+16, n+32, n+48 hold the same row.
+// Lanes n, n+16, n+32, n+48 hold the same row.  The permlane swaps give every
+// lane {v[l], v[l^32]} and then {v[l], v[l^16]}, each pair in the same order on
+// all four lanes of a row, so the results are bitwise equal across the row.
+// Both halves of a swap are copied to scalars before any bit_cast: clang's
+// __builtin_bit_cast of a vector element reads element 0 whatever the index.
+__device__ __forceinline__ void swap32(float v, float &x0, float &x1)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    x0 = __builtin_bit_cast(float, r0);
+    x1 = __builtin_bit_cast(float, r1);
+}
+
+__device__ __forceinline__ void swap16(float v, float &x0, float &x1)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    x0 = __builtin_bit_cast(float, r0);
+    x1 = __builtin_bit_cast(float, r1);
+}
+
 __device__ __forceinline__ float max_over_groups(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
+    float a, b;
+    swap32(v, a, b);
+    swap16(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float sum_over_groups(float v)
 {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
+    float a, b;
+    swap32(v, a, b);
+    swap16(a + b, a, b);
+    return a + b;
 }
 
 template <int D>
@@ -225,6 +275,25 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int R = a.rows, G = a.group;
     const int ps = a.page_size;
 
+    // ---- query fragments: B operand of S^T = K Q^T (issued first, so their
+    //      latency overlaps the length and page-table reads) ------------------
+    QFrag qf[kRowBlocks][C::KB];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = rb * 16 + n;
+        const bool live = r < R;
+        const int i = live ? r / G : 0;
+        const int h = kvh * G + (live ? r - i * G : 0);
+        const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + i) * a.num_heads + h) * D;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (live)
+                v = *(const uint4 *)(qrow + kb * 32 + g * 8);
+            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
+        }
+    }
+
     // ---- lengths -----------------------------------------------------------
     int lmax = 0;
     int lrow[kRowBlocks] = {0, 0, 0};
@@ -267,25 +336,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         slots[i] = int2v{phys, tb};
     }
 
-    // ---- query fragments: B operand of S^T = K Q^T ---------------------------
-    QFrag qf[kRowBlocks][C::KB];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-        const bool live = r < R;
-        const int i = live ? r / G : 0;
-        const int h = kvh * G + (live ? r - i * G : 0);
-        const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + i) * a.num_heads + h) * D;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (live)
-                v = *(const uint4 *)(qrow + kb * 32 + g * 8);
-            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
-        }
-    }
     // Q and the slot table are in before any direct-to-LDS load is issued, so no
-    // later wait on them can also drain the K/V pipeline.
+    // later wait on them can also drain the K/V pipeline.  Q only ever feeds
+    // MFMA as the B operand: it is kept in AGPRs, leaving the VGPRs to the
+    // accumulators and the per-step working set.
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+            asm volatile("" : "+a"(qf[rb][kb]));
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -345,16 +404,35 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 end_b = phys_b >= 0 ? min(end_b, na + lmax - tb_b) : 0;
             }
             const int64_t base_a = (int64_t)phys_a * a.page_stride + (int64_t)ua * a.token_stride + head_off;
-            const int64_t base_b = (int64_t)phys_b * a.page_stride - (int64_t)na * a.token_stride + head_off;
+            if (na == kSub && end_a == kSub) {
+                // the whole block is valid and inside one page: SGPR base + lane offset
+                const uint8_t *sb = pool + base_a;
 #pragma unroll
-            for (int i = 0; i < C::DMA; ++i) {
-                const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
-                const bool in_b = r >= na;
-                const bool ok = in_b ? (r < end_b) : (r < end_a);
-                const int64_t src = ok ? (in_b ? base_b : base_a) + loff[i] : 0;
-                dma16(pool + src, dst + i * 1024);
-                if (SPARSE && tokst != nullptr && cp == 0)
-                    tokst[w * kSub + r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
+                for (int i = 0; i < C::DMA; ++i) {
+                    if (i == 0)
+                        dma16_s<true>(sb, (uint32_t)loff[i], dst);
+                    else
+                        dma16_s<false>(sb, (uint32_t)loff[i], dst + i * 1024);
+                }
+                if (SPARSE && tokst != nullptr && cp == 0) {
+#pragma unroll
+                    for (int i = 0; i < C::DMA; ++i) {
+                        const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
+                        tokst[w * kSub + r] = tb_a + ua + r;
+                    }
+                }
+            } else {
+                const int64_t base_b = (int64_t)phys_b * a.page_stride - (int64_t)na * a.token_stride + head_off;
+#pragma unroll
+                for (int i = 0; i < C::DMA; ++i) {
+                    const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
+                    const bool in_b = r >= na;
+                    const bool ok = in_b ? (r < end_b) : (r < end_a);
+                    const int64_t src = ok ? (in_b ? base_b : base_a) + loff[i] : 0;
+                    dma16(pool + src, dst + i * 1024);
+                    if (SPARSE && tokst != nullptr && cp == 0)
+                        tokst[w * kSub + r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
+                }
             }
         } else {
 #pragma unroll
@@ -441,7 +519,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         }
         const int tfirst = pos0 + w * kSub + 8 * g;
         uint32_t vis[kRowBlocks];
-        float y[kRowBlocks][8];
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) {
             if (!SPARSE) {
@@ -454,22 +531,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     m |= (tok[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid tok = INT32_MAX
                 vis[rb] = m;
             }
+            // c > 0, so the largest logit comes from the largest raw score
             float mloc = -INFINITY;
             if (__all(vis[rb] == 0xFFu)) {
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    y[rb][jj] = s[rb][jj >> 2][jj & 3] * c;
-                    mloc = fmaxf(mloc, y[rb][jj]);
-                }
+                for (int jj = 0; jj < 8; ++jj)
+                    mloc = fmaxf(mloc, s[rb][jj >> 2][jj & 3]);
             } else if (!__all(vis[rb] == 0u)) {
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const float v = s[rb][jj >> 2][jj & 3] * c;
-                    y[rb][jj] = ((vis[rb] >> jj) & 1u) ? v : -INFINITY;
-                    mloc = fmaxf(mloc, y[rb][jj]);
-                }
+                for (int jj = 0; jj < 8; ++jj)
+                    mloc = fmaxf(mloc, ((vis[rb] >> jj) & 1u) ? s[rb][jj >> 2][jj & 3] : -INFINITY);
             }
-            mloc = max_over_groups(mloc);
+            mloc = max_over_groups(mloc) * c;
             if (g == 0)
                 xmax[w][rb * 16 + n] = mloc;
         }
@@ -494,16 +567,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     acc[rb][d] *= alpha;
                 m_ref[rb] = mt;
             }
-            const float mu = (m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb];
+            // p = 2^(logit - m_ref + 6) = exp2(fma(s, c, 6 - m_ref)): P carries 2^6
+            const float bias = kPLog2 - ((m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb]);
             half8 ph = {}, pl = {};
             if (!__all(vis[rb] == 0u)) {
+                const bool full = __all(vis[rb] == 0xFFu);
                 float lsum = 0.0f;
 #pragma unroll
                 for (int jj = 0; jj < 8; jj += 2) {
-                    const float p0 = exp2f(y[rb][jj] - mu);
-                    const float p1 = exp2f(y[rb][jj + 1] - mu);
-                    lsum += p0 + p1;
-                    const float s0 = p0 * kPScale, s1 = p1 * kPScale;
+                    float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
+                    float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
+                    if (!full) {
+                        a0 = ((vis[rb] >> jj) & 1u) ? a0 : -INFINITY;
+                        a1 = ((vis[rb] >> (jj + 1)) & 1u) ? a1 : -INFINITY;
+                    }
+                    const float s0 = exp2f(a0), s1 = exp2f(a1);
+                    lsum += s0 + s1;
                     const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s0) & 0xFFFFE000u);
                     const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s1) & 0xFFFFE000u);
                     const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
@@ -600,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r = rb * 16 + n;
         if (r < R) {
-            // everything accumulated is relative to m_ref; P also carried 2^6
+            // acc and l are relative to m_ref and both carry the 2^6 of P
             const float sc = (m_ref[rb] == -INFINITY) ? 0.0f : exp2f(m_ref[rb] - m_true[rb]);
             const float sa = sc * kPUnscale;
             const int i = r / G, h = kvh * G + (r - i * G);
@@ -616,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 for (int v = 0; v < kWaves; ++v)
                     L += xl[v][r];
                 a.ws_max[ws_base + orow] = m_true[rb];
-                a.ws_sum[ws_base + orow] = L * sc;
+                a.ws_sum[ws_base + orow] = L * sa;
             }
         }
     }
