@@ -24,21 +24,55 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+CODEGEN_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the
+    # (rare) accumulator rescale in the verify kernel
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+]
+
+# sources whose kernels issue direct-to-LDS loads as inline asm
+ASM_DMA_SOURCES = ["verify_mfma.hip"]
+
+
+def check_hazards(extra_flags=()) -> None:
+    """Compile the inline-asm DMA sources to gfx950 assembly and reject the
+    build if a load lacks the wait states gfx9 requires before it."""
+    try:
+        from . import asm_hazards
+    except ImportError:          # run as a script
+        import asm_hazards
+
+    for name in ASM_DMA_SOURCES:
+        src = os.path.join(CSRC, name)
+        asm = os.path.join(HERE, name + ".s.tmp")
+        cmd = [hipcc(), *CODEGEN_FLAGS, "--cuda-device-only", "-S",
+               "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra_flags, src, "-o", asm]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc -S failed:\n" + r.stdout + r.stderr)
+        with open(asm) as f:
+            found = asm_hazards.check(f.read())
+        os.remove(asm)
+        if found:
+            lines = "\n".join(f"  {k}: {p}  ->  {t}" for k, p, t in found[:10])
+            raise RuntimeError(f"{name}: {len(found)} unprotected hazards before "
+                               f"direct-to-LDS loads:\n{lines}")
+
+
 def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = out + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), *CODEGEN_FLAGS, "-fPIC", "-shared",
            "-Wall", "-Werror", "-Wno-unused-function",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the
-           # (rare) accumulator rescale in the verify kernel
-           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra_flags, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
     if verbose:
         print(r.stderr)
+    check_hazards(extra_flags)
     os.replace(tmp, out)
     return out
 
