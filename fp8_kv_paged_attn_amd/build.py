@@ -27,9 +27,6 @@ def hipcc() -> str:
 CODEGEN_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the
-    # (rare) accumulator rescale in the verify kernel
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 # sources whose kernels issue direct-to-LDS loads as inline asm

@@ -7,29 +7,32 @@
 // on an MI355X:
 //
 //  * One workgroup per (split, KV unit): four waves, one per SIMD.  The split
-//    is walked in macro-steps of 128 tokens.  Wave w owns tokens [32w, 32w+32)
-//    of each macro-step for S = Q K^T and owns d-quarter w of the output for
-//    P.V, so the FP32 accumulator of a wave is 48 rows x D/4 columns (48
-//    registers at D = 256) and no end-of-kernel reduction of accumulators is
-//    needed.  P and the per-row step maxima are exchanged through LDS.
-//  * K/V bytes move HBM -> LDS with direct-to-LDS 16-byte loads (no VGPRs).
-//    Two stages per plane; K is prefetched two macro-steps ahead, V one.
-//    16-byte chunks of each token row are XOR-swizzled so that the MFMA
-//    operand reads are free of LDS bank conflicts.
+//    is cut into 32-token blocks dealt to the waves in turn; each wave runs the
+//    whole attention (S = Q K^T, online softmax, O += P V over all D columns)
+//    on its own blocks, with its own running max and sum.  The main loop has
+//    no barrier and no exchange between waves; the four partial states are
+//    merged once, through LDS, at the end of the split.
+//  * K/V bytes move HBM -> LDS with direct-to-LDS 16-byte loads (no VGPRs),
+//    into two stages per plane per wave, two blocks ahead, on a fixed issue
+//    schedule so that the wait counts are the same every step.  The 16-byte
+//    chunks of each token row are XOR-swizzled so that the MFMA operand reads
+//    are free of LDS bank conflicts.
 //  * E4M3 -> FP16 (or BF16 for a BF16 query) with the hardware converter,
 //    which is exact for every finite code.
 //  * S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K is the A operand (one
 //    ds_read_b64 per lane per 32 dims), Q^T the B operand, in registers for the
 //    whole kernel.  The 16 tokens of each MFMA are ordered so that each lane's
 //    8 scores of a 32-token block are exactly the 8 P^T elements it provides to
-//    P.V: the P^T fragments are written to LDS as they are, 16 bytes per lane.
+//    P.V, so P never leaves the registers.
 //  * O^T += V^T P^T: V^T fragments come straight from LDS with ds_read_tr8_b64
 //    (the transposing read).  P is split into FP16 hi + lo parts and both are
 //    multiplied ("compensated probabilities", design note first section);
-//    every product is exact in FP32.
-//  * The running reference max of a row moves only when a step exceeds it by
-//    more than 2^8, so P <= 2^8 and accumulator rescales are rare; the partial
-//    written out uses the exact row max.
+//    every product is exact in FP32.  A wave's FP32 accumulator is 48 rows x D.
+//  * Row blocks (16 rows) in which no row sees any token are skipped: the main
+//    loop is instantiated for 1, 2 or 3 row blocks.
+//  * The running reference max of a row moves only when a block exceeds it by
+//    more than 2^8, so P <= 2^14 in FP16 and accumulator rescales are rare;
+//    the partial written out uses the exact row max.
 //  * Tokens a row must not see get score -inf by select, and V bytes of
 //    positions no row sees are zeroed by select before P.V, so NaN bytes in
 //    padding pages cannot leak (null-block fix of 1Cat-vLLM PR #702).
@@ -38,13 +41,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSub = 32;                  // tokens per wave per macro-step
-constexpr int kMacro = kSub * kWaves;     // tokens per macro-step
+constexpr int kSub = 32;                  // tokens of one wave block
+constexpr int kMacro = kSub * kWaves;     // tokens per macro-step (all waves)
 constexpr int kRowBlocks = 3;             // 48 rows
 constexpr float kLazy = 8.0f;             // reference-max slack (log2 units)
 constexpr float kPLog2 = 6.0f;            // P is carried as 2^6 * p (FP16 normal range)
@@ -57,7 +62,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Unsigned division by the page size: q = (n * m) >> s for 0 <= n < 2^31.
 struct DivMagic {
@@ -91,18 +95,6 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS data.  __syncthreads() (and any release fence on
-// LDS) makes the compiler drain every in-flight direct-to-LDS load first, which
-// would empty the prefetch pipeline at each barrier.  Here the wave's own LDS
-// stores are completed (lgkmcnt 0), the direct loads that other waves will read
-// are waited for explicitly by the caller, and the asm memory clobber keeps the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void barrier_lds()
-{
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
-    asm volatile("s_barrier" ::: "memory");
 }
 
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from gaddr land at
@@ -225,18 +217,44 @@ __device__ __forceinline__ float sum_over_groups(float v)
     return a + b;
 }
 
+// x *= f, one accumulator fragment at a time: the volatile asm keeps the
+// compiler from reading a whole accumulator array out of AGPRs at once.
+__device__ __forceinline__ void scale_in_place(f32x4 &x, float f)
+{
+    f32x4 t = x;
+    asm volatile("" : "+v"(t));
+    t *= f;
+    asm volatile("" : "+v"(t));
+    x = t;
+}
+
+// Max over lanes 0..7 (the row lengths of one request), broadcast to the wave.
+__device__ __forceinline__ int max8_broadcast(int v)
+{
+    v = max(v, __shfl_xor(v, 1, 64));
+    v = max(v, __shfl_xor(v, 2, 64));
+    v = max(v, __shfl_xor(v, 4, 64));
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 template <int D>
 struct Cfg {
     static constexpr int KB = D / 32;                 // QK k-blocks
-    static constexpr int DBW = D / 16 / kWaves;       // PV d-blocks per wave
+    static constexpr int DB = D / 16;                 // PV d-blocks (all of D per wave)
+    static constexpr int DQ = DB / kWaves;            // d-blocks of one output quarter
     static constexpr int BLOCK = kSub * D;            // bytes of one wave's 32 rows
-    static constexpr int DMA = BLOCK / 1024;          // 1 KB direct loads per plane
+    static constexpr int DMA = BLOCK / 1024;          // 1 KB direct loads per stage
     static constexpr int ROWS_PER_DMA = 1024 / D;
     static constexpr int LANES_PER_ROW = D / 16;
+    static constexpr int STAGES = 2 * 2 * kWaves * BLOCK;           // K and V, two stages
+    // end-of-split merge: each wave leaves its three foreign output quarters
+    static constexpr int QUARTER = kRowBlocks * DQ * 64 * 16;       // bytes per (wave, quarter)
+    static constexpr int MERGE = kWaves * (kWaves - 1) * QUARTER;
+    static constexpr int SHARED = STAGES > MERGE ? STAGES : MERGE;
 };
 
-constexpr int kMaxSlotsD256 = 512;
-constexpr int kMaxSlotsD128 = 1024;
+constexpr int kMaxSlotsD256 = 1024;
+constexpr int kMaxSlotsD128 = 2048;
 
 template <int D>
 constexpr int max_slots()
@@ -250,21 +268,19 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     typedef Cfg<D> C;
     typedef typename Frag<SPARSE>::T QFrag;
     constexpr int kSlots = max_slots<D>();
+    constexpr int kEnt = (kSlots + kThreads - 1) / kThreads;
 
-    // stage planes: [wave block][32 rows][D], swizzled
-    __shared__ __attribute__((aligned(16))) uint8_t k_s0[kWaves * C::BLOCK];
-    __shared__ __attribute__((aligned(16))) uint8_t k_s1[kWaves * C::BLOCK];
-    __shared__ __attribute__((aligned(16))) uint8_t v_s0[kWaves * C::BLOCK];
-    __shared__ __attribute__((aligned(16))) uint8_t v_s1[kWaves * C::BLOCK];
-    // P^T fragments: [token block kk][row block][hi, lo][64 lanes] x 16 bytes
-    __shared__ __attribute__((aligned(16))) int4v p_s[kWaves][kRowBlocks][2][64];
+    // K/V stages during the split, the merge area after it.  Stage layout:
+    // [K0 | K1 | V0 | V1], each [wave][32 rows][D] with swizzled chunks.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::SHARED];
     __shared__ int2v slots[kSlots];                 // (physical page, first token) per slot
-    __shared__ __attribute__((aligned(16))) int32_t tok_s[2][kMacro];   // sparse: token per position
-    __shared__ float xmax[kWaves][16 * kRowBlocks];
-    __shared__ float xl[kWaves][16 * kRowBlocks];
+    __shared__ __attribute__((aligned(16))) int32_t tok_s[kWaves][2][kSub];   // sparse tokens
+    __shared__ float xm[kWaves][16 * kRowBlocks];   // merge: per-wave row max
+    __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave scaled row sum
+    __shared__ float xf[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator scale
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
@@ -275,8 +291,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int R = a.rows, G = a.group;
     const int ps = a.page_size;
 
-    // ---- query fragments: B operand of S^T = K Q^T (issued first, so their
-    //      latency overlaps the length and page-table reads) ------------------
+    uint8_t *const k_st = smem;                               // [2][kWaves][BLOCK]
+    uint8_t *const v_st = smem + 2 * kWaves * C::BLOCK;       // [2][kWaves][BLOCK]
+
+    // ---- one round trip: Q fragments, row lengths, page table -------------
+    // Q^T is the B operand of S^T = K Q^T: lane (n, g) holds row 16rb + n.
+    // The head dimension is walked in a permuted order that both operands
+    // share: MFMA k-block kb = 2t + e, lane group g covers dims
+    // 64t + 16g + 8e .. +7, so that one 16-byte LDS chunk (dims 64t + 16g ..
+    // +15) feeds two consecutive k-blocks of K.
     QFrag qf[kRowBlocks][C::KB];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
@@ -289,67 +312,73 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         for (int kb = 0; kb < C::KB; ++kb) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (live)
-                v = *(const uint4 *)(qrow + kb * 32 + g * 8);
+                v = *(const uint4 *)(qrow + 64 * (kb >> 1) + 16 * g + 8 * (kb & 1));
             qf[rb][kb] = __builtin_bit_cast(QFrag, v);
         }
     }
-
-    // ---- lengths -----------------------------------------------------------
-    int lmax = 0;
-    int lrow[kRowBlocks] = {0, 0, 0};
-    for (int i = 0; i < a.q_rows; ++i) {
-        int L = a.row_lens[(int64_t)b * a.q_rows + i];
-        L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-        lmax = max(lmax, L);
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            const int r = rb * 16 + n;
-            if (r < R && r / G == i)
-                lrow[rb] = L;
-        }
+    int lmine = 0;                                  // lane i < q_rows: length of query row i
+    if (lane < a.q_rows) {
+        lmine = a.row_lens[(int64_t)b * a.q_rows + lane];
+        lmine = lmine < 0 ? 0 : (lmine > a.len_cap ? a.len_cap : lmine);
     }
     const int lo = split * a.tokens_per_split;
-    int hi = min(lo + a.tokens_per_split, a.list_len);
-    if (!SPARSE)
-        hi = min(hi, lmax);
-
-    // ---- page slots of this split (the host guarantees they fit) -----------
+    const int hi_list = min(lo + a.tokens_per_split, a.list_len);
     const int32_t *table = SPARSE ? a.block_table + (int64_t)b * a.table_stride : a.block_table;
     int slot0 = 0, nslots = 0;
-    if (hi > lo) {
+    if (hi_list > lo) {
         slot0 = divp(lo, dm);
-        nslots = min(divp(hi - 1, dm) + 1 - slot0, kSlots);
+        nslots = min(divp(hi_list - 1, dm) + 1 - slot0, kSlots);
     }
-    for (int i = tid; i < nslots; i += kThreads) {
-        const int slot = slot0 + i;
-        int phys = -1, tb = 0;
-        if (!SPARSE) {
-            phys = table[slot];
-            tb = slot * ps;
-        } else {
-            const int blk = a.sel[((int64_t)b * a.num_kv_heads + kvh) * a.topk + slot];
-            if (blk >= 0 && (int64_t)blk * ps < lmax) {
-                phys = table[blk];
-                tb = blk * ps;
+    // table entries of this split's slots (dense) or its selected blocks (sparse)
+    int ent[kEnt];
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+        const int i = tid + k * kThreads;
+        ent[k] = -1;
+        if (i < nslots)
+            ent[k] = SPARSE ? a.sel[((int64_t)b * a.num_kv_heads + kvh) * a.topk + slot0 + i]
+                            : table[slot0 + i];
+    }
+    const int lmax = max8_broadcast(lmine);
+    int lrow[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = rb * 16 + n;
+        const int lr = __shfl(lmine, r < R ? r / G : 0, 64);
+        lrow[rb] = r < R ? lr : 0;
+    }
+    // row blocks up to the last one with a row that sees a token
+    int nrb = 1;
+#pragma unroll
+    for (int rb = 1; rb < kRowBlocks; ++rb)
+        if (__any(lrow[rb] > 0))
+            nrb = rb + 1;
+    int hi = hi_list;
+    if (!SPARSE)
+        hi = min(hi, lmax);
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < nslots) {
+            int phys = -1, tb = 0;
+            if (!SPARSE) {
+                phys = ent[k];
+                tb = (slot0 + i) * ps;
+            } else {
+                const int blk = ent[k];
+                if (blk >= 0 && (int64_t)blk * ps < lmax) {
+                    phys = table[blk];
+                    tb = blk * ps;
+                }
             }
+            slots[i] = int2v{phys, tb};
         }
-        slots[i] = int2v{phys, tb};
     }
-
-    // Q and the slot table are in before any direct-to-LDS load is issued, so no
-    // later wait on them can also drain the K/V pipeline.  Q only ever feeds
-    // MFMA as the B operand: it is kept in AGPRs, leaving the VGPRs to the
-    // accumulators and the per-step working set.
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-            asm volatile("" : "+a"(qf[rb][kb]));
-    wait_vmcnt<0>();
     __syncthreads();
 
     const int64_t head_off = (int64_t)kvh * a.head_stride;
-    const int nms = hi > lo ? (hi - lo + kMacro - 1) / kMacro : 0;  // macro-steps
+    // this wave's blocks: positions lo + 32 (4j + w), j = 0 .. nms-1
+    const int nms = hi > lo ? (hi - lo + kMacro - 1) / kMacro : 0;
 
     // Position -> (byte offset of the K/V head row, token, valid).  Branch-free;
     // the slot cache is the only table read.
@@ -366,12 +395,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         return ok;
     };
 
-    // Direct-to-LDS loads of this wave's 32 rows of macro-step j into one plane.
-    // Lane l loads, in load i, row r_i = i*ROWS_PER_DMA + l/LANES_PER_ROW, swizzled
-    // chunk position l%LANES_PER_ROW.  With pages of at least 32 tokens a wave's
-    // block spans at most two page slots, so the page lookup is done once per
-    // block (wave-uniform) and a lane only adds its precomputed row offset; small
-    // pages or very large token strides take the per-row resolve.
+    // Direct-to-LDS loads of this wave's block j into one stage.  Lane l loads,
+    // in load i, row r_i = i*ROWS_PER_DMA + l/LANES_PER_ROW, swizzled chunk
+    // position l%LANES_PER_ROW.  With pages of at least 32 tokens a block spans
+    // at most two page slots, so the page lookup is done once per block
+    // (wave-uniform) and a lane only adds its precomputed row offset; small
+    // pages or very large token strides take the per-row resolve.  Positions
+    // past the end load an in-bounds dummy address, so that every step issues
+    // the same number of loads.  tokst (sparse, V loads only) receives the
+    // token of each row, INT32_MAX for rows no query sees.
     const int cp = lane % C::LANES_PER_ROW;
     const bool two_slot = ps >= kSub && a.token_stride < (1 << 25);
     int32_t loff[C::DMA];
@@ -380,11 +412,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
         loff[i] = two_slot ? r * (int32_t)a.token_stride + 16 * (cp ^ swz<D>(r)) : 0;
     }
-    auto issue_plane = [&](int j, const uint8_t *pool, uint8_t *plane, int32_t *tokst)
+    auto issue_plane = [&](int j, const uint8_t *pool, uint8_t *stage, int32_t *tokst)
         __attribute__((always_inline)) {
-        const int pos0 = lo + j * kMacro + w * kSub;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(plane + w * C::BLOCK));
-        // the stage being refilled was read by this wave's previous step
+        const int pos0 = lo + (j * kWaves + w) * kSub;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + w * C::BLOCK));
+        // the stage being refilled was read by this wave's previous use of it
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         if (two_slot) {
             const int sa = divp(pos0, dm);
@@ -418,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                     for (int i = 0; i < C::DMA; ++i) {
                         const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
-                        tokst[w * kSub + r] = tb_a + ua + r;
+                        tokst[r] = tb_a + ua + r;
                     }
                 }
             } else {
@@ -431,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     const int64_t src = ok ? (in_b ? base_b : base_a) + loff[i] : 0;
                     dma16(pool + src, dst + i * 1024);
                     if (SPARSE && tokst != nullptr && cp == 0)
-                        tokst[w * kSub + r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
+                        tokst[r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
                 }
             }
         } else {
@@ -444,17 +476,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 const int64_t src = ok ? off + 16 * (cp ^ swz<D>(row)) : 0;
                 dma16(pool + src, dst + i * 1024);
                 if (SPARSE && tokst != nullptr && cp == 0)
-                    tokst[w * kSub + row] = ok ? t : INT32_MAX;
+                    tokst[row] = ok ? t : INT32_MAX;
             }
         }
     };
 
-    // ---- state -------------------------------------------------------------
-    f32x4 acc[kRowBlocks][C::DBW];
+    // ---- per-wave state ------------------------------------------------------
+    f32x4 acc[kRowBlocks][C::DB];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
-        for (int d = 0; d < C::DBW; ++d)
+        for (int d = 0; d < C::DB; ++d)
             acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_true[kRowBlocks], m_ref[kRowBlocks], l_part[kRowBlocks];
 #pragma unroll
@@ -465,237 +497,297 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     const float c = a.logit_scale;
 
-    // One macro-step on the stage pair (kst, vst).  Every step issues K(j+2)
-    // after its QK and V(j+1) after its step-max barrier; past the end of the
-    // split these are dummy loads (every position invalid) into stages that are
-    // not read again, so the wait counts below are the same for every step:
-    //  * before QK(j), the groups issued after K(j) are V(j-1), K(j+1), V(j);
-    //    V(j-1) is complete already (P.V of step j-1 waited for it), so leaving
-    //    two groups in flight means K(j) has landed (steps 0 and 1 have exactly
-    //    two later groups: V(0), K(1) and K(2), V(1));
-    //  * before the P.V barrier, the groups issued after V(j) are K(j+2) and
-    //    V(j+1) (step 0 also has K(1), so it waits a little longer).
-    auto step = [&](int j, uint8_t *kst, uint8_t *vst, uint8_t *kst_next2, uint8_t *vst_next1,
-                    int32_t *tok_cur, int32_t *tok_next1) __attribute__((always_inline)) {
-        const int pos0 = lo + j * kMacro;
-        wait_vmcnt<2 * C::DMA>();
+    // Per-lane parts of the LDS read addresses.  Stage bases are multiples of
+    // the block size, so a 16-byte chunk index can be XORed into an address.
+    //  K (A operand of QK): lane (n, g) reads rows 8(n/4) + 4bb + n%4 (MFMA row
+    //    n of token block bb), chunk 4t + g, i.e. dims 64t + 16g .. +15.
+    //  V^T (A operand of P.V): the transposing read's supplier lane (n, g)
+    //    points at row 8g + n/2, byte 8(n%2) of d-block db's chunk.
+    uint32_t koff[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+        const int krow = 8 * (n >> 2) + 4 * bb + (n & 3);
+        koff[bb] = krow * D + ((g ^ swz<D>(krow)) << 4);
+    }
+    const int vrow = 8 * g + (n >> 1);
+    const uint32_t voff = vrow * D + (swz<D>(vrow) << 4) + ((n & 1) << 3);
 
-        // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
-        f32x4 s[kRowBlocks][2];
+    // Zero V rows [from, 32) of this wave's stage: V bytes of positions that no
+    // query sees must not reach P.V (they may be NaN).  Rare: the last block of
+    // a split, or a sparse block cut by the lengths.
+    const uint32_t rowbit = 1u << (lane / C::LANES_PER_ROW);   // row of this lane in a 1 KB load
+    auto zero_v_rows = [&](uint8_t *vst, uint32_t keep) __attribute__((always_inline)) {
+        uint8_t *blk = vst + w * C::BLOCK;
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
-            s[rb][0] = s[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint8_t *kblk = kst + w * C::BLOCK;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            // MFMA row m of block bb is token 8(m/4) + 4bb + m%4
-            const int krow = 8 * (n >> 2) + 4 * bb + (n & 3);
-            const uint8_t *kr = kblk + krow * D + ((g & 1) << 3);
-            const int sw = swz<D>(krow);
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-                const int2v raw = *(const int2v *)(kr + (((2 * kb + (g >> 1)) ^ sw) << 4));
-                QFrag kf;
-                if (SPARSE)
-                    kf = __builtin_bit_cast(QFrag, dec_bf16(raw));
-                else
-                    kf = __builtin_bit_cast(QFrag, dec_f16(raw));
-#pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb)
-                    s[rb][bb] = mfma_qk(kf, qf[rb][kb], s[rb][bb]);
-            }
-        }
-        issue_plane(j + 2, a.k_pool, kst_next2, nullptr);
-
-        // ---- visibility of this lane's 8 scores (tokens 32w + 8g + jj) ---------
-        // vis[rb] bit jj: row 16rb + n sees token jj.  Row blocks that see the
-        // whole block skip the selects; blocks that see none of it skip P.
-        int tok[8];
-        if (SPARSE) {
-            const int4v t0 = *(const int4v *)&tok_cur[w * kSub + 8 * g];
-            const int4v t1 = *(const int4v *)&tok_cur[w * kSub + 8 * g + 4];
-            tok[0] = t0.x; tok[1] = t0.y; tok[2] = t0.z; tok[3] = t0.w;
-            tok[4] = t1.x; tok[5] = t1.y; tok[6] = t1.z; tok[7] = t1.w;
-        }
-        const int tfirst = pos0 + w * kSub + 8 * g;
-        uint32_t vis[kRowBlocks];
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            if (!SPARSE) {
-                const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
-                vis[rb] = (1u << nv) - 1u;
-            } else {
-                uint32_t m = 0;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    m |= (tok[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid tok = INT32_MAX
-                vis[rb] = m;
-            }
-            // c > 0, so the largest logit comes from the largest raw score
-            float mloc = -INFINITY;
-            if (__all(vis[rb] == 0xFFu)) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    mloc = fmaxf(mloc, s[rb][jj >> 2][jj & 3]);
-            } else if (!__all(vis[rb] == 0u)) {
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    mloc = fmaxf(mloc, ((vis[rb] >> jj) & 1u) ? s[rb][jj >> 2][jj & 3] : -INFINITY);
-            }
-            mloc = max_over_groups(mloc) * c;
-            if (g == 0)
-                xmax[w][rb * 16 + n] = mloc;
-        }
-        barrier_lds();   // step maxima published; every wave is past P.V of step j-1
-        issue_plane(j + 1, a.v_pool, vst_next1, tok_next1);
-
-        // ---- online softmax with the shared reference max --------------------
-#pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
-            float mstep = xmax[0][rb * 16 + n];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v)
-                mstep = fmaxf(mstep, xmax[v][rb * 16 + n]);
-            const float mt = fmaxf(m_true[rb], mstep);
-            m_true[rb] = mt;
-            // identical inputs in every wave, so every wave takes the same branch
-            if (__any(mt > m_ref[rb] + kLazy)) {
-                const float alpha = (mt == -INFINITY) ? 1.0f : exp2f(m_ref[rb] - mt);
-                l_part[rb] *= alpha;
-#pragma unroll
-                for (int d = 0; d < C::DBW; ++d)
-                    acc[rb][d] *= alpha;
-                m_ref[rb] = mt;
-            }
-            // p = 2^(logit - m_ref + 6) = exp2(fma(s, c, 6 - m_ref)): P carries 2^6
-            const float bias = kPLog2 - ((m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb]);
-            half8 ph = {}, pl = {};
-            if (!__all(vis[rb] == 0u)) {
-                const bool full = __all(vis[rb] == 0xFFu);
-                float lsum = 0.0f;
-#pragma unroll
-                for (int jj = 0; jj < 8; jj += 2) {
-                    float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
-                    float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
-                    if (!full) {
-                        a0 = ((vis[rb] >> jj) & 1u) ? a0 : -INFINITY;
-                        a1 = ((vis[rb] >> (jj + 1)) & 1u) ? a1 : -INFINITY;
-                    }
-                    const float s0 = exp2f(a0), s1 = exp2f(a1);
-                    lsum += s0 + s1;
-                    const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s0) & 0xFFFFE000u);
-                    const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, s1) & 0xFFFFE000u);
-                    const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
-                    const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(s0 - h0, s1 - h1));
-                    ph[jj] = hh.x;
-                    ph[jj + 1] = hh.y;
-                    pl[jj] = ll.x;
-                    pl[jj + 1] = ll.y;
-                }
-                l_part[rb] += lsum;
-            }
-            p_s[w][rb][0][lane] = __builtin_bit_cast(int4v, ph);
-            p_s[w][rb][1][lane] = __builtin_bit_cast(int4v, pl);
-        }
-        wait_vmcnt<2 * C::DMA>();   // V(j) landed; K(j+2), V(j+1) may fly
-        barrier_lds();   // P^T of all four token blocks and V(j) are in LDS
-
-        // ---- O^T[d-quarter w] += V^T P^T over the 128 tokens ------------------
-#pragma unroll
-        for (int kk = 0; kk < kWaves; ++kk) {
-            half8 ph[kRowBlocks], pl[kRowBlocks];
-#pragma unroll
-            for (int rb = 0; rb < kRowBlocks; ++rb) {
-                ph[rb] = __builtin_bit_cast(half8, p_s[kk][rb][0][lane]);
-                pl[rb] = __builtin_bit_cast(half8, p_s[kk][rb][1][lane]);
-            }
-            // V rows of token block kk that no row may see are zeroed (select)
-            uint32_t vm_lo = 0xFFFFFFFFu, vm_hi = 0xFFFFFFFFu;
-            const int tbase = pos0 + kk * kSub + 8 * g;
-            if (!SPARSE) {
-                if (pos0 + kMacro > hi) {
-                    vm_lo = 0;
-                    vm_hi = 0;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        vm_lo |= (tbase + jj < hi) ? (0xFFu << (8 * jj)) : 0u;
-                        vm_hi |= (tbase + 4 + jj < hi) ? (0xFFu << (8 * jj)) : 0u;
-                    }
-                }
-            } else {
-                vm_lo = 0;
-                vm_hi = 0;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    vm_lo |= (tok_cur[kk * kSub + 8 * g + jj] != INT32_MAX) ? (0xFFu << (8 * jj)) : 0u;
-                    vm_hi |= (tok_cur[kk * kSub + 8 * g + 4 + jj] != INT32_MAX) ? (0xFFu << (8 * jj)) : 0u;
-                }
-            }
-            // supplier lane (n, g) of the transposing read points at row 8g + n/2,
-            // half n%2 of the 16-byte chunk of d-block db
-            const int vrow = 8 * g + (n >> 1);
-            const uint8_t *vr = vst + kk * C::BLOCK + vrow * D + ((n & 1) << 3);
-            const int vsw = swz<D>(vrow);
-#pragma unroll
-            for (int d = 0; d < C::DBW; ++d) {
-                const int db = w * C::DBW + d;
-                int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(vr + ((db ^ vsw) << 4)));
-                raw.x &= (int)vm_lo;
-                raw.y &= (int)vm_hi;
-                const half8 vf = dec_f16(raw);
-#pragma unroll
-                for (int rb = 0; rb < kRowBlocks; ++rb) {
-                    acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[rb], acc[rb][d], 0, 0, 0);
-                    acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][d], 0, 0, 0);
-                }
-            }
+        for (int i = 0; i < C::DMA; ++i) {
+            if (!((keep >> (i * C::ROWS_PER_DMA)) & rowbit))
+                *(int4v *)(blk + i * 1024 + lane * 16) = int4v{0, 0, 0, 0};
         }
     };
 
-    // ---- pipeline ------------------------------------------------------------
+    // One block of this wave (step j) with NRB live row blocks.  Block j uses K
+    // stage j%2 and V stage j%2.  Issue order: K0 V0 K1 V1 (prologue), then in
+    // step j: K(j+2) after QK(j), V(j+2) after P.V(j).  Before QK(j) the groups
+    // issued after K(j) are V(j), K(j+1), V(j+1); before P.V(j) they are
+    // K(j+1), V(j+1), K(j+2): three groups may stay in flight at both waits.
+    auto step = [&](auto nrb_c, int j) __attribute__((always_inline)) {
+        constexpr int NRB = decltype(nrb_c)::value;
+        const int st = j & 1;
+        uint8_t *kst = k_st + st * (kWaves * C::BLOCK);
+        uint8_t *vst = v_st + st * (kWaves * C::BLOCK);
+        int32_t *tok = &tok_s[w][st][0];
+        const int pos0 = lo + (j * kWaves + w) * kSub;
+        const bool any = pos0 < hi;                  // wave-uniform
+        wait_vmcnt<3 * C::DMA>();
+
+        // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
+        f32x4 s[NRB][2];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+            s[rb][0] = s[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (any) {
+            const uint32_t kbase = lds_addr(kst + w * C::BLOCK);
+#pragma unroll
+            for (int t = 0; t < C::KB / 2; ++t) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const uint32_t ad = (kbase + koff[bb]) ^ (uint32_t)(t << 6);
+                    const int4v raw = *(const __attribute__((address_space(3))) int4v *)(uintptr_t)ad;
+                    QFrag k0, k1;
+                    if (SPARSE) {
+                        k0 = __builtin_bit_cast(QFrag, dec_bf16(int2v{raw.x, raw.y}));
+                        k1 = __builtin_bit_cast(QFrag, dec_bf16(int2v{raw.z, raw.w}));
+                    } else {
+                        k0 = __builtin_bit_cast(QFrag, dec_f16(int2v{raw.x, raw.y}));
+                        k1 = __builtin_bit_cast(QFrag, dec_f16(int2v{raw.z, raw.w}));
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb)
+                        s[rb][bb] = mfma_qk(k0, qf[rb][2 * t], s[rb][bb]);
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb)
+                        s[rb][bb] = mfma_qk(k1, qf[rb][2 * t + 1], s[rb][bb]);
+                }
+            }
+        }
+        issue_plane(j + 2, a.k_pool, kst, nullptr);
+
+        // ---- visibility, online softmax, P = hi + lo -------------------------
+        half8 ph[NRB], pl[NRB];
+        uint32_t keep = 0xFFFFFFFFu;                 // V rows some query sees
+        if (any) {
+            // this lane's 8 scores are tokens at positions pos0 + 8g + jj
+            const int tfirst = pos0 + 8 * g;
+            int tk[8];
+            if (SPARSE) {
+                const int4v t0 = *(const int4v *)&tok[8 * g];
+                const int4v t1 = *(const int4v *)&tok[8 * g + 4];
+                tk[0] = t0.x; tk[1] = t0.y; tk[2] = t0.z; tk[3] = t0.w;
+                tk[4] = t1.x; tk[5] = t1.y; tk[6] = t1.z; tk[7] = t1.w;
+                uint32_t mine = 0;
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    mine |= (tk[jj] != INT32_MAX) ? (1u << jj) : 0u;
+                // gather the 32 row flags: lane group g holds rows 8g .. 8g+7
+                keep = 0;
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg)
+                    keep |= (uint32_t)__builtin_amdgcn_readlane((int)mine, 16 * gg) << (8 * gg);
+            } else if (pos0 + kSub > hi) {
+                keep = (1u << (hi - pos0)) - 1u;
+            }
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                // vis bit jj: row 16rb + n sees the lane's token jj
+                uint32_t vis;
+                if (!SPARSE) {
+                    const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
+                    vis = (1u << nv) - 1u;
+                } else {
+                    vis = 0;
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        vis |= (tk[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid = INT32_MAX
+                }
+                const bool full = __all(vis == 0xFFu);
+                const bool none = __all(vis == 0u);
+                // c > 0, so the largest logit comes from the largest raw score
+                float mloc = -INFINITY;
+                if (full) {
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        mloc = fmaxf(mloc, s[rb][jj >> 2][jj & 3]);
+                } else if (!none) {
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        mloc = fmaxf(mloc, ((vis >> jj) & 1u) ? s[rb][jj >> 2][jj & 3] : -INFINITY);
+                }
+                const float mt = fmaxf(m_true[rb], max_over_groups(mloc) * c);
+                m_true[rb] = mt;
+                if (__any(mt > m_ref[rb] + kLazy)) {
+                    // rare: move the reference and rescale what was accumulated.
+                    // A row that has seen nothing keeps -inf (and zero state).
+                    const float alpha = (mt == -INFINITY) ? 1.0f : exp2f(m_ref[rb] - mt);
+                    l_part[rb] *= alpha;
+#pragma unroll
+                    for (int d = 0; d < C::DB; ++d)
+                        scale_in_place(acc[rb][d], alpha);
+                    m_ref[rb] = mt;
+                }
+                // p = 2^(logit - m_ref + 6) = exp2(fma(s, c, 6 - m_ref)): P carries 2^6
+                const float bias = kPLog2 - ((m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb]);
+                half8 hh8 = {}, ll8 = {};
+                if (!none) {
+                    float lsum = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 8; jj += 2) {
+                        float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
+                        float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
+                        if (!full) {
+                            a0 = ((vis >> jj) & 1u) ? a0 : -INFINITY;
+                            a1 = ((vis >> (jj + 1)) & 1u) ? a1 : -INFINITY;
+                        }
+                        const float p0 = __builtin_amdgcn_exp2f(a0);
+                        const float p1 = __builtin_amdgcn_exp2f(a1);
+                        lsum += p0 + p1;
+                        const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p0) & 0xFFFFE000u);
+                        const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p1) & 0xFFFFE000u);
+                        const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
+                        const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
+                        hh8[jj] = hh.x;
+                        hh8[jj + 1] = hh.y;
+                        ll8[jj] = ll.x;
+                        ll8[jj + 1] = ll.y;
+                    }
+                    l_part[rb] += lsum;
+                }
+                ph[rb] = hh8;
+                pl[rb] = ll8;
+            }
+        }
+        wait_vmcnt<3 * C::DMA>();   // V(j) landed
+
+        // ---- O^T += V^T P^T over the wave's 32 tokens, all D columns ---------
+        if (any) {
+            if (keep != 0xFFFFFFFFu)
+                zero_v_rows(vst, keep);
+            const uint32_t vaddr = lds_addr(vst + w * C::BLOCK) + voff;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                const uint32_t ad = vaddr ^ (uint32_t)(db << 4);
+                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(uintptr_t)ad);
+                const half8 vf = dec_f16(raw);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[rb], acc[rb][db], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][db], 0, 0, 0);
+            }
+        }
+        issue_plane(j + 2, a.v_pool, vst, tok);
+    };
+
+    auto main_loop = [&](auto nrb_c) __attribute__((always_inline)) {
+        for (int j = 0; j < nms; ++j)
+            step(nrb_c, j);
+    };
+
     if (nms > 0) {
-        issue_plane(0, a.k_pool, k_s0, nullptr);
-        issue_plane(0, a.v_pool, v_s0, &tok_s[0][0]);
-        issue_plane(1, a.k_pool, k_s1, nullptr);
-    }
-    for (int j = 0; j < nms; j += 2) {
-        step(j, k_s0, v_s0, k_s0, v_s1, &tok_s[0][0], &tok_s[1][0]);
-        if (j + 1 < nms)
-            step(j + 1, k_s1, v_s1, k_s1, v_s0, &tok_s[1][0], &tok_s[0][0]);
+        issue_plane(0, a.k_pool, k_st, nullptr);
+        issue_plane(0, a.v_pool, v_st, &tok_s[w][0][0]);
+        issue_plane(1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
+        issue_plane(1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
+        if (nrb == 1)
+            main_loop(std::integral_constant<int, 1>());
+        else if (nrb == 2)
+            main_loop(std::integral_constant<int, 2>());
+        else
+            main_loop(std::integral_constant<int, 3>());
     }
 
-    // ---- finish: exact max, summed l, this wave's d-quarter ----------------------
-    wait_vmcnt<0>();   // the trailing dummy loads
+    // ---- merge the four waves' states and write the split's partial --------
+    // Wave w owns output quarter w: d-blocks [w*DQ, (w+1)*DQ).  Every wave
+    // leaves its accumulators of the three other quarters in LDS (the stages'
+    // space), scaled to its own reference; the owner adds them with weights
+    // 2^(m_ref - M), M the exact row max over the split.
+    wait_vmcnt<0>();   // trailing dummy loads still target the stages
+    float lw[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb)
+        lw[rb] = sum_over_groups(l_part[rb]);
+    __syncthreads();   // every wave is done with the stages
+    if (g == 0) {
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+            xm[w][rb * 16 + n] = m_true[rb];
+    }
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+        if (q == w)
+            continue;
+        uint8_t *dstq = smem + (w * (kWaves - 1) + (q < w ? q : q - 1)) * C::QUARTER;
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+            for (int d = 0; d < C::DQ; ++d)
+                *(f32x4 *)(dstq + ((rb * C::DQ + d) * 64 + lane) * 16) = acc[rb][q * C::DQ + d];
+    }
+    __syncthreads();
+    float M[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-        l_part[rb] = sum_over_groups(l_part[rb]);
-        if (g == 0)
-            xl[w][rb * 16 + n] = l_part[rb];
+        const int r = rb * 16 + n;
+        float mm = xm[0][r];
+#pragma unroll
+        for (int v = 1; v < kWaves; ++v)
+            mm = fmaxf(mm, xm[v][r]);
+        M[rb] = mm;
+        const float f = (m_ref[rb] == -INFINITY) ? 0.0f : exp2f(m_ref[rb] - mm);
+        if (g == 0) {
+            xf[w][r] = f;
+            xl[w][r] = lw[rb] * f;
+        }
     }
     __syncthreads();
     const int64_t ws_base = (int64_t)split * a.total_rows;
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-        if (r < R) {
-            // acc and l are relative to m_ref and both carry the 2^6 of P
-            const float sc = (m_ref[rb] == -INFINITY) ? 0.0f : exp2f(m_ref[rb] - m_true[rb]);
-            const float sa = sc * kPUnscale;
+    for (int q = 0; q < kWaves; ++q) {
+        if (q != w)
+            continue;
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
+            const int r = rb * 16 + n;
+            float fv[kWaves];
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v)
+                fv[v] = xf[v][r] * kPUnscale;
             const int i = r / G, h = kvh * G + (r - i * G);
             const int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             float *dst = a.ws_acc + (ws_base + orow) * D;
-            // lane (n, g) of d-block db holds d = 16 db + 4 g + k
 #pragma unroll
-            for (int d = 0; d < C::DBW; ++d)
-                *(f32x4 *)(dst + 16 * (w * C::DBW + d) + 4 * g) = acc[rb][d] * sa;
-            if (w == 0 && g == 0) {
+            for (int d = 0; d < C::DQ; ++d) {
+                f32x4 o = acc[rb][q * C::DQ + d] * fv[q];
+#pragma unroll
+                for (int v = 0; v < kWaves; ++v) {
+                    if (v == q)
+                        continue;
+                    const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
+                    const f32x4 x = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
+                    o += x * fv[v];
+                }
+                // lane (n, g) of d-block db holds d = 16 db + 4 g + k
+                if (r < R)
+                    *(f32x4 *)(dst + 16 * (q * C::DQ + d) + 4 * g) = o;
+            }
+            if (q == 0 && g == 0 && r < R) {
                 float L = 0.0f;
 #pragma unroll
                 for (int v = 0; v < kWaves; ++v)
                     L += xl[v][r];
-                a.ws_max[ws_base + orow] = m_true[rb];
-                a.ws_sum[ws_base + orow] = L * sa;
+                a.ws_max[ws_base + orow] = M[rb];
+                a.ws_sum[ws_base + orow] = L * kPUnscale;
             }
         }
     }
