@@ -7,14 +7,18 @@
 // "Qwen4Exp: fp8_e4m3 main KV cache on the QSA path", review thread on
 // host-side KV scales).
 //
-// Split weights are w_s = 2^(m_s - M) with M the largest max among non-empty
-// splits (l_s > 0); empty splits get weight 0 and are skipped, so -inf - -inf
-// never forms, and a row whose splits are all empty is written as 0.
+// For a row with split partials (m_s, l_s, acc_s) (base-2 max, sum and
+// numerator relative to m_s), the result is
+//     M = max over non-empty splits (l_s > 0) of m_s
+//     o = out_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+// with empty splits weighted 0 (so -inf - -inf never forms) and o = 0 when
+// every split is empty.
 //
-// One workgroup per (row, 64-column chunk): 16 column lanes x 16 split groups.
-// The weights of 256 splits at a time are computed once into LDS, each thread
-// accumulates float4 columns over its splits, and the 16 split groups are
-// summed through LDS.  The split sums are plain FP32 sums in a fixed order.
+// One workgroup per (row, 64-column chunk): 16 float4 column lanes x 16 split
+// groups.  Split group k takes splits k, k+16, k+32, ...; all of a thread's
+// loads are issued before any is used (one memory round trip), and the thread
+// merges its splits online against its own running max.  The 16 groups are
+// then merged through LDS in a fixed order.  All arithmetic is FP32.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -25,6 +29,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLanes = 16;                 // float4 column lanes: 64 columns
 constexpr int kGroups = kThreads / kLanes; // split groups
+constexpr int kBatch = 16;                 // splits per group loaded at once
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -35,73 +40,67 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                                                            float out_scale,
                                                            uint16_t *__restrict__ out)
 {
-    __shared__ float red[kThreads];
-    __shared__ float wts[kThreads];
-    __shared__ f32x4 part[kGroups][kLanes];
+    __shared__ float gm[kGroups][kLanes];
+    __shared__ float gl[kGroups][kLanes];
+    __shared__ f32x4 gn[kGroups][kLanes];
 
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid % kLanes, grp = tid / kLanes;
     const int d0 = blockIdx.y * (4 * kLanes) + 4 * lane;
-
-    // M = max over non-empty splits
-    float m = -INFINITY;
-    for (int s = tid; s < S; s += kThreads) {
-        const int64_t k = (int64_t)s * R + r;
-        if (sm[k] > 0.0f)
-            m = fmaxf(m, mx[k]);
-    }
-    red[tid] = m;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (tid < off)
-            red[tid] = fmaxf(red[tid], red[tid + off]);
-        __syncthreads();
-    }
-    const float M = red[0];
-    __syncthreads();
-
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den_part = 0.0f;
     const bool col_ok = d0 < D;          // D is a multiple of 4
-    for (int s0 = 0; s0 < S; s0 += kThreads) {
-        const int s = s0 + tid;
-        float w = 0.0f;
-        if (s < S) {
-            const int64_t k = (int64_t)s * R + r;
-            const float l = sm[k];
-            if (l > 0.0f) {
-                w = exp2f(mx[k] - M);
-                den_part += w * l;
+
+    // running state of this thread's splits: max m, sum l, numerator num
+    float m = -INFINITY, l = 0.0f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = grp; s0 < S; s0 += kGroups * kBatch) {
+        float ms[kBatch], ls[kBatch];
+        f32x4 vs[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int s = s0 + k * kGroups;
+            ms[k] = -INFINITY;
+            ls[k] = 0.0f;
+            vs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (s < S) {
+                const int64_t i = (int64_t)s * R + r;
+                ms[k] = mx[i];
+                ls[k] = sm[i];
+                if (col_ok)
+                    vs[k] = *(const f32x4 *)(acc + i * D + d0);
             }
         }
-        wts[tid] = w;
-        __syncthreads();
-        const int cnt = min(kThreads, S - s0);
-        if (col_ok) {
-            for (int j = grp; j < cnt; j += kGroups) {
-                const float wj = wts[j];
-                if (wj != 0.0f) {
-                    const f32x4 v = *(const f32x4 *)(acc + ((int64_t)(s0 + j) * R + r) * D + d0);
-                    num += wj * v;
-                }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (ls[k] > 0.0f) {
+                const float mn = fmaxf(m, ms[k]);
+                const float a = exp2f(m - mn);        // 0 while m = -inf
+                const float b = exp2f(ms[k] - mn);
+                l = l * a + ls[k] * b;
+                num = num * a + vs[k] * b;
+                m = mn;
             }
         }
-        __syncthreads();
     }
-    red[tid] = den_part;
-    part[grp][lane] = num;
+    gm[grp][lane] = m;
+    gl[grp][lane] = l;
+    gn[grp][lane] = num;
     __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (tid < off)
-            red[tid] += red[tid + off];
-        __syncthreads();
-    }
     if (grp == 0 && col_ok) {
-        f32x4 tot = part[0][lane];
-        for (int gq = 1; gq < kGroups; ++gq)
-            tot += part[gq][lane];
-        const float den = red[0];
+        float M = gm[0][lane];
+#pragma unroll
+        for (int k = 1; k < kGroups; ++k)
+            M = fmaxf(M, gm[k][lane]);
+        float den = 0.0f;
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < kGroups; ++k) {
+                const float w = exp2f(gm[k][lane] - M);   // 0 for empty groups
+                den += w * gl[k][lane];
+                tot += w * gn[k][lane];
+            }
+        }
         uint16_t h[4];
         for (int k = 0; k < 4; ++k) {
             const float o = den > 0.0f ? (tot[k] / den) * out_scale : 0.0f;
