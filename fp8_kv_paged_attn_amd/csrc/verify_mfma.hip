@@ -275,6 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SHARED];
     __shared__ int2v slots[kSlots];                 // (physical page, first token) per slot
     __shared__ __attribute__((aligned(16))) int32_t tok_s[kWaves][2][kSub];   // sparse tokens
+    __shared__ int32_t blk_tmax[kWaves][2];         // sparse: last token of an all-valid block
     __shared__ float xm[kWaves][16 * kRowBlocks];   // merge: per-wave row max
     __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave scaled row sum
     __shared__ float xf[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator scale
@@ -356,6 +357,24 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     int hi = hi_list;
     if (!SPARSE)
         hi = min(hi, lmax);
+    // Per row block, the smallest length among the rows that can see tokens of
+    // this split (dense: length past the split start; sparse: nonzero).  A
+    // block whose tokens all lie below it is seen whole by every such row, and
+    // is processed without masks; rows that see nothing of the split are reset
+    // to the empty state at the end.
+    // Dense blocks are never unmasked past hi, where the K bytes may be NaN.
+    int minl[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        int v = SPARSE ? INT32_MAX : hi;
+        if (rb * 16 + n < R && lrow[rb] > (SPARSE ? 0 : lo))
+            v = SPARSE ? lrow[rb] : min(lrow[rb], hi);
+        v = min(v, __shfl_xor(v, 1, 64));
+        v = min(v, __shfl_xor(v, 2, 64));
+        v = min(v, __shfl_xor(v, 4, 64));
+        v = min(v, __shfl_xor(v, 8, 64));
+        minl[rb] = __builtin_amdgcn_readfirstlane(v);
+    }
 #pragma unroll
     for (int k = 0; k < kEnt; ++k) {
         const int i = tid + k * kThreads;
@@ -414,6 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     auto issue_plane = [&](int j, const uint8_t *pool, uint8_t *stage, int32_t *tokst)
         __attribute__((always_inline)) {
+        int32_t *tmaxp = &blk_tmax[w][j & 1];
         const int pos0 = lo + (j * kWaves + w) * kSub;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + w * C::BLOCK));
         // the stage being refilled was read by this wave's previous use of it
@@ -453,6 +473,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                         tokst[r] = tb_a + ua + r;
                     }
                 }
+                if (SPARSE && tokst != nullptr && lane == 0)
+                    *tmaxp = tb_a + ua + kSub - 1;
             } else {
                 const int64_t base_b = (int64_t)phys_b * a.page_stride - (int64_t)na * a.token_stride + head_off;
 #pragma unroll
@@ -465,6 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     if (SPARSE && tokst != nullptr && cp == 0)
                         tokst[r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
                 }
+                if (SPARSE && tokst != nullptr && lane == 0)
+                    *tmaxp = INT32_MAX;
             }
         } else {
 #pragma unroll
@@ -478,6 +502,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 if (SPARSE && tokst != nullptr && cp == 0)
                     tokst[row] = ok ? t : INT32_MAX;
             }
+            if (SPARSE && tokst != nullptr && lane == 0)
+                *tmaxp = INT32_MAX;
         }
     };
 
@@ -547,12 +573,20 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             s[rb][0] = s[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (any) {
             const uint32_t kbase = lds_addr(kst + w * C::BLOCK);
+            // all K reads of the block first, so that their latencies overlap
+            int4v kraw[C::KB / 2][2];
+#pragma unroll
+            for (int t = 0; t < C::KB / 2; ++t)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+                    kraw[t][bb] = *(const __attribute__((address_space(3))) int4v *)(uintptr_t)(
+                        (kbase + koff[bb]) ^ (uint32_t)(t << 6));
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their uses
 #pragma unroll
             for (int t = 0; t < C::KB / 2; ++t) {
 #pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {
-                    const uint32_t ad = (kbase + koff[bb]) ^ (uint32_t)(t << 6);
-                    const int4v raw = *(const __attribute__((address_space(3))) int4v *)(uintptr_t)ad;
+                    const int4v raw = kraw[t][bb];
                     QFrag k0, k1;
                     if (SPARSE) {
                         k0 = __builtin_bit_cast(QFrag, dec_bf16(int2v{raw.x, raw.y}));
@@ -576,10 +610,19 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         half8 ph[NRB], pl[NRB];
         uint32_t keep = 0xFFFFFFFFu;                 // V rows some query sees
         if (any) {
+            // row blocks that see every token of this block (wave-uniform)
+            const int tmax = SPARSE ? blk_tmax[w][st] : 0;
+            bool full[NRB];
+            bool all_full = true;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                full[rb] = SPARSE ? (tmax < minl[rb]) : (pos0 + kSub <= minl[rb]);
+                all_full = all_full && full[rb];
+            }
             // this lane's 8 scores are tokens at positions pos0 + 8g + jj
             const int tfirst = pos0 + 8 * g;
             int tk[8];
-            if (SPARSE) {
+            if (SPARSE && !all_full) {
                 const int4v t0 = *(const int4v *)&tok[8 * g];
                 const int4v t1 = *(const int4v *)&tok[8 * g + 4];
                 tk[0] = t0.x; tk[1] = t0.y; tk[2] = t0.z; tk[3] = t0.w;
@@ -593,31 +636,29 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                 for (int gg = 0; gg < 4; ++gg)
                     keep |= (uint32_t)__builtin_amdgcn_readlane((int)mine, 16 * gg) << (8 * gg);
-            } else if (pos0 + kSub > hi) {
+            } else if (!SPARSE && pos0 + kSub > hi) {
                 keep = (1u << (hi - pos0)) - 1u;
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                // vis bit jj: row 16rb + n sees the lane's token jj
-                uint32_t vis;
-                if (!SPARSE) {
-                    const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
-                    vis = (1u << nv) - 1u;
-                } else {
-                    vis = 0;
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj)
-                        vis |= (tk[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid = INT32_MAX
-                }
-                const bool full = __all(vis == 0xFFu);
-                const bool none = __all(vis == 0u);
+                // vis bit jj: row 16rb + n sees the lane's token jj (masked blocks)
+                uint32_t vis = 0xFFu;
                 // c > 0, so the largest logit comes from the largest raw score
-                float mloc = -INFINITY;
-                if (full) {
+                float mloc;
+                if (full[rb]) {
+                    mloc = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
+                                 fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
+                } else {
+                    if (!SPARSE) {
+                        const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
+                        vis = (1u << nv) - 1u;
+                    } else {
+                        vis = 0;
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj)
-                        mloc = fmaxf(mloc, s[rb][jj >> 2][jj & 3]);
-                } else if (!none) {
+                        for (int jj = 0; jj < 8; ++jj)
+                            vis |= (tk[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid = INT32_MAX
+                    }
+                    mloc = -INFINITY;
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj)
                         mloc = fmaxf(mloc, ((vis >> jj) & 1u) ? s[rb][jj >> 2][jj & 3] : -INFINITY);
@@ -636,31 +677,31 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 }
                 // p = 2^(logit - m_ref + 6) = exp2(fma(s, c, 6 - m_ref)): P carries 2^6
                 const float bias = kPLog2 - ((m_ref[rb] == -INFINITY) ? 0.0f : m_ref[rb]);
-                half8 hh8 = {}, ll8 = {};
-                if (!none) {
-                    float lsum = 0.0f;
+                half8 hh8, ll8;
+                float lsum = 0.0f;
 #pragma unroll
-                    for (int jj = 0; jj < 8; jj += 2) {
-                        float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
-                        float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
-                        if (!full) {
-                            a0 = ((vis >> jj) & 1u) ? a0 : -INFINITY;
-                            a1 = ((vis >> (jj + 1)) & 1u) ? a1 : -INFINITY;
-                        }
-                        const float p0 = __builtin_amdgcn_exp2f(a0);
-                        const float p1 = __builtin_amdgcn_exp2f(a1);
-                        lsum += p0 + p1;
-                        const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p0) & 0xFFFFE000u);
-                        const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p1) & 0xFFFFE000u);
-                        const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
-                        const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
-                        hh8[jj] = hh.x;
-                        hh8[jj + 1] = hh.y;
-                        ll8[jj] = ll.x;
-                        ll8[jj + 1] = ll.y;
+                for (int jj = 0; jj < 8; jj += 2) {
+                    float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
+                    float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
+                    if (!full[rb]) {
+                        a0 = ((vis >> jj) & 1u) ? a0 : -INFINITY;
+                        a1 = ((vis >> (jj + 1)) & 1u) ? a1 : -INFINITY;
                     }
-                    l_part[rb] += lsum;
+                    const float p0 = __builtin_amdgcn_exp2f(a0);
+                    const float p1 = __builtin_amdgcn_exp2f(a1);
+                    lsum += p0 + p1;
+                    // hi = p with the low 13 mantissa bits cleared (exact in FP16),
+                    // lo = the rest, rounded toward zero
+                    const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p0) & 0xFFFFE000u);
+                    const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p1) & 0xFFFFE000u);
+                    const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
+                    const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
+                    hh8[jj] = hh.x;
+                    hh8[jj + 1] = hh.y;
+                    ll8[jj] = ll.x;
+                    ll8[jj + 1] = ll.y;
                 }
+                l_part[rb] += lsum;
                 ph[rb] = hh8;
                 pl[rb] = ll8;
             }
@@ -672,12 +713,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             if (keep != 0xFFFFFFFFu)
                 zero_v_rows(vst, keep);
             const uint32_t vaddr = lds_addr(vst + w * C::BLOCK) + voff;
+            // all V^T reads of the block first, so that their latencies overlap
+            int2v vraw[C::DB];
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+                vraw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (__attribute__((address_space(3))) int2v *)(uintptr_t)(vaddr ^ (uint32_t)(db << 4)));
+            __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their uses
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
-                const uint32_t ad = vaddr ^ (uint32_t)(db << 4);
-                const int2v raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (__attribute__((address_space(3))) int2v *)(uintptr_t)ad);
-                const half8 vf = dec_f16(raw);
+                const half8 vf = dec_f16(vraw[db]);
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb)
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[rb], acc[rb][db], 0, 0, 0);
@@ -713,6 +758,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // space), scaled to its own reference; the owner adds them with weights
     // 2^(m_ref - M), M the exact row max over the split.
     wait_vmcnt<0>();   // trailing dummy loads still target the stages
+    // rows that see no token of this split may have accumulated values in
+    // blocks processed without masks: they get the empty state
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        if (lrow[rb] <= (SPARSE ? 0 : lo)) {
+            m_true[rb] = -INFINITY;
+            m_ref[rb] = -INFINITY;
+            l_part[rb] = 0.0f;
+        }
+    }
     float lw[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb)
