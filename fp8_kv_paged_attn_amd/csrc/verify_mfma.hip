@@ -97,6 +97,15 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Workgroup barrier for LDS data that this wave wrote with ordinary LDS
+// stores or read with LDS loads: they complete first (lgkmcnt 0).  Unlike
+// __syncthreads() it does not wait for direct-to-LDS loads still in flight.
+__device__ __forceinline__ void barrier_lds()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from gaddr land at
 // LDS byte lds_base + 16 l.  Issued as inline asm so that the compiler does not
 // track it: its own tracking of these loads is conservative (it drains every
@@ -295,26 +304,24 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     uint8_t *const k_st = smem;                               // [2][kWaves][BLOCK]
     uint8_t *const v_st = smem + 2 * kWaves * C::BLOCK;       // [2][kWaves][BLOCK]
 
-    // ---- one round trip: Q fragments, row lengths, page table -------------
-    // Q^T is the B operand of S^T = K Q^T: lane (n, g) holds row 16rb + n.
-    // The head dimension is walked in a permuted order that both operands
-    // share: MFMA k-block kb = 2t + e, lane group g covers dims
-    // 64t + 16g + 8e .. +7, so that one 16-byte LDS chunk (dims 64t + 16g ..
-    // +15) feeds two consecutive k-blocks of K.
-    QFrag qf[kRowBlocks][C::KB];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-        const bool live = r < R;
-        const int i = live ? r / G : 0;
-        const int h = kvh * G + (live ? r - i * G : 0);
-        const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + i) * a.num_heads + h) * D;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (live)
-                v = *(const uint4 *)(qrow + 64 * (kb >> 1) + 16 * g + 8 * (kb & 1));
-            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
+    // ---- one round trip: Q (to LDS), row lengths, page table ----------------
+    // Q is fetched once per workgroup with direct-to-LDS loads into the K0
+    // stage (free until the first K/V loads), rows of 2D bytes with their
+    // 16-byte chunks XOR-swizzled by row, and read into registers from there.
+    // Q row r of this KV unit is query row r / G, head kvh*G + r % G.
+    constexpr int kQRowsPerDma = 1024 / (2 * D);
+    constexpr int kQLanesPerRow = 2 * D / 16;
+    {
+        const int nq = (R * 2 * D + 1023) / 1024;          // 1 KB loads for R rows
+        const int r_in = lane / kQLanesPerRow, c = lane % kQLanesPerRow;
+        for (int i = w; i < nq; i += kWaves) {
+            const int r = i * kQRowsPerDma + r_in;
+            if (r < R) {
+                const int qi = r / G, h = kvh * G + (r - qi * G);
+                const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + qi) * a.num_heads + h) * D;
+                dma16((const uint8_t *)qrow + 16 * (c ^ (r & 15)),
+                      __builtin_amdgcn_readfirstlane(lds_addr(smem + i * 1024)));
+            }
         }
     }
     int lmine = 0;                                  // lane i < q_rows: length of query row i
@@ -393,7 +400,30 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             slots[i] = int2v{phys, tb};
         }
     }
+    wait_vmcnt<0>();   // this wave's Q loads
     __syncthreads();
+
+    // Q^T is the B operand of S^T = K Q^T: lane (n, g) holds row 16rb + n.
+    // The head dimension is walked in a permuted order that both operands
+    // share: MFMA k-block kb = 2t + e, lane group g covers dims
+    // 64t + 16g + 8e .. +7 (16-byte chunk 8t + 2g + e of the row), so that one
+    // 16-byte LDS chunk of K (dims 64t + 16g .. +15) feeds two consecutive
+    // k-blocks.
+    QFrag qf[kRowBlocks][C::KB];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = rb * 16 + n;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            int4v v = int4v{0, 0, 0, 0};
+            if (r < R) {
+                const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
+                v = *(const int4v *)(smem + r * 2 * D + 16 * (c ^ (r & 15)));
+            }
+            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
+        }
+    }
+    barrier_lds();     // everyone has its Q before the K0 stage is refilled
 
     const int64_t head_off = (int64_t)kvh * a.head_stride;
     // this wave's blocks: positions lo + 32 (4j + w), j = 0 .. nms-1
