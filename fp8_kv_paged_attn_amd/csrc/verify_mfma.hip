@@ -583,9 +583,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 
     // One block of this wave (step j) with NRB live row blocks.  Block j uses K
     // stage j%2 and V stage j%2.  Issue order: K0 V0 K1 V1 (prologue), then in
-    // step j: K(j+2) after QK(j), V(j+2) after P.V(j).  Before QK(j) the groups
-    // issued after K(j) are V(j), K(j+1), V(j+1); before P.V(j) they are
-    // K(j+1), V(j+1), K(j+2): three groups may stay in flight at both waits.
+    // step j: K(j+2) after QK(j), V(j+2) after P.V(j); blocks past the last
+    // step are not loaded.  Before QK(j) the groups issued after K(j) are
+    // V(j), and K(j+1), V(j+1) if block j+1 exists; before P.V(j) they are
+    // K(j+1), V(j+1) and K(j+2) where those blocks exist.  Loads complete in
+    // issue order, so allowing exactly that many groups in flight means the
+    // awaited group has landed.
+    auto wait_groups = [&](int groups) __attribute__((always_inline)) {
+        if (groups >= 3)
+            wait_vmcnt<3 * C::DMA>();
+        else if (groups == 2)
+            wait_vmcnt<2 * C::DMA>();
+        else if (groups == 1)
+            wait_vmcnt<C::DMA>();
+        else
+            wait_vmcnt<0>();
+    };
     auto step = [&](auto nrb_c, int j) __attribute__((always_inline)) {
         constexpr int NRB = decltype(nrb_c)::value;
         const int st = j & 1;
@@ -594,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         int32_t *tok = &tok_s[w][st][0];
         const int pos0 = lo + (j * kWaves + w) * kSub;
         const bool any = pos0 < hi;                  // wave-uniform
-        wait_vmcnt<3 * C::DMA>();
+        wait_groups(j + 1 < nms ? 3 : 1);
 
         // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
         f32x4 s[NRB][2];
@@ -634,7 +647,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 }
             }
         }
-        issue_plane(j + 2, a.k_pool, kst, nullptr);
+        if (j + 2 < nms)
+            issue_plane(j + 2, a.k_pool, kst, nullptr);
 
         // ---- visibility, online softmax, P = hi + lo -------------------------
         half8 ph[NRB], pl[NRB];
@@ -736,7 +750,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 pl[rb] = ll8;
             }
         }
-        wait_vmcnt<3 * C::DMA>();   // V(j) landed
+        wait_groups(j + 2 < nms ? 3 : (j + 1 < nms ? 2 : 0));   // V(j) landed
 
         // ---- O^T += V^T P^T over the wave's 32 tokens, all D columns ---------
         if (any) {
@@ -761,7 +775,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][db], 0, 0, 0);
             }
         }
-        issue_plane(j + 2, a.v_pool, vst, tok);
+        if (j + 2 < nms)
+            issue_plane(j + 2, a.v_pool, vst, tok);
     };
 
     auto main_loop = [&](auto nrb_c) __attribute__((always_inline)) {
@@ -772,8 +787,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     if (nms > 0) {
         issue_plane(0, a.k_pool, k_st, nullptr);
         issue_plane(0, a.v_pool, v_st, &tok_s[w][0][0]);
-        issue_plane(1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
-        issue_plane(1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
+        if (nms > 1) {
+            issue_plane(1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
+            issue_plane(1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
+        }
         if (nrb == 1)
             main_loop(std::integral_constant<int, 1>());
         else if (nrb == 2)
@@ -787,7 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // leaves its accumulators of the three other quarters in LDS (the stages'
     // space), scaled to its own reference; the owner adds them with weights
     // 2^(m_ref - M), M the exact row max over the split.
-    wait_vmcnt<0>();   // trailing dummy loads still target the stages
+    wait_vmcnt<0>();   // nothing may still target the stages (the merge area)
     // rows that see no token of this split may have accumulated values in
     // blocks processed without masks: they get the empty state
 #pragma unroll
@@ -815,9 +832,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         uint8_t *dstq = smem + (w * (kWaves - 1) + (q < w ? q : q - 1)) * C::QUARTER;
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
+            if (rb < nrb)     // row blocks past nrb were never accumulated: zero
 #pragma unroll
-            for (int d = 0; d < C::DQ; ++d)
-                *(f32x4 *)(dstq + ((rb * C::DQ + d) * 64 + lane) * 16) = acc[rb][q * C::DQ + d];
+                for (int d = 0; d < C::DQ; ++d)
+                    *(f32x4 *)(dstq + ((rb * C::DQ + d) * 64 + lane) * 16) = acc[rb][q * C::DQ + d];
     }
     __syncthreads();
     float M[kRowBlocks];
@@ -853,14 +871,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             float *dst = a.ws_acc + (ws_base + orow) * D;
 #pragma unroll
             for (int d = 0; d < C::DQ; ++d) {
-                f32x4 o = acc[rb][q * C::DQ + d] * fv[q];
+                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (rb < nrb) {
+                    o = acc[rb][q * C::DQ + d] * fv[q];
 #pragma unroll
-                for (int v = 0; v < kWaves; ++v) {
-                    if (v == q)
-                        continue;
-                    const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
-                    const f32x4 x = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
-                    o += x * fv[v];
+                    for (int v = 0; v < kWaves; ++v) {
+                        if (v == q)
+                            continue;
+                        const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
+                        const f32x4 x = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
+                        o += x * fv[v];
+                    }
                 }
                 // lane (n, g) of d-block db holds d = 16 db + 4 g + k
                 if (r < R)
