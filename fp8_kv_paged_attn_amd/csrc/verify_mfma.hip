@@ -461,34 +461,49 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
         loff[i] = two_slot ? r * (int32_t)a.token_stride + 16 * (cp ^ swz<D>(r)) : 0;
     }
-    auto issue_plane = [&](int j, const uint8_t *pool, uint8_t *stage, int32_t *tokst)
-        __attribute__((always_inline)) {
+    // Page lookup of block j of this wave (wave-uniform), done once for its K
+    // and V loads.  With pages of at least 32 tokens the block spans at most
+    // two page slots: rows [0, end_a) come from the first at base_a + row
+    // offset, rows [na, end_b) from the second at base_b + row offset.
+    struct BlockRef {
+        int na, ua, end_a, end_b, tb_a, tb_b;
+        int64_t base_a, base_b;
+    };
+    auto lookup = [&](int j) __attribute__((always_inline)) -> BlockRef {
+        BlockRef br = {};
+        if (two_slot) {
+            const int pos0 = lo + (j * kWaves + w) * kSub;
+            const int sa = divp(pos0, dm);
+            br.ua = pos0 - sa * ps;
+            br.na = min(kSub, ps - br.ua);
+            const int2v ea = slots[min(max(sa - slot0, 0), kSlots - 1)];
+            const int2v eb = slots[min(max(sa + 1 - slot0, 0), kSlots - 1)];
+            const int phys_a = __builtin_amdgcn_readfirstlane(ea.x);
+            br.tb_a = __builtin_amdgcn_readfirstlane(ea.y);
+            const int phys_b = __builtin_amdgcn_readfirstlane(eb.x);
+            br.tb_b = __builtin_amdgcn_readfirstlane(eb.y);
+            const int hip = hi - pos0;
+            br.end_a = min(br.na, hip);
+            br.end_b = hip;
+            if (SPARSE) {
+                br.end_a = phys_a >= 0 ? min(br.end_a, lmax - (br.tb_a + br.ua)) : 0;
+                br.end_b = phys_b >= 0 ? min(br.end_b, br.na + lmax - br.tb_b) : 0;
+            }
+            br.base_a = (int64_t)phys_a * a.page_stride + (int64_t)br.ua * a.token_stride + head_off;
+            br.base_b = (int64_t)phys_b * a.page_stride - (int64_t)br.na * a.token_stride + head_off;
+        }
+        return br;
+    };
+    auto issue_plane = [&](const BlockRef &br, int j, const uint8_t *pool, uint8_t *stage,
+                           int32_t *tokst) __attribute__((always_inline)) {
         int32_t *tmaxp = &blk_tmax[w][j & 1];
-        const int pos0 = lo + (j * kWaves + w) * kSub;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(stage + w * C::BLOCK));
         // the stage being refilled was read by this wave's previous use of it
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         if (two_slot) {
-            const int sa = divp(pos0, dm);
-            const int ua = pos0 - sa * ps;
-            const int na = min(kSub, ps - ua);            // rows in the first slot
-            const int2v ea = slots[min(max(sa - slot0, 0), kSlots - 1)];
-            const int2v eb = slots[min(max(sa + 1 - slot0, 0), kSlots - 1)];
-            const int phys_a = __builtin_amdgcn_readfirstlane(ea.x);
-            const int tb_a = __builtin_amdgcn_readfirstlane(ea.y);
-            const int phys_b = __builtin_amdgcn_readfirstlane(eb.x);
-            const int tb_b = __builtin_amdgcn_readfirstlane(eb.y);
-            const int hip = hi - pos0;
-            // valid rows: [0, end_a) in the first slot, [na, end_b) in the second
-            int end_a = min(na, hip), end_b = hip;
-            if (SPARSE) {
-                end_a = phys_a >= 0 ? min(end_a, lmax - (tb_a + ua)) : 0;
-                end_b = phys_b >= 0 ? min(end_b, na + lmax - tb_b) : 0;
-            }
-            const int64_t base_a = (int64_t)phys_a * a.page_stride + (int64_t)ua * a.token_stride + head_off;
-            if (na == kSub && end_a == kSub) {
+            if (br.na == kSub && br.end_a == kSub) {
                 // the whole block is valid and inside one page: SGPR base + lane offset
-                const uint8_t *sb = pool + base_a;
+                const uint8_t *sb = pool + br.base_a;
 #pragma unroll
                 for (int i = 0; i < C::DMA; ++i) {
                     if (i == 0)
@@ -500,27 +515,27 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                     for (int i = 0; i < C::DMA; ++i) {
                         const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
-                        tokst[r] = tb_a + ua + r;
+                        tokst[r] = br.tb_a + br.ua + r;
                     }
                 }
                 if (SPARSE && tokst != nullptr && lane == 0)
-                    *tmaxp = tb_a + ua + kSub - 1;
+                    *tmaxp = br.tb_a + br.ua + kSub - 1;
             } else {
-                const int64_t base_b = (int64_t)phys_b * a.page_stride - (int64_t)na * a.token_stride + head_off;
 #pragma unroll
                 for (int i = 0; i < C::DMA; ++i) {
                     const int r = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
-                    const bool in_b = r >= na;
-                    const bool ok = in_b ? (r < end_b) : (r < end_a);
-                    const int64_t src = ok ? (in_b ? base_b : base_a) + loff[i] : 0;
+                    const bool in_b = r >= br.na;
+                    const bool ok = in_b ? (r < br.end_b) : (r < br.end_a);
+                    const int64_t src = ok ? (in_b ? br.base_b : br.base_a) + loff[i] : 0;
                     dma16(pool + src, dst + i * 1024);
                     if (SPARSE && tokst != nullptr && cp == 0)
-                        tokst[r] = ok ? (in_b ? tb_b - na + r : tb_a + ua + r) : INT32_MAX;
+                        tokst[r] = ok ? (in_b ? br.tb_b - br.na + r : br.tb_a + br.ua + r) : INT32_MAX;
                 }
                 if (SPARSE && tokst != nullptr && lane == 0)
                     *tmaxp = INT32_MAX;
             }
         } else {
+            const int pos0 = lo + (j * kWaves + w) * kSub;
 #pragma unroll
             for (int i = 0; i < C::DMA; ++i) {
                 const int row = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
@@ -647,8 +662,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 }
             }
         }
-        if (j + 2 < nms)
-            issue_plane(j + 2, a.k_pool, kst, nullptr);
+        BlockRef br2 = {};
+        if (j + 2 < nms) {
+            br2 = lookup(j + 2);
+            issue_plane(br2, j + 2, a.k_pool, kst, nullptr);
+        }
 
         // ---- visibility, online softmax, P = hi + lo -------------------------
         half8 ph[NRB], pl[NRB];
@@ -685,14 +703,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                // vis bit jj: row 16rb + n sees the lane's token jj (masked blocks)
-                uint32_t vis = 0xFFu;
-                // c > 0, so the largest logit comes from the largest raw score
-                float mloc;
-                if (full[rb]) {
-                    mloc = fmaxf(fmaxf(fmaxf(s[rb][0][0], s[rb][0][1]), fmaxf(s[rb][0][2], s[rb][0][3])),
-                                 fmaxf(fmaxf(s[rb][1][0], s[rb][1][1]), fmaxf(s[rb][1][2], s[rb][1][3])));
-                } else {
+                // this lane's 8 raw scores; in a block not seen whole, the ones
+                // its row must not see become -inf (c > 0 keeps them -inf)
+                float sv[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    sv[jj] = s[rb][jj >> 2][jj & 3];
+                if (!full[rb]) {
+                    uint32_t vis;
                     if (!SPARSE) {
                         const int nv = min(max(min(lrow[rb], hi) - tfirst, 0), 8);
                         vis = (1u << nv) - 1u;
@@ -702,11 +720,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                         for (int jj = 0; jj < 8; ++jj)
                             vis |= (tk[jj] < lrow[rb]) ? (1u << jj) : 0u;   // invalid = INT32_MAX
                     }
-                    mloc = -INFINITY;
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj)
-                        mloc = fmaxf(mloc, ((vis >> jj) & 1u) ? s[rb][jj >> 2][jj & 3] : -INFINITY);
+                        sv[jj] = ((vis >> jj) & 1u) ? sv[jj] : -INFINITY;
                 }
+                // c > 0, so the largest logit comes from the largest raw score
+                const float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
                 const float mt = fmaxf(m_true[rb], max_over_groups(mloc) * c);
                 m_true[rb] = mt;
                 if (__any(mt > m_ref[rb] + kLazy)) {
@@ -725,14 +745,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 float lsum = 0.0f;
 #pragma unroll
                 for (int jj = 0; jj < 8; jj += 2) {
-                    float a0 = __builtin_fmaf(s[rb][jj >> 2][jj & 3], c, bias);
-                    float a1 = __builtin_fmaf(s[rb][(jj + 1) >> 2][(jj + 1) & 3], c, bias);
-                    if (!full[rb]) {
-                        a0 = ((vis >> jj) & 1u) ? a0 : -INFINITY;
-                        a1 = ((vis >> (jj + 1)) & 1u) ? a1 : -INFINITY;
-                    }
-                    const float p0 = __builtin_amdgcn_exp2f(a0);
-                    const float p1 = __builtin_amdgcn_exp2f(a1);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[jj], c, bias));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[jj + 1], c, bias));
                     lsum += p0 + p1;
                     // hi = p with the low 13 mantissa bits cleared (exact in FP16),
                     // lo = the rest, rounded toward zero
@@ -776,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             }
         }
         if (j + 2 < nms)
-            issue_plane(j + 2, a.v_pool, vst, tok);
+            issue_plane(br2, j + 2, a.v_pool, vst, tok);
     };
 
     auto main_loop = [&](auto nrb_c) __attribute__((always_inline)) {
@@ -785,11 +799,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     };
 
     if (nms > 0) {
-        issue_plane(0, a.k_pool, k_st, nullptr);
-        issue_plane(0, a.v_pool, v_st, &tok_s[w][0][0]);
+        const BlockRef br0 = lookup(0);
+        issue_plane(br0, 0, a.k_pool, k_st, nullptr);
+        issue_plane(br0, 0, a.v_pool, v_st, &tok_s[w][0][0]);
         if (nms > 1) {
-            issue_plane(1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
-            issue_plane(1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
+            const BlockRef br1 = lookup(1);
+            issue_plane(br1, 1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
+            issue_plane(br1, 1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
         }
         if (nrb == 1)
             main_loop(std::integral_constant<int, 1>());
