@@ -55,7 +55,8 @@ class PaWorkspace(ctypes.Structure):
 
 
 EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
-           "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3")
+           "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
+           "paged_attn_timer_arm", "paged_attn_timer_read")
 
 _LIB = None
 
@@ -86,12 +87,35 @@ def lib() -> ctypes.CDLL:
                                          i32, i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                          ctypes.POINTER(PaWorkspace), p]
     L.qsa_sparse_verify_e4m3.restype = i32
+    L.paged_attn_timer_arm.argtypes = [i32]
+    L.paged_attn_timer_arm.restype = i32
+    L.paged_attn_timer_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
+                                        ctypes.POINTER(ctypes.c_int32)]
+    L.paged_attn_timer_read.restype = i32
     ver = L.paged_attn_abi_version()
     if ver != ABI_VERSION:
         raise RuntimeError(f"libpaged_attn_e4m3 ABI revision {ver}, this binding needs "
                            f"{ABI_VERSION}: rebuild the library")
     _LIB = L
     return L
+
+
+TIMER_MAX_LAUNCHES = 1024
+
+
+def timer_arm(n: int) -> None:
+    """Time the kernels of the next `n` verify launches (0 disarms)."""
+    _check(lib().paged_attn_timer_arm(int(n)), "paged_attn_timer_arm")
+
+
+def timer_read() -> list:
+    """Kernel times in ms of the launches timed since timer_arm, in launch
+    order (waits for them); disarms."""
+    ms = (ctypes.c_float * TIMER_MAX_LAUNCHES)()
+    n = ctypes.c_int32(0)
+    _check(lib().paged_attn_timer_read(ms, TIMER_MAX_LAUNCHES, ctypes.byref(n)),
+           "paged_attn_timer_read")
+    return [float(ms[i]) for i in range(min(n.value, TIMER_MAX_LAUNCHES))]
 
 
 def status_string(rc: int) -> str:

@@ -13,6 +13,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -122,26 +123,51 @@ int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows
     return PA_OK;
 }
 
+// Kernel timer: (begin, end) event pairs handed to the next `armed` verify
+// launches on the device the timer was armed on.  The events are bound to the
+// kernel dispatch itself, so an interval is the kernel alone.
+struct KernelTimer {
+    std::mutex mu;
+    hipEvent_t ev[2 * PA_TIMER_MAX_LAUNCHES] = {};
+    bool created = false;
+    int device = -1;
+    int armed = 0, used = 0;
+};
+KernelTimer g_timer;
+
+// The event pair for this launch, or nullptr when the timer is not armed.
+const hipEvent_t *timer_take()
+{
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    if (g_timer.used >= g_timer.armed)
+        return nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != g_timer.device)
+        return nullptr;
+    return &g_timer.ev[2 * g_timer.used++];
+}
+
 int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim, bool sparse,
                  hipStream_t stream)
 {
     int32_t rc = check_device();
     if (rc != PA_OK)
         return rc;
+    const hipEvent_t *ev = timer_take();
     hipError_t err;
     switch (plan->kernel) {
     case PA_KERNEL_SIMPLE:
-        err = pa::launch_verify_simple(a, head_dim, sparse, stream);
+        err = pa::launch_verify_simple(a, head_dim, sparse, stream, ev);
         break;
     case PA_KERNEL_MFMA:
-        err = pa::launch_verify_mfma(a, head_dim, sparse, stream);
+        err = pa::launch_verify_mfma(a, head_dim, sparse, stream, ev);
         if (err == hipErrorNotSupported)
             return PA_EUNSUPPORTED;
         break;
     default:
-        err = pa::launch_verify_mfma(a, head_dim, sparse, stream);
+        err = pa::launch_verify_mfma(a, head_dim, sparse, stream, ev);
         if (err == hipErrorNotSupported)
-            err = pa::launch_verify_simple(a, head_dim, sparse, stream);
+            err = pa::launch_verify_simple(a, head_dim, sparse, stream, ev);
         break;
     }
     return err == hipSuccess ? PA_OK : PA_EHIP;
@@ -359,6 +385,48 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     return dispatch(a, plan, head_dim, true, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_timer_arm(int32_t n)
+{
+    if (n < 0 || n > PA_TIMER_MAX_LAUNCHES)
+        return PA_EINVAL;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return PA_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    if (n > 0 && g_timer.created && dev != g_timer.device)
+        return PA_EDEVICE;
+    if (n > 0 && !g_timer.created) {
+        for (int i = 0; i < 2 * PA_TIMER_MAX_LAUNCHES; ++i) {
+            if (hipEventCreate(&g_timer.ev[i]) != hipSuccess) {
+                for (int k = 0; k < i; ++k)
+                    (void)hipEventDestroy(g_timer.ev[k]);
+                return PA_EHIP;
+            }
+        }
+        g_timer.created = true;
+        g_timer.device = dev;
+    }
+    g_timer.armed = n;
+    g_timer.used = 0;
+    return PA_OK;
+}
+
+int32_t paged_attn_timer_read(float *ms, int32_t cap, int32_t *count)
+{
+    if (!count || cap < 0 || (cap > 0 && !ms))
+        return PA_EINVAL;
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    const int used = g_timer.used;
+    g_timer.armed = g_timer.used = 0;
+    *count = used;
+    for (int i = 0; i < used && i < cap; ++i) {
+        if (hipEventSynchronize(g_timer.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms[i], g_timer.ev[2 * i], g_timer.ev[2 * i + 1]) != hipSuccess)
+            return PA_EHIP;
+    }
+    return PA_OK;
 }
 
 }  // extern "C"

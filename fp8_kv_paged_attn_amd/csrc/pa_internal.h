@@ -2,6 +2,7 @@
 // Internal to libpaged_attn_e4m3; the public interface is include/paged_attn_e4m3.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,10 +37,12 @@ struct VerifyArgs {
 enum class Variant : int { kSimple = 0, kMfma = 1 };
 
 // Launchers return hipSuccess or the launch error.  Grid = (num_splits, units).
+// `ev`, when not null, is a (begin, end) pair of HIP events bound to the
+// kernel's own dispatch (hipExtLaunchKernel), for the kernel timer.
 hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
-                                hipStream_t stream);
+                                hipStream_t stream, const hipEvent_t *ev = nullptr);
 hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse,
-                              hipStream_t stream);
+                              hipStream_t stream, const hipEvent_t *ev = nullptr);
 hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
                           int num_rows, int head_dim, float out_scale, uint16_t *out,
                           hipStream_t stream);

@@ -928,28 +928,30 @@ DivMagic make_magic(int d)
 }
 
 template <int D, bool SPARSE>
-hipError_t launch_t(const VerifyArgs &a, hipStream_t stream)
+hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
 {
     // every split's page slots must fit the LDS slot cache
     const int64_t slots = (int64_t)(a.tokens_per_split - 1) / a.page_size + 2;
     if (slots > max_slots<D>())
         return hipErrorNotSupported;
     dim3 grid(a.num_splits, a.batch * a.num_kv_heads);
-    hipLaunchKernelGGL((verify_mfma_kernel<D, SPARSE>), grid, dim3(kThreads), 0, stream, a,
-                       make_magic(a.page_size));
+    hipExtLaunchKernelGGL((verify_mfma_kernel<D, SPARSE>), grid, dim3(kThreads), 0, stream,
+                          ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
+                          make_magic(a.page_size));
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse, hipStream_t stream)
+hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse, hipStream_t stream,
+                              const hipEvent_t *ev)
 {
     if (a.rows > 16 * kRowBlocks)
         return hipErrorNotSupported;
     if (head_dim == 256)
-        return sparse ? launch_t<256, true>(a, stream) : launch_t<256, false>(a, stream);
+        return sparse ? launch_t<256, true>(a, stream, ev) : launch_t<256, false>(a, stream, ev);
     if (head_dim == 128)
-        return sparse ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+        return sparse ? launch_t<128, true>(a, stream, ev) : launch_t<128, false>(a, stream, ev);
     return hipErrorNotSupported;
 }
 

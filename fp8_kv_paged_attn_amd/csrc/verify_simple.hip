@@ -195,18 +195,19 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 }  // namespace
 
 hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
-                                hipStream_t stream)
+                                hipStream_t stream, const hipEvent_t *ev)
 {
     dim3 grid(a.num_splits, a.batch * a.num_kv_heads);
     dim3 block(kThreads);
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     if (head_dim == 256 && !sparse)
-        hipLaunchKernelGGL((verify_simple_kernel<256, false>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((verify_simple_kernel<256, false>), grid, block, 0, stream, e0, e1, 0, a);
     else if (head_dim == 128 && !sparse)
-        hipLaunchKernelGGL((verify_simple_kernel<128, false>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((verify_simple_kernel<128, false>), grid, block, 0, stream, e0, e1, 0, a);
     else if (head_dim == 256 && sparse)
-        hipLaunchKernelGGL((verify_simple_kernel<256, true>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((verify_simple_kernel<256, true>), grid, block, 0, stream, e0, e1, 0, a);
     else if (head_dim == 128 && sparse)
-        hipLaunchKernelGGL((verify_simple_kernel<128, true>), grid, block, 0, stream, a);
+        hipExtLaunchKernelGGL((verify_simple_kernel<128, true>), grid, block, 0, stream, e0, e1, 0, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -29,8 +29,10 @@
  * Conventions for every entry point:
  *   - Buffers are device pointers unless marked (host).  The caller owns all
  *     memory; the library never allocates, never frees, keeps no state
- *     between calls except a per-device record of whether it is a gfx950,
- *     never synchronises and never copies host memory to the device.  Work
+ *     between calls except a per-device record of whether it is a gfx950
+ *     (and the kernel timer's events, below, once a caller arms it), never
+ *     synchronises (but in paged_attn_timer_read) and never copies host
+ *     memory to the device.  Work
  *     is enqueued on `stream` (a hipStream_t; NULL = the null stream), so
  *     calls can be captured into a HIP graph.
  *   - A problem the host can see (null pointer, bad shape, misalignment, a
@@ -203,6 +205,26 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream);
+
+/* Kernel timer, for measurement harnesses; no result depends on it.
+ *
+ * paged_attn_timer_arm(n), 0 <= n <= PA_TIMER_MAX_LAUNCHES: the next n verify
+ * launches (paged_attn_verify_e4m3 or qsa_sparse_verify_e4m3, any stream) made
+ * with the current device current get a pair of HIP events bound to the kernel
+ * dispatch itself (hipExtLaunchKernel), so each interval is that kernel's own
+ * run, with no marker commands added to the stream.  n = 0 disarms.  The first
+ * arm creates 2 * PA_TIMER_MAX_LAUNCHES events on the current device, kept
+ * until the process ends; arming later on another device gives PA_EDEVICE.
+ *
+ * paged_attn_timer_read(ms, cap, count): (host) *count = launches timed since
+ * the arm; waits for each of the first min(count, cap) and writes its kernel
+ * time in milliseconds to ms[i], in launch order; disarms.  PA_EHIP if an
+ * event cannot be read (for example a launch that failed).
+ *
+ * Arm, launches and read must not interleave with another thread's. */
+#define PA_TIMER_MAX_LAUNCHES 1024
+int32_t paged_attn_timer_arm(int32_t n);
+int32_t paged_attn_timer_read(float *ms, int32_t cap, int32_t *count);
 
 #ifdef __cplusplus
 }

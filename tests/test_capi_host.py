@@ -182,6 +182,24 @@ def test_valid_call_without_device_reports_edevice(L):
     assert Call()(L) == PA_EDEVICE
 
 
+def test_timer_rejects_bad_arguments(L):
+    n = ctypes.c_int32(7)
+    ms = (ctypes.c_float * 4)()
+    assert L.paged_attn_timer_arm(-1) == PA_EINVAL
+    assert L.paged_attn_timer_arm(pa.TIMER_MAX_LAUNCHES + 1) == PA_EINVAL
+    assert L.paged_attn_timer_read(ms, 4, None) == PA_EINVAL
+    assert L.paged_attn_timer_read(None, 4, ctypes.byref(n)) == PA_EINVAL
+    assert L.paged_attn_timer_read(ms, -1, ctypes.byref(n)) == PA_EINVAL
+    # nothing armed: nothing timed
+    assert L.paged_attn_timer_read(None, 0, ctypes.byref(n)) == PA_OK and n.value == 0
+
+
+@no_device
+def test_timer_without_device_reports_edevice(L):
+    assert L.paged_attn_timer_arm(4) == PA_EDEVICE
+    assert L.paged_attn_timer_arm(0) == PA_EDEVICE
+
+
 def test_python_binding_rejects_cpu_fallback(monkeypatch, tmp_path):
     """Without the built library every op raises: there is no CPU path."""
     monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -316,3 +316,34 @@ def test_graph_replay_changed_lengths(kernel):
         assert np.array_equal(replayed, eager), lv
         zero_rows = [i for i, x in enumerate(lv) if x == 0]
         assert not replayed[zero_rows].any()
+
+
+# ---------------------------------------------------------------------------
+# kernel timer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_kernel_timer(kernel):
+    """Timed launches give the same bytes as untimed ones; the timer records
+    exactly the armed number of launches, each inside the bracketing events."""
+    w = wl.make_dense("timer", 0x7133, q_rows=8, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=9000, page_size=1648, pool_pages=8, sigma=1.0, k_scale=0.7,
+                      v_scale=1.2)
+    d = gu.dense_to_dev(w)
+    announce("timer untimed", kernel)
+    ref = gu.run_dense(w, kernel, d=d)
+    announce("timer armed", kernel)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    pa.timer_arm(2)
+    t0.record()
+    outs = [gu.run_dense(w, kernel, d=d) for _ in range(3)]
+    t1.record()
+    torch.cuda.synchronize()
+    ms = pa.timer_read()
+    assert len(ms) == 2
+    total = t0.elapsed_time(t1)
+    assert all(0.0 < x < total for x in ms), (ms, total)
+    for o in outs:
+        assert np.array_equal(o, ref)
+    assert pa.timer_read() == []            # reading disarmed it
