@@ -12,10 +12,14 @@ identical inputs back to back) is reported beside it, with the other contexts
 of the range (8K, 64K, 128K).
 
 Throughput counts algorithmic bytes only: the longest visible prefix x 512 B
-(K and V, one KV head, D = 256, one byte per element).  The verify kernel's own
-duration comes from HIP events around each verify launch on the stream it runs
-on; roofline.achieved = algorithmic bytes / that duration.  The FP64 CPU oracle
-is timed on the host's cores on the same workload as a reported baseline.
+(K and V, one KV head, D = 256, one byte per element).  The timed region holds
+the calls alone; the verify kernel's own duration comes from the library's
+kernel timer (HIP events passed with each verify dispatch, on the stream it
+runs on), and roofline.achieved = algorithmic bytes / that duration.  A plain
+streaming-read kernel over a 2 GiB buffer gives the device's practical read
+ceiling beside the published peak.  The sparse (QSA) batch is timed the same
+way.  The FP64 CPU oracle is timed on the host's cores on the same workload as
+a reported baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -23,7 +27,6 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -40,6 +43,7 @@ METRIC = "µs/call and KV-read GB/s (% HBM peak), q8 H6/Hkv1/D256 E4M3, 8K–256
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 PMC_FILE = os.path.join(ROOT, "profiles", "verify_kernel_pmc.json")
+KERNEL_SOURCES = ("verify_mfma.hip", "pa_internal.h")
 
 
 def log(*a):
@@ -47,10 +51,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the verify kernel's sources (the kernel the counters describe)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "fp8_kv_paged_attn_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp8_kv_paged_attn_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -104,18 +109,92 @@ class DenseBench:
             self.verify(i if rotate else 0)
             self.combine()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+        # an event every SAMPLE calls: per-call percentiles over the samples
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps // SAMPLE + 2)]
         pa.timer_arm(min(steps, pa.TIMER_MAX_LAUNCHES))
-        t0.record()
+        marks[0].record()
+        nm = 1
         for i in range(steps):
             self.verify(i if rotate else 0)
             self.combine()
-        t1.record()
+            if (i + 1) % SAMPLE == 0 or i + 1 == steps:
+                marks[nm].record()
+                nm += 1
         torch.cuda.synchronize()
-        total_ms = t0.elapsed_time(t1)
+        total_ms = marks[0].elapsed_time(marks[nm - 1])
+        per_call = [marks[k - 1].elapsed_time(marks[k]) / SAMPLE
+                    for k in range(1, nm) if k * SAMPLE <= steps]
+        self.pcts = percentiles(per_call)
         vk = pa.timer_read()
         return total_ms / steps, statistics.fmean(vk), statistics.median(vk)
+
+
+SAMPLE = 10          # calls per timing sample
+
+
+def percentiles(xs):
+    """p10/p50/p90 (us) of per-call times given in ms."""
+    if not xs:
+        return None
+    ys = sorted(x * 1e3 for x in xs)
+    pick = lambda q: ys[min(len(ys) - 1, int(round(q * (len(ys) - 1))))]
+    return {"p10": round(pick(0.1), 3), "p50": round(pick(0.5), 3), "p90": round(pick(0.9), 3),
+            "samples": len(ys), "calls_per_sample": SAMPLE}
+
+
+class QsaBench(DenseBench):
+    """The sparse (QSA) batch resident on the device, with n_copies of its pool."""
+
+    def __init__(self, w, n_copies: int, kernel: str):
+        import numpy as np
+        import torch
+
+        import fp8_kv_paged_attn_amd as pa
+
+        self.w, self.pa, self.torch = w, pa, torch
+        dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(np.ascontiguousarray(w.q_bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        k = torch.from_numpy(w.k_pool).to(dev)
+        v = torch.from_numpy(w.v_pool).to(dev)
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
+        self.table = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
+        self.sel = torch.from_numpy(w.sel_blocks.astype(np.int32)).to(dev)
+        self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
+        G = w.num_heads // w.num_kv_heads
+        self.plan = pa.plan(w.topk * w.page_size, w.q_rows * G, w.batch * w.num_kv_heads,
+                            w.head_dim, splits=w.num_splits, kernel=kernel)
+        self.rows = w.num_rows
+        self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
+        self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),
+                               dtype=torch.float16, device=dev)
+        self.kv_bytes = w.kv_bytes()
+
+    def verify(self, i: int):
+        k, v = self.pools[i % len(self.pools)]
+        w = self.w
+        self.pa.qsa_sparse_verify_e4m3(self.q, k, v, self.table, self.sel, self.lens, w.sm_scale,
+                                       w.k_scale, self.plan, self.ws)
+
+
+def read_ceiling(torch, pa, nbytes: int = 2 << 30, reps: int = 5):
+    """Read bandwidth (GB/s) of the plain streaming-read probe over nbytes."""
+    buf = torch.zeros(nbytes // 16, 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for _ in range(2):
+        pa.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pa.stream_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def copies_for(pool_bytes: int) -> int:
@@ -135,11 +214,16 @@ def cpu_baseline(w, max_seconds: float = 20.0):
         orc.dense_workload(w, nthreads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
+    t0 = time.perf_counter()
+    orc.dense_workload(w, nthreads=1)
+    t1 = time.perf_counter() - t0
     return {"value": round(w.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole {w.name} workload (all {w.q_rows} rows x {w.num_heads} heads), "
                       f"FP64 oracle on {threads} threads, median of {len(times)} runs, "
-                      f"{t * 1e3:.1f} ms per call"}
+                      f"{t * 1e3:.1f} ms per call",
+            "value_1thread": round(w.kv_bytes() / t1 / 1e9, 4),
+            "sample_1thread": f"the same workload on 1 thread, one run, {t1 * 1e3:.1f} ms"}
 
 
 def traffic_from_profile(src_hash: str, workload: str):
@@ -202,8 +286,10 @@ def main():
     log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
     b = DenseBench(w, n_copies, args.kernel, args.splits)
     ms, vk_mean, vk_med = b.run(args.steps, args.warmup, rotate=True)
+    pcts_cold = b.pcts
     log(f"[bench] cold: {ms * 1e3:.2f} us/call, verify {vk_mean * 1e3:.2f} us")
     ms_hot, vk_hot, _ = b.run(args.steps, args.warmup, rotate=False)
+    pcts_hot = b.pcts
     log(f"[bench] hot: {ms_hot * 1e3:.2f} us/call, verify {vk_hot * 1e3:.2f} us")
     gbs = b.kv_bytes / (ms * 1e-3) / 1e9
     achieved = b.kv_bytes / (vk_mean * 1e-3) / 1e9
@@ -229,12 +315,30 @@ def main():
                           "hot_gbs": round(bs.kv_bytes / (h_ms * 1e-3) / 1e9, 1)})
             del bs
             torch.cuda.empty_cache()
+        log("[bench] sweep c4 (QSA)")
+        wq = wl.cached("c4")
+        bq = QsaBench(wq, copies_for(2 * wq.k_pool.size), args.kernel)
+        steps = max(20, args.steps // 2)
+        c_ms, c_vk, _ = bq.run(steps, args.warmup, rotate=True)
+        h_ms, h_vk, _ = bq.run(steps, args.warmup, rotate=False)
+        sweep.append({"workload": wq.name, "kv_bytes": bq.kv_bytes,
+                      "splits": bq.plan.num_splits, "units": wq.batch * wq.num_kv_heads,
+                      "us_per_call": round(c_ms * 1e3, 3), "verify_us": round(c_vk * 1e3, 3),
+                      "gbs": round(bq.kv_bytes / (c_ms * 1e-3) / 1e9, 1),
+                      "verify_gbs": round(bq.kv_bytes / (c_vk * 1e-3) / 1e9, 1),
+                      "hot_us_per_call": round(h_ms * 1e3, 3),
+                      "hot_gbs": round(bq.kv_bytes / (h_ms * 1e-3) / 1e9, 1)})
+        del bq
+        torch.cuda.empty_cache()
         sweep.append({"workload": w.name, "ctx": w.max_tokens, "kv_bytes": w.kv_bytes(),
                       "splits": plan.num_splits, "us_per_call": round(ms * 1e3, 3),
                       "verify_us": round(vk_mean * 1e3, 3), "gbs": round(gbs, 1),
                       "verify_gbs": round(achieved, 1),
                       "hot_us_per_call": round(ms_hot * 1e3, 3),
                       "hot_gbs": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 1)})
+
+    log("[bench] streaming-read ceiling")
+    ceiling = read_ceiling(torch, pa)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -264,11 +368,14 @@ def main():
                    "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
         "hot": {"us_per_call": round(ms_hot * 1e3, 3),
                 "value": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 2),
-                "verify_us": round(vk_hot * 1e3, 3)},
+                "verify_us": round(vk_hot * 1e3, 3), "us_per_call_pcts": pcts_hot},
+        "us_per_call_pcts": pcts_cold,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "verify", "verify_us": round(vk_mean * 1e3, 3),
-                     "verify_us_median": round(vk_med * 1e3, 3)},
+                     "verify_us_median": round(vk_med * 1e3, 3),
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
         "cpu_baseline": cpu,
         "sweep": sweep,
         "source_hash": src_hash,

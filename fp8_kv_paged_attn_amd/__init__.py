@@ -56,7 +56,7 @@ class PaWorkspace(ctypes.Structure):
 
 EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
-           "paged_attn_timer_arm", "paged_attn_timer_read")
+           "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe")
 
 _LIB = None
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_timer_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
                                         ctypes.POINTER(ctypes.c_int32)]
     L.paged_attn_timer_read.restype = i32
+    L.paged_attn_stream_read_probe.argtypes = [p, i64, p, p]
+    L.paged_attn_stream_read_probe.restype = i32
     ver = L.paged_attn_abi_version()
     if ver != ABI_VERSION:
         raise RuntimeError(f"libpaged_attn_e4m3 ABI revision {ver}, this binding needs "
@@ -116,6 +118,16 @@ def timer_read() -> list:
     _check(lib().paged_attn_timer_read(ms, TIMER_MAX_LAUNCHES, ctypes.byref(n)),
            "paged_attn_timer_read")
     return [float(ms[i]) for i in range(min(n.value, TIMER_MAX_LAUNCHES))]
+
+
+def stream_read_probe(buf, sink) -> None:
+    """Read all of buf (a contiguous device tensor, size a multiple of 16 bytes)
+    once on the current stream; sink is a device tensor of at least 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or sink.device != buf.device or sink.numel() * sink.element_size() < 4:
+        raise ValueError("buf must be contiguous and sink a 4-byte tensor on its device")
+    _check(lib().paged_attn_stream_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                              _stream(buf.device)), "paged_attn_stream_read_probe")
 
 
 def status_string(rc: int) -> str:

@@ -124,8 +124,7 @@ int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows
 }
 
 // Kernel timer: (begin, end) event pairs handed to the next `armed` verify
-// launches on the device the timer was armed on.  The events are bound to the
-// kernel dispatch itself, so an interval is the kernel alone.
+// launches on the device the timer was armed on, passed with the dispatch.
 struct KernelTimer {
     std::mutex mu;
     hipEvent_t ev[2 * PA_TIMER_MAX_LAUNCHES] = {};
@@ -385,6 +384,19 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     return dispatch(a, plan, head_dim, true, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_stream_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink || bytes < 0 || bytes % 16 != 0)
+        return PA_EINVAL;
+    if (!aligned16(buf))
+        return PA_EALIGN;
+    int32_t rc = check_device();
+    if (rc != PA_OK)
+        return rc;
+    hipError_t err = pa::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_EHIP;
 }
 
 int32_t paged_attn_timer_arm(int32_t n)

@@ -210,9 +210,11 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
  *
  * paged_attn_timer_arm(n), 0 <= n <= PA_TIMER_MAX_LAUNCHES: the next n verify
  * launches (paged_attn_verify_e4m3 or qsa_sparse_verify_e4m3, any stream) made
- * with the current device current get a pair of HIP events bound to the kernel
- * dispatch itself (hipExtLaunchKernel), so each interval is that kernel's own
- * run, with no marker commands added to the stream.  n = 0 disarms.  The first
+ * with the current device current get a pair of HIP events passed with the
+ * kernel's dispatch (hipExtLaunchKernel): the interval runs from the point the
+ * launch is processed on the stream to the kernel's completion, so it adds no
+ * marker commands to the stream but includes the dispatch delay after the
+ * previous command.  n = 0 disarms.  The first
  * arm creates 2 * PA_TIMER_MAX_LAUNCHES events on the current device, kept
  * until the process ends; arming later on another device gives PA_EDEVICE.
  *
@@ -225,6 +227,16 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
 #define PA_TIMER_MAX_LAUNCHES 1024
 int32_t paged_attn_timer_arm(int32_t n);
 int32_t paged_attn_timer_read(float *ms, int32_t cap, int32_t *count);
+
+/* Streaming read probe, for measurement harnesses; no result depends on it.
+ * Reads bytes (>= 0, a multiple of 16) from buf (16-byte aligned) once, with
+ * 16-byte loads spread over every compute unit, and keeps nothing (sink, one
+ * uint32, is written only in a case that zero-filled buffers never reach).
+ * The bandwidth it reaches on a buffer much larger than the 256 MB Infinity
+ * Cache is the practical HBM read ceiling of the device.  PA_EINVAL for a null
+ * pointer or a bad size, PA_EALIGN for a misaligned buffer. */
+int32_t paged_attn_stream_read_probe(const void *buf, int64_t bytes, uint32_t *sink,
+                                     void *stream);
 
 #ifdef __cplusplus
 }

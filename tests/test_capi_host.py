@@ -194,6 +194,15 @@ def test_timer_rejects_bad_arguments(L):
     assert L.paged_attn_timer_read(None, 0, ctypes.byref(n)) == PA_OK and n.value == 0
 
 
+def test_stream_read_probe_rejects_bad_arguments(L):
+    A = ctypes.c_void_p(0x10000)
+    assert L.paged_attn_stream_read_probe(None, 64, A, None) == PA_EINVAL
+    assert L.paged_attn_stream_read_probe(A, 64, None, None) == PA_EINVAL
+    assert L.paged_attn_stream_read_probe(A, -16, A, None) == PA_EINVAL
+    assert L.paged_attn_stream_read_probe(A, 40, A, None) == PA_EINVAL
+    assert L.paged_attn_stream_read_probe(ctypes.c_void_p(0x10008), 64, A, None) == PA_EALIGN
+
+
 @no_device
 def test_timer_without_device_reports_edevice(L):
     assert L.paged_attn_timer_arm(4) == PA_EDEVICE

@@ -347,3 +347,13 @@ def test_kernel_timer(kernel):
     for o in outs:
         assert np.array_equal(o, ref)
     assert pa.timer_read() == []            # reading disarmed it
+
+
+def test_stream_read_probe_runs():
+    """The read probe reads a zero buffer without touching its sink."""
+    announce("stream read probe")
+    buf = torch.zeros(1 << 20, 4, dtype=torch.int32, device=gu.DEV)
+    sink = torch.full((1,), 7, dtype=torch.int32, device=gu.DEV)
+    pa.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
