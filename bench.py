@@ -9,17 +9,20 @@ the metric is quoted on).  The KV pool is replicated in device memory and the
 steps rotate through the copies, so every call reads K/V from HBM rather than
 from the 256 MB Infinity Cache ("cold"); the same loop on one copy ("hot",
 identical inputs back to back) is reported beside it, with the other contexts
-of the range (8K, 64K, 128K).
+of the range (8K, 64K, 128K) and the sparse (QSA) batch.
 
-Throughput counts algorithmic bytes only: the longest visible prefix x 512 B
-(K and V, one KV head, D = 256, one byte per element).  The timed region holds
-the calls alone; the verify kernel's own duration comes from the library's
-kernel timer (HIP events passed with each verify dispatch, on the stream it
-runs on), and roofline.achieved = algorithmic bytes / that duration.  A plain
-streaming-read kernel over a 2 GiB buffer gives the device's practical read
-ceiling beside the published peak.  The sparse (QSA) batch is timed the same
-way.  The FP64 CPU oracle is timed on the host's cores on the same workload as
-a reported baseline.
+Per-call time is measured on a HIP graph of 10 consecutive verify + combine
+calls, replayed (the pages time their kernels from CUDA-graph samples), so that
+Python launch overhead does not set the pace; the eager per-call time is
+reported beside it.  Throughput counts algorithmic bytes only: the longest
+visible prefix x 512 B (K and V, one KV head, D = 256, one byte per element).
+The verify kernel's own duration comes from the library's kernel timer (HIP
+events passed with each verify dispatch, on the stream it runs on) over an
+eager loop of the same calls, and roofline.achieved = algorithmic bytes / that
+duration.  A plain streaming-read kernel over a 2 GiB buffer gives the
+device's practical read ceiling beside the published peak.  The FP64 CPU
+oracle is timed on the host's cores on the same workload as a reported
+baseline.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -98,8 +101,46 @@ class DenseBench:
         self.pa.paged_attn_combine_fp32(self.ws, self.plan.num_splits, self.rows,
                                         self.w.head_dim, self.w.v_scale, self.out)
 
+    def run_graph(self, steps: int, warmup: int, rotate: bool):
+        """Per-call time of verify + combine replayed from a HIP graph.
+
+        GRAPH_CALLS consecutive calls (rotating over the pool copies when
+        rotate) are captured once and the graph is replayed; an event follows
+        every replay.  Returns ms per call and sets self.pcts (per-call
+        percentiles over the replays)."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(GRAPH_CALLS):
+                self.verify(i if rotate else 0)
+                self.combine()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(GRAPH_CALLS):
+                self.verify(i if rotate else 0)
+                self.combine()
+        torch.cuda.synchronize()
+        reps = max(1, steps // GRAPH_CALLS)
+        for _ in range(max(1, warmup // GRAPH_CALLS)):
+            g.replay()
+        torch.cuda.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        marks[0].record()
+        for k in range(reps):
+            g.replay()
+            marks[k + 1].record()
+        torch.cuda.synchronize()
+        total_ms = marks[0].elapsed_time(marks[reps])
+        self.pcts = percentiles([marks[k].elapsed_time(marks[k + 1]) / GRAPH_CALLS
+                                 for k in range(reps)], GRAPH_CALLS)
+        del g
+        return total_ms / (reps * GRAPH_CALLS)
+
     def run(self, steps: int, warmup: int, rotate: bool):
-        """Time `steps` calls; returns (ms per call, mean and median verify-kernel ms).
+        """Time `steps` eager calls; returns (ms per call, mean and median verify-kernel ms).
 
         The timed region holds the calls alone.  Each verify kernel's own run
         is timed by the library's kernel timer (HIP events bound to the
@@ -124,22 +165,23 @@ class DenseBench:
         total_ms = marks[0].elapsed_time(marks[nm - 1])
         per_call = [marks[k - 1].elapsed_time(marks[k]) / SAMPLE
                     for k in range(1, nm) if k * SAMPLE <= steps]
-        self.pcts = percentiles(per_call)
+        self.pcts = percentiles(per_call, SAMPLE)
         vk = pa.timer_read()
         return total_ms / steps, statistics.fmean(vk), statistics.median(vk)
 
 
-SAMPLE = 10          # calls per timing sample
+SAMPLE = 10          # eager calls per timing sample
+GRAPH_CALLS = 10     # verify + combine calls captured in one graph
 
 
-def percentiles(xs):
+def percentiles(xs, calls_per_sample: int):
     """p10/p50/p90 (us) of per-call times given in ms."""
     if not xs:
         return None
     ys = sorted(x * 1e3 for x in xs)
     pick = lambda q: ys[min(len(ys) - 1, int(round(q * (len(ys) - 1))))]
     return {"p10": round(pick(0.1), 3), "p50": round(pick(0.5), 3), "p90": round(pick(0.9), 3),
-            "samples": len(ys), "calls_per_sample": SAMPLE}
+            "samples": len(ys), "calls_per_sample": calls_per_sample}
 
 
 class QsaBench(DenseBench):
@@ -175,6 +217,31 @@ class QsaBench(DenseBench):
         w = self.w
         self.pa.qsa_sparse_verify_e4m3(self.q, k, v, self.table, self.sel, self.lens, w.sm_scale,
                                        w.k_scale, self.plan, self.ws)
+
+
+def measure(b, steps: int, warmup: int) -> dict:
+    """Cold (rotating pool copies) and hot (one copy) timings of one workload:
+    per-call time from graph replays, verify-kernel time from the eager,
+    timer-armed loop (in microseconds)."""
+    c_ms = b.run_graph(steps, warmup, rotate=True)
+    c_pcts = b.pcts
+    e_ms, vk, vmed = b.run(steps, warmup, rotate=True)
+    h_ms = b.run_graph(steps, warmup, rotate=False)
+    h_pcts = b.pcts
+    _, h_vk, _ = b.run(steps, warmup, rotate=False)
+    return {"us": c_ms * 1e3, "pcts": c_pcts, "eager_us": e_ms * 1e3, "verify_us": vk * 1e3,
+            "verify_med_us": vmed * 1e3, "hot_us": h_ms * 1e3, "hot_pcts": h_pcts,
+            "hot_verify_us": h_vk * 1e3}
+
+
+def sweep_entry(name: str, kv_bytes: int, plan, m: dict, **extra) -> dict:
+    gb = lambda us: round(kv_bytes / (us * 1e-6) / 1e9, 1)
+    return {"workload": name, **extra, "kv_bytes": kv_bytes, "splits": plan.num_splits,
+            "us_per_call": round(m["us"], 3), "gbs": gb(m["us"]),
+            "verify_us": round(m["verify_us"], 3), "verify_gbs": gb(m["verify_us"]),
+            "eager_us_per_call": round(m["eager_us"], 3),
+            "hot_us_per_call": round(m["hot_us"], 3), "hot_gbs": gb(m["hot_us"]),
+            "hot_verify_us": round(m["hot_verify_us"], 3)}
 
 
 def read_ceiling(torch, pa, nbytes: int = 2 << 30, reps: int = 5):
@@ -285,57 +352,35 @@ def main():
     n_copies = copies_for(2 * w.k_pool.size)
     log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
     b = DenseBench(w, n_copies, args.kernel, args.splits)
-    ms, vk_mean, vk_med = b.run(args.steps, args.warmup, rotate=True)
-    pcts_cold = b.pcts
-    log(f"[bench] cold: {ms * 1e3:.2f} us/call, verify {vk_mean * 1e3:.2f} us")
-    ms_hot, vk_hot, _ = b.run(args.steps, args.warmup, rotate=False)
-    pcts_hot = b.pcts
-    log(f"[bench] hot: {ms_hot * 1e3:.2f} us/call, verify {vk_hot * 1e3:.2f} us")
-    gbs = b.kv_bytes / (ms * 1e-3) / 1e9
-    achieved = b.kv_bytes / (vk_mean * 1e-3) / 1e9
+    m = measure(b, args.steps, args.warmup)
+    log(f"[bench] cold: {m['us']:.2f} us/call (graph), {m['eager_us']:.2f} eager, "
+        f"verify {m['verify_us']:.2f} us; hot: {m['hot_us']:.2f} us/call, "
+        f"verify {m['hot_verify_us']:.2f} us")
+    gbs = b.kv_bytes / (m["us"] * 1e-6) / 1e9
+    achieved = b.kv_bytes / (m["verify_us"] * 1e-6) / 1e9
     plan = b.plan
     del b
     torch.cuda.empty_cache()
 
     sweep = []
     if not args.no_sweep:
+        steps = max(20, args.steps // 2)
         for name in ["c1", "c2_64k", "c2_128k"]:
             log(f"[bench] sweep {name}")
             ws = wl.cached(name)
             bs = DenseBench(ws, copies_for(2 * ws.k_pool.size), args.kernel, 0)
-            steps = max(20, args.steps // 2)
-            c_ms, c_vk, _ = bs.run(steps, args.warmup, rotate=True)
-            h_ms, h_vk, _ = bs.run(steps, args.warmup, rotate=False)
-            sweep.append({"workload": ws.name, "ctx": ws.max_tokens, "kv_bytes": bs.kv_bytes,
-                          "splits": bs.plan.num_splits, "us_per_call": round(c_ms * 1e3, 3),
-                          "verify_us": round(c_vk * 1e3, 3),
-                          "gbs": round(bs.kv_bytes / (c_ms * 1e-3) / 1e9, 1),
-                          "verify_gbs": round(bs.kv_bytes / (c_vk * 1e-3) / 1e9, 1),
-                          "hot_us_per_call": round(h_ms * 1e3, 3),
-                          "hot_gbs": round(bs.kv_bytes / (h_ms * 1e-3) / 1e9, 1)})
+            sweep.append(sweep_entry(ws.name, bs.kv_bytes, bs.plan, measure(bs, steps, args.warmup),
+                                     ctx=ws.max_tokens))
             del bs
             torch.cuda.empty_cache()
         log("[bench] sweep c4 (QSA)")
         wq = wl.cached("c4")
         bq = QsaBench(wq, copies_for(2 * wq.k_pool.size), args.kernel)
-        steps = max(20, args.steps // 2)
-        c_ms, c_vk, _ = bq.run(steps, args.warmup, rotate=True)
-        h_ms, h_vk, _ = bq.run(steps, args.warmup, rotate=False)
-        sweep.append({"workload": wq.name, "kv_bytes": bq.kv_bytes,
-                      "splits": bq.plan.num_splits, "units": wq.batch * wq.num_kv_heads,
-                      "us_per_call": round(c_ms * 1e3, 3), "verify_us": round(c_vk * 1e3, 3),
-                      "gbs": round(bq.kv_bytes / (c_ms * 1e-3) / 1e9, 1),
-                      "verify_gbs": round(bq.kv_bytes / (c_vk * 1e-3) / 1e9, 1),
-                      "hot_us_per_call": round(h_ms * 1e3, 3),
-                      "hot_gbs": round(bq.kv_bytes / (h_ms * 1e-3) / 1e9, 1)})
+        sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, measure(bq, steps, args.warmup),
+                                 units=wq.batch * wq.num_kv_heads))
         del bq
         torch.cuda.empty_cache()
-        sweep.append({"workload": w.name, "ctx": w.max_tokens, "kv_bytes": w.kv_bytes(),
-                      "splits": plan.num_splits, "us_per_call": round(ms * 1e3, 3),
-                      "verify_us": round(vk_mean * 1e3, 3), "gbs": round(gbs, 1),
-                      "verify_gbs": round(achieved, 1),
-                      "hot_us_per_call": round(ms_hot * 1e3, 3),
-                      "hot_gbs": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 1)})
+        sweep.append(sweep_entry(w.name, w.kv_bytes(), plan, m, ctx=w.max_tokens))
 
     log("[bench] streaming-read ceiling")
     ceiling = read_ceiling(torch, pa)
@@ -354,7 +399,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
+        "ms_per_step": round(m["us"] * 1e-3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -365,15 +410,17 @@ def main():
                    "ctx": w.max_tokens, "page_size": w.page_size, "kv_bytes": w.kv_bytes(),
                    "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
                    "kernel": kernel_name, "cache": f"cold: {n_copies} rotating pool copies",
-                   "us_per_call": round(ms * 1e3, 3), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
-        "hot": {"us_per_call": round(ms_hot * 1e3, 3),
-                "value": round(w.kv_bytes() / (ms_hot * 1e-3) / 1e9, 2),
-                "verify_us": round(vk_hot * 1e3, 3), "us_per_call_pcts": pcts_hot},
-        "us_per_call_pcts": pcts_cold,
+                   "us_per_call": round(m["us"], 3), "timing": "HIP graph of 10 verify + combine calls, replayed",
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "hot": {"us_per_call": round(m["hot_us"], 3),
+                "value": round(w.kv_bytes() / (m["hot_us"] * 1e-6) / 1e9, 2),
+                "verify_us": round(m["hot_verify_us"], 3), "us_per_call_pcts": m["hot_pcts"]},
+        "us_per_call_pcts": m["pcts"],
+        "eager_us_per_call": round(m["eager_us"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "verify", "verify_us": round(vk_mean * 1e3, 3),
-                     "verify_us_median": round(vk_med * 1e3, 3),
+                     "traffic": traffic, "kernel": "verify", "verify_us": round(m["verify_us"], 3),
+                     "verify_us_median": round(m["verify_med_us"], 3),
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
         "cpu_baseline": cpu,
