@@ -14,11 +14,15 @@
 // with empty splits weighted 0 (so -inf - -inf never forms) and o = 0 when
 // every split is empty.
 //
-// One workgroup per (row, 64-column chunk): 16 float4 column lanes x 16 split
-// groups.  Split group k takes splits k, k+16, k+32, ...; all of a thread's
-// loads are issued before any is used (one memory round trip), and the thread
-// merges its splits online against its own running max.  The 16 groups are
-// then merged through LDS in a fixed order.  All arithmetic is FP32.
+// A thread owns one float4 of columns of one row and a group of its splits
+// (splits g, g + GROUPS, ...).  A workgroup of 256 threads covers 64 columns of
+// 16 / GROUPS rows.  All loads of a batch are issued before any is used (one
+// memory round trip per batch of BATCH splits), and the thread merges its
+// splits online against its own running max.  The GROUPS states of a row's
+// float4 are then merged through LDS in group order.  GROUPS is chosen on the
+// host so that the grid has about 128 K threads: many splits over few rows
+// (one request, long context) get 16 groups; many rows over few splits (a
+// batch of sparse requests) get 1 or 2.  All arithmetic is FP32.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -28,11 +32,23 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kLanes = 16;                 // float4 column lanes: 64 columns
-constexpr int kGroups = kThreads / kLanes; // split groups
-constexpr int kBatch = 16;                 // splits per group loaded at once
+constexpr int kTargetThreads = 131072;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// (m, l, num) <- merge with the state (mo, lo, no); max -inf is the empty state.
+__device__ __forceinline__ void merge_state(float &m, float &l, f32x4 &num, float mo, float lo,
+                                            f32x4 no)
+{
+    const float mn = fmaxf(m, mo);
+    const float a = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+    const float b = (mo == -INFINITY) ? 0.0f : exp2f(mo - mn);
+    l = l * a + lo * b;
+    num = num * a + no * b;
+    m = mn;
+}
+
+template <int GROUPS, int BATCH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ acc,
                                                            const float *__restrict__ mx,
                                                            const float *__restrict__ sm,
@@ -40,75 +56,80 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                                                            float out_scale,
                                                            uint16_t *__restrict__ out)
 {
-    __shared__ float gm[kGroups][kLanes];
-    __shared__ float gl[kGroups][kLanes];
-    __shared__ f32x4 gn[kGroups][kLanes];
+    constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
+    __shared__ float gm[GROUPS > 1 ? kThreads : 1];
+    __shared__ float gl[GROUPS > 1 ? kThreads : 1];
+    __shared__ f32x4 gn[GROUPS > 1 ? kThreads : 1];
 
-    const int r = blockIdx.x;
     const int tid = threadIdx.x;
-    const int lane = tid % kLanes, grp = tid / kLanes;
+    const int lane = tid % kLanes;
+    const int grp = (tid / kLanes) % GROUPS;
+    const int rsub = tid / (kLanes * GROUPS);
+    const int r = blockIdx.x * kRowsPerWG + rsub;
     const int d0 = blockIdx.y * (4 * kLanes) + 4 * lane;
-    const bool col_ok = d0 < D;          // D is a multiple of 4
+    const bool ok = r < R && d0 < D;          // D is a multiple of 4
 
     // running state of this thread's splits: max m, sum l, numerator num
     float m = -INFINITY, l = 0.0f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = grp; s0 < S; s0 += kGroups * kBatch) {
-        float ms[kBatch], ls[kBatch];
-        f32x4 vs[kBatch];
+    if (ok) {
+        for (int s0 = grp; s0 < S; s0 += GROUPS * BATCH) {
+            float ms[BATCH], ls[BATCH];
+            f32x4 vs[BATCH];
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int s = s0 + k * kGroups;
-            ms[k] = -INFINITY;
-            ls[k] = 0.0f;
-            vs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (s < S) {
-                const int64_t i = (int64_t)s * R + r;
-                ms[k] = mx[i];
-                ls[k] = sm[i];
-                if (col_ok)
+            for (int k = 0; k < BATCH; ++k) {
+                const int s = s0 + k * GROUPS;
+                ms[k] = -INFINITY;
+                ls[k] = 0.0f;
+                vs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (s < S) {
+                    const int64_t i = (int64_t)s * R + r;
+                    ms[k] = mx[i];
+                    ls[k] = sm[i];
                     vs[k] = *(const f32x4 *)(acc + i * D + d0);
+                }
             }
-        }
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            if (ls[k] > 0.0f) {
-                const float mn = fmaxf(m, ms[k]);
-                const float a = exp2f(m - mn);        // 0 while m = -inf
-                const float b = exp2f(ms[k] - mn);
-                l = l * a + ls[k] * b;
-                num = num * a + vs[k] * b;
-                m = mn;
+            for (int k = 0; k < BATCH; ++k) {
+                if (ls[k] > 0.0f)
+                    merge_state(m, l, num, ms[k], ls[k], vs[k]);
             }
         }
     }
-    gm[grp][lane] = m;
-    gl[grp][lane] = l;
-    gn[grp][lane] = num;
-    __syncthreads();
-    if (grp == 0 && col_ok) {
-        float M = gm[0][lane];
+    if (GROUPS > 1) {
+        gm[tid] = m;
+        gl[tid] = l;
+        gn[tid] = num;
+        __syncthreads();
+        if (grp != 0)
+            return;
+        const int base = rsub * kLanes * GROUPS + lane;
 #pragma unroll
-        for (int k = 1; k < kGroups; ++k)
-            M = fmaxf(M, gm[k][lane]);
-        float den = 0.0f;
-        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int k = 0; k < kGroups; ++k) {
-                const float w = exp2f(gm[k][lane] - M);   // 0 for empty groups
-                den += w * gl[k][lane];
-                tot += w * gn[k][lane];
-            }
-        }
+        for (int k = 1; k < GROUPS; ++k)
+            merge_state(m, l, num, gm[base + k * kLanes], gl[base + k * kLanes],
+                        gn[base + k * kLanes]);
+    }
+    if (ok) {
         uint16_t h[4];
         for (int k = 0; k < 4; ++k) {
-            const float o = den > 0.0f ? (tot[k] / den) * out_scale : 0.0f;
+            const float o = l > 0.0f ? (num[k] / l) * out_scale : 0.0f;
             h[k] = __builtin_bit_cast(uint16_t, (_Float16)o);
         }
         uint2 packed = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
         *(uint2 *)(out + (int64_t)r * D + d0) = packed;
     }
+}
+
+template <int GROUPS, int BATCH>
+hipError_t launch_g(const float *acc, const float *mx, const float *sm, int num_splits,
+                    int num_rows, int head_dim, float out_scale, uint16_t *out,
+                    hipStream_t stream)
+{
+    constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
+    dim3 grid((num_rows + kRowsPerWG - 1) / kRowsPerWG, (head_dim + 4 * kLanes - 1) / (4 * kLanes));
+    hipLaunchKernelGGL((combine_kernel<GROUPS, BATCH>), grid, dim3(kThreads), 0, stream, acc, mx,
+                       sm, num_splits, num_rows, head_dim, out_scale, out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -121,10 +142,26 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
         return hipSuccess;
     if (head_dim % 4 != 0)
         return hipErrorInvalidValue;
-    dim3 grid(num_rows, (head_dim + 4 * kLanes - 1) / (4 * kLanes));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, acc, mx, sm, num_splits,
-                       num_rows, head_dim, out_scale, out);
-    return hipGetLastError();
+    // split groups per (row, float4): double while the grid stays under the
+    // target thread count and every group has a split
+    const int64_t base = (int64_t)num_rows * ((head_dim + 63) / 64) * kLanes;
+    int groups = 1;
+    while (groups < 16 && groups < num_splits && base * groups * 2 <= kTargetThreads)
+        groups *= 2;
+    const bool big = (num_splits + groups - 1) / groups > 8;   // splits per thread
+#define PA_COMBINE(G)                                                                          \
+    return big ? launch_g<G, 16>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,  \
+                                 stream)                                                       \
+               : launch_g<G, 8>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,   \
+                                stream)
+    switch (groups) {
+    case 1: PA_COMBINE(1);
+    case 2: PA_COMBINE(2);
+    case 4: PA_COMBINE(4);
+    case 8: PA_COMBINE(8);
+    default: PA_COMBINE(16);
+    }
+#undef PA_COMBINE
 }
 
 }  // namespace pa
