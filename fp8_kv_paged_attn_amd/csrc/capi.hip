@@ -23,7 +23,7 @@ constexpr int kMaxQRows = 8;
 constexpr int kDefaultCUs = 256;
 // Fewest tokens a split should read, so that the FP32 partial it writes
 // (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.
-constexpr int kMinTokensPerSplit = 256;
+constexpr int kMinTokensPerSplit = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

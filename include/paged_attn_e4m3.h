@@ -136,10 +136,11 @@ typedef struct pa_workspace {
 /* (host, pure integer) Choose the split of max_tokens tokens for
  * num_kv_units units of rows_per_kv_unit rows.  num_cus = compute units to
  * fill (<= 0: 256, the MI355X count).  requested_splits > 0 forces the split
- * count (clamped to what the token count allows); 0 picks one: enough
- * workgroups to fill the device, balanced against the FP32 workspace each
- * split writes (the pages tune split counts per device and region, [QSA]
- * sm_120 retune commit).  Returns PA_EINVAL for non-positive sizes. */
+ * count (clamped to what the token count allows); 0 picks one: one workgroup
+ * per compute unit over all units, but no split shorter than 128 tokens, so
+ * that the FP32 partial each split writes stays small against its K/V bytes
+ * (the pages tune split counts per device and region, [QSA] sm_120 retune
+ * commit).  Returns PA_EINVAL for non-positive sizes. */
 int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
                         int32_t head_dim, int32_t num_cus, int32_t requested_splits,
                         pa_plan *out);

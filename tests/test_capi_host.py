@@ -66,7 +66,7 @@ def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
     else:
         c = cus if cus > 0 else 256
         assert S <= max(1, -(-c // units))
-        assert S <= max(1, -(-max_tokens // 256))
+        assert S <= max(1, -(-max_tokens // 128))
     assert (p.max_tokens, p.rows_per_kv_unit, p.num_kv_units, p.head_dim) == (max_tokens, rows, units, D)
     assert p.ws_acc_bytes == S * rows * units * D * 4
     assert p.ws_stat_bytes == S * rows * units * 4
