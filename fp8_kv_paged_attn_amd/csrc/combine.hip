@@ -9,10 +9,12 @@
 //
 // For a row with split partials (m_s, l_s, acc_s) (base-2 max, sum and
 // numerator relative to m_s), the result is
-//     M = max over non-empty splits (l_s > 0) of m_s
+//     M = max over non-empty splits (l_s != 0) of m_s
 //     o = out_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// with empty splits weighted 0 (so -inf - -inf never forms) and o = 0 when
-// every split is empty.
+// with empty splits (l_s = 0) weighted 0, so -inf - -inf never forms, and
+// o = 0 when every split is empty.  A split whose sum is NaN (NaN bytes at
+// positions a row sees) is not empty: the NaN reaches the row, as it does in
+// the unsplit definition.
 //
 // A thread owns one float4 of columns of one row and a group of its splits
 // (splits g, g + GROUPS, ...).  A workgroup of 256 threads covers 64 columns of
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
             }
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
-                if (ls[k] > 0.0f)
+                if (ls[k] != 0.0f)              // empty: l = 0; a NaN sum is kept
                     merge_state(m, l, num, ms[k], ls[k], vs[k]);
             }
         }
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
     if (ok) {
         uint16_t h[4];
         for (int k = 0; k < 4; ++k) {
-            const float o = l > 0.0f ? (num[k] / l) * out_scale : 0.0f;
+            const float o = l != 0.0f ? (num[k] / l) * out_scale : 0.0f;
             h[k] = __builtin_bit_cast(uint16_t, (_Float16)o);
         }
         uint2 packed = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));

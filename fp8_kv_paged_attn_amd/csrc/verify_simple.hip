@@ -20,11 +20,13 @@ constexpr int kMaxRows = 48;
 
 // E4M3 -> float.  The 7 magnitude bits, shifted under an FP16 exponent field,
 // form an FP16 number equal to the E4M3 value times 2^-8 for every finite code
-// (subnormals included); the factor is undone exactly in FP32.
+// (subnormals included); the factor is undone exactly in FP32.  The two NaN
+// codes S.1111.111 decode to NaN.
 __device__ inline float e4m3_to_float(uint32_t byte)
 {
     uint16_t h = (uint16_t)(((byte & 0x7Fu) << 7) | ((byte & 0x80u) << 8));
-    return (float)__builtin_bit_cast(_Float16, h) * 256.0f;
+    const float f = (float)__builtin_bit_cast(_Float16, h) * 256.0f;
+    return (byte & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : f;
 }
 
 __device__ inline float fp16_to_float(uint16_t bits)

@@ -174,7 +174,9 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
 /* FP32 combination of split partials into FP16 rows ([DN] first section):
  *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),
  *   out[r][d] = fp16_rne(out_scale * sum_s w_s acc[s][r][d] / sum_s w_s sum[s][r]),
- * and out[r][:] = 0 when every split of row r is empty.  out_scale is the
+ * and out[r][:] = 0 when every split of row r is empty.  A split is empty when
+ * its sum is exactly 0; a NaN sum (NaN bytes at positions the row sees) is not
+ * empty and makes the row NaN, as the unsplit definition does.  out_scale is the
  * V dequantisation scale ([QSA] output scale).  ws_* as written by a verify
  * call with num_splits splits and num_rows rows; out_fp16 [num_rows][head_dim]
  * (= [q_rows][num_heads][head_dim], or [batch][q_rows][num_heads][head_dim]).

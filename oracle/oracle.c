@@ -547,7 +547,7 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
             int64_t k = (int64_t)s * R + r;
             double l = sm64 ? sm64[k] : (double)sm32[k];
             double m = mx64 ? mx64[k] : (double)mx32[k];
-            if (l > 0.0 && m > M)
+            if (l != 0.0 && m > M)
                 M = m;
         }
         for (int d = 0; d < D; ++d)
@@ -557,7 +557,7 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
             double l = sm64 ? sm64[k] : (double)sm32[k];
             double m = mx64 ? mx64[k] : (double)mx32[k];
             double w;
-            if (!(l > 0.0))
+            if (l == 0.0)              /* empty split; a NaN sum is not empty */
                 continue;
             w = (ORC_MUTANT == 9) ? 1.0 : exp2(m - M);
             den += w * l;
@@ -567,7 +567,7 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
             }
         }
         for (int d = 0; d < D; ++d)
-            out[(int64_t)r * D + d] = den > 0.0 ? v_scale * out[(int64_t)r * D + d] / den : 0.0;
+            out[(int64_t)r * D + d] = den != 0.0 ? v_scale * out[(int64_t)r * D + d] / den : 0.0;
     }
     return 0;
 }

@@ -402,6 +402,47 @@ def pin_nan_poison(o):
     assert np.array_equal(o.qsa_workload(qz)[1, 0], np.zeros((4, 16))), "qsa zero row"
 
 
+def pin_visible_nan(o):
+    """NaN bytes at positions a row sees: a NaN K byte makes every row seeing
+    the token NaN, a NaN V byte makes that column NaN for the rows seeing it
+    (PyTorch SDPA on the decoded tokens agrees); split partials combined give
+    the same NaN pattern and the same finite values as the one-pass result."""
+    w = _dense_case(1)                       # H6/Hkv1/D32, page 7, lengths 0, 23, 50
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    tk, tv, dv = 30, 10, 5                   # token 30: row 2 only; token 10: rows 1, 2
+    k[w.block_table[tk // w.page_size], tk % w.page_size, 0, 3] = 0x7F
+    v[w.block_table[tv // w.page_size], tv % w.page_size, 0, dv] = 0xFF
+    w2 = _with_pool(w, k, v)
+    one = o.dense_workload(w2)
+    assert np.all(np.isnan(one[2])), "row seeing the NaN key"
+    assert np.all(np.isnan(one[1][:, dv])), "column of the NaN value"
+    assert np.all(np.isfinite(np.delete(one[1], dv, axis=1)))
+    assert not one[0].any(), "zero-length row"
+    # SDPA per row over that row's visible tokens only (a boolean mask is
+    # additive inside SDPA, so a NaN key it masks would still reach the row)
+    q = fp16_bits_to_f64(w2.q_bits)
+    t = np.arange(w2.max_tokens)
+    phys = w2.block_table[t // w2.page_size]
+    kd = torch_e4m3(w2.k_pool[phys, t % w2.page_size, 0])
+    vd = torch_e4m3(w2.v_pool[phys, t % w2.page_size, 0])
+    ref = np.zeros_like(one)
+    for i, L in enumerate(w2.row_lens):
+        if L > 0:
+            ref[i] = sdpa_rows(q[i], kd[:L], vd[:L], np.ones((w2.num_heads, L), bool),
+                               w2.sm_scale * w2.k_scale) * w2.v_scale
+    assert np.array_equal(np.isnan(ref), np.isnan(one)), "NaN pattern vs SDPA"
+    fin = np.isfinite(one)
+    assert_close_rel(one[fin], ref[fin], 1e-12, "finite part vs SDPA")
+    for S, T in [(1, 64), (4, 13), (7, 8), (60, 1)]:
+        acc, mx, sm = o.verify_dense_split(w2.q_bits, w2.k_pool, w2.v_pool, w2.block_table,
+                                           w2.row_lens, w2.max_tokens, w2.num_kv_heads,
+                                           w2.sm_scale, w2.k_scale, S, T)
+        comb = o.combine(acc, mx, sm, w2.v_scale).reshape(one.shape)
+        assert np.array_equal(np.isnan(comb), np.isnan(one)), f"NaN pattern S={S}"
+        assert_close_rel(comb[fin], one[fin], 1e-12, f"finite part S={S}")
+
+
 def pin_split_combine(o):
     """Split partials combined give the one-pass result (<= 1e-12 relative) for
     S in {1, 2, 4, 7, many}, including splits past every length; each split's
@@ -474,6 +515,6 @@ def pin_selection_order(o):
 ALL_PINS = [
     pin_e4m3_golden, pin_e4m3_structure, pin_e4m3_vs_torch, pin_encoder_roundtrip,
     pin_encoder_vs_torch, pin_one_hot_probe, pin_closed_forms, pin_relocation,
-    pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine,
+    pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine, pin_visible_nan,
     pin_selection_order, pin_fp16_decode, pin_bf16_decode,
 ]

@@ -248,6 +248,31 @@ def test_nan_poison_bit_identical(kernel):
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("splits", [0, 1])
+def test_visible_nan_propagates(orc, kernel, splits):
+    """NaN bytes at positions a row sees reach the output as in the oracle: a
+    NaN K byte makes the rows seeing that token NaN, a NaN V byte makes one
+    column NaN; everything else matches the oracle at the usual bar, with one
+    split and with the planner's splits."""
+    w = wl.make_dense("vnan", 0x7A7, q_rows=4, num_heads=6, num_kv_heads=1, head_dim=256,
+                      ctx=700, page_size=96, pool_pages=9, sigma=1.0, k_scale=0.5,
+                      v_scale=1.5, row_lens=[700, 640, 120, 0], num_splits=splits)
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    tk, tv, dv = 660, 100, 7              # token 660: row 0 only; token 100: rows 0-2
+    k[w.block_table[tk // w.page_size], tk % w.page_size, 0, 11] = 0x7F
+    v[w.block_table[tv // w.page_size], tv % w.page_size, 0, dv] = 0xFF
+    w = dataclasses.replace(w, k_pool=k, v_pool=v)
+    announce("visible nan", kernel, splits)
+    got = gu.run_dense(w, kernel).astype(np.float64)
+    ref = orc.dense_workload(w)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(ref[0]).all() and np.isnan(ref[1:3, :, dv]).all() and not ref[3].any()
+    fin = np.isfinite(ref)
+    gu.assert_parity(got[fin], ref[fin], f"visible nan/{kernel}/S{splits}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 def test_zero_lengths(kernel):
     w = wl.make_dense("zeros", 0x2E0, q_rows=4, num_heads=6, num_kv_heads=1, head_dim=256,
                       ctx=700, page_size=96, pool_pages=9, sigma=1.0, k_scale=1.0, v_scale=1.0,
