@@ -62,6 +62,10 @@ class Oracle:
         lib.orc_combine.restype = ctypes.c_int
         lib.orc_combine_f32.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f64, _p]
         lib.orc_combine_f32.restype = ctypes.c_int
+        lib.orc_combine_lse.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f64, _p, _p]
+        lib.orc_combine_lse.restype = ctypes.c_int
+        lib.orc_combine_lse_f32.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f64, _p, _p]
+        lib.orc_combine_lse_f32.restype = ctypes.c_int
         self.lib = lib
 
     # -- number formats ------------------------------------------------------
@@ -174,25 +178,26 @@ class Oracle:
             raise ValueError(f"orc_qsa_split precondition failed ({rc})")
         return acc, mx, sm
 
-    def combine(self, acc, mx, sm, v_scale) -> np.ndarray:
-        """Merge split partials (FP64 or FP32 arrays) into FP64 rows."""
+    def combine(self, acc, mx, sm, v_scale, with_lse: bool = False):
+        """Merge split partials (FP64 or FP32 arrays) into FP64 rows; with
+        with_lse, also the base-2 LSE of each row: returns (out, lse)."""
         S, R, D = acc.shape
         out = np.empty((R, D), np.float64)
-        if acc.dtype == np.float32:
-            acc = np.ascontiguousarray(acc)
-            mx = np.ascontiguousarray(mx, np.float32)
-            sm = np.ascontiguousarray(sm, np.float32)
-            rc = self.lib.orc_combine_f32(_ptr(acc), _ptr(mx), _ptr(sm), S, R, D,
-                                          float(v_scale), _ptr(out))
+        lse = np.empty(R, np.float64)
+        f32 = acc.dtype == np.float32
+        dt = np.float32 if f32 else np.float64
+        acc = np.ascontiguousarray(acc, dt)
+        mx = np.ascontiguousarray(mx, dt)
+        sm = np.ascontiguousarray(sm, dt)
+        if with_lse:
+            fn = self.lib.orc_combine_lse_f32 if f32 else self.lib.orc_combine_lse
+            rc = fn(_ptr(acc), _ptr(mx), _ptr(sm), S, R, D, float(v_scale), _ptr(out), _ptr(lse))
         else:
-            acc = np.ascontiguousarray(acc, np.float64)
-            mx = np.ascontiguousarray(mx, np.float64)
-            sm = np.ascontiguousarray(sm, np.float64)
-            rc = self.lib.orc_combine(_ptr(acc), _ptr(mx), _ptr(sm), S, R, D,
-                                      float(v_scale), _ptr(out))
+            fn = self.lib.orc_combine_f32 if f32 else self.lib.orc_combine
+            rc = fn(_ptr(acc), _ptr(mx), _ptr(sm), S, R, D, float(v_scale), _ptr(out))
         if rc != 0:
             raise ValueError("orc_combine failed")
-        return out
+        return (out, lse) if with_lse else out
 
     # -- conveniences over the seeded workloads --------------------------------
     def dense_workload(self, w, nthreads=1) -> np.ndarray:

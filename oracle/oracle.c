@@ -537,7 +537,7 @@ int orc_qsa_split(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_poo
 
 static int combine_any(const double *acc64, const float *acc32, const double *mx64,
                        const float *mx32, const double *sm64, const float *sm32, int S,
-                       int R, int D, double v_scale, double *out)
+                       int R, int D, double v_scale, double *out, double *lse)
 {
     if (S <= 0 || R < 0 || D <= 0)
         return -1;
@@ -568,6 +568,9 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
         }
         for (int d = 0; d < D; ++d)
             out[(int64_t)r * D + d] = den != 0.0 ? v_scale * out[(int64_t)r * D + d] / den : 0.0;
+        /* base-2 log of the row's whole sum: log2 sum_t 2^(y_t) = M + log2(den) */
+        if (lse)
+            lse[r] = den != 0.0 ? M + log2(den) : -INFINITY;
     }
     return 0;
 }
@@ -577,7 +580,7 @@ int orc_combine(const double *ws_acc, const double *ws_max, const double *ws_sum
                 double *out)
 {
     return combine_any(ws_acc, NULL, ws_max, NULL, ws_sum, NULL, num_splits, num_rows,
-                       head_dim, v_scale, out);
+                       head_dim, v_scale, out, NULL);
 }
 
 int orc_combine_f32(const float *ws_acc, const float *ws_max, const float *ws_sum,
@@ -585,5 +588,21 @@ int orc_combine_f32(const float *ws_acc, const float *ws_max, const float *ws_su
                     double *out)
 {
     return combine_any(NULL, ws_acc, NULL, ws_max, NULL, ws_sum, num_splits, num_rows,
-                       head_dim, v_scale, out);
+                       head_dim, v_scale, out, NULL);
+}
+
+int orc_combine_lse(const double *ws_acc, const double *ws_max, const double *ws_sum,
+                    int32_t num_splits, int32_t num_rows, int32_t head_dim, double v_scale,
+                    double *out, double *lse)
+{
+    return combine_any(ws_acc, NULL, ws_max, NULL, ws_sum, NULL, num_splits, num_rows,
+                       head_dim, v_scale, out, lse);
+}
+
+int orc_combine_lse_f32(const float *ws_acc, const float *ws_max, const float *ws_sum,
+                        int32_t num_splits, int32_t num_rows, int32_t head_dim, double v_scale,
+                        double *out, double *lse)
+{
+    return combine_any(NULL, ws_acc, NULL, ws_max, NULL, ws_sum, num_splits, num_rows,
+                       head_dim, v_scale, out, lse);
 }

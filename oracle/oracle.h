@@ -79,6 +79,20 @@ int orc_combine_f32(const float *ws_acc, const float *ws_max, const float *ws_su
                     int32_t num_splits, int32_t num_rows, int32_t head_dim, double v_scale,
                     double *out);
 
+/* The same merge, also writing lse[r] = M + log2(sum_s w_s l_s): the base-2
+ * log of the row's whole softmax sum, log2 sum_t 2^(y_t) with y_t the logit
+ * times log2(e); -inf for a row whose splits are all empty.  Two disjoint token
+ * sets of one row merge as LSE = log2(2^lse_1 + 2^lse_2),
+ * o = 2^(lse_1 - LSE) o_1 + 2^(lse_2 - LSE) o_2 (1Cat-vLLM PR "Qualify
+ * calibrated E4M3 and disk PLE with QSA DCP2": base-2 LSE and FP32 partial
+ * output exported for the merge across ranks). */
+int orc_combine_lse(const double *ws_acc, const double *ws_max, const double *ws_sum,
+                    int32_t num_splits, int32_t num_rows, int32_t head_dim, double v_scale,
+                    double *out, double *lse);
+int orc_combine_lse_f32(const float *ws_acc, const float *ws_max, const float *ws_sum,
+                        int32_t num_splits, int32_t num_rows, int32_t head_dim,
+                        double v_scale, double *out, double *lse);
+
 /* Sparse (QSA) verify over selected blocks, a batch of requests.
  *   q          [batch][q_rows][num_heads][head_dim] bfloat16 bit patterns
  *   block_table[batch][max_blocks]: logical block -> physical page (block = page)

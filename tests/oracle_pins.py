@@ -493,6 +493,54 @@ def pin_split_combine(o):
         assert_close_rel(comb, oneq, 1e-12, f"qsa split S={S}")
 
 
+def lse_merge(parts):
+    """Merge (out, lse) pairs of disjoint token sets of the same rows:
+    LSE = log2 sum_k 2^lse_k, o = sum_k 2^(lse_k - LSE) o_k; rows empty in every
+    part give 0."""
+    lses = np.stack([l for _, l in parts])
+    top = lses.max(axis=0)
+    safe = np.where(np.isfinite(top), top, 0.0)
+    w = np.exp2(lses - safe)                                  # 0 for empty parts
+    tot = w.sum(axis=0)
+    out = sum(wk[:, None] * ok for wk, (ok, _) in zip(w, parts))
+    out = np.where(tot[:, None] > 0, out / np.where(tot > 0, tot, 1.0)[:, None], 0.0)
+    return out, np.where(tot > 0, safe + np.log2(np.where(tot > 0, tot, 1.0)), -np.inf)
+
+
+def pin_combine_lse(o):
+    """The base-2 LSE of a row is log2 sum_t 2^(y_t), i.e. torch.logsumexp of its
+    logits over ln 2 (-inf for an empty row), and two disjoint groups of splits,
+    each combined with its LSE and then merged by the LSE rule, give the one-pass
+    output and LSE."""
+    w = _dense_case(1)                       # H6/Hkv1/D32, page 7, lengths 0, 23, 50
+    S, T = 7, 8
+    acc, mx, sm = o.verify_dense_split(w.q_bits, w.k_pool, w.v_pool, w.block_table,
+                                       w.row_lens, w.max_tokens, w.num_kv_heads,
+                                       w.sm_scale, w.k_scale, S, T)
+    out, lse = o.combine(acc, mx, sm, w.v_scale, with_lse=True)
+    assert np.array_equal(out, o.combine(acc, mx, sm, w.v_scale)), "lse form changes out"
+    q = fp16_bits_to_f64(w.q_bits)
+    t = np.arange(w.max_tokens)
+    k = torch_e4m3(w.k_pool[w.block_table[t // w.page_size], t % w.page_size, 0])
+    for i, L in enumerate(w.row_lens):
+        for h in range(w.num_heads):
+            r = i * w.num_heads + h
+            if L <= 0:
+                assert lse[r] == -np.inf, "empty row"
+                continue
+            s = (k[:L] @ q[i, h]) * (w.sm_scale * w.k_scale)
+            ref = float(torch.logsumexp(torch.from_numpy(s), 0)) / math.log(2.0)
+            assert abs(lse[r] - ref) <= 1e-12 * max(1.0, abs(ref)), f"lse row {r}"
+    for cut in (1, 3, 6):
+        a = o.combine(acc[:cut], mx[:cut], sm[:cut], w.v_scale, with_lse=True)
+        b = o.combine(acc[cut:], mx[cut:], sm[cut:], w.v_scale, with_lse=True)
+        mo, ml = lse_merge([a, b])
+        assert_close_rel(mo, out, 1e-12, f"merged output, cut {cut}")
+        live = np.isfinite(lse)
+        assert np.array_equal(np.isfinite(ml), live)
+        assert_close_rel(ml[live], lse[live], 1e-12, f"merged lse, cut {cut}")
+
+
 def pin_selection_order(o):
     import dataclasses
 
@@ -516,5 +564,6 @@ ALL_PINS = [
     pin_e4m3_golden, pin_e4m3_structure, pin_e4m3_vs_torch, pin_encoder_roundtrip,
     pin_encoder_vs_torch, pin_one_hot_probe, pin_closed_forms, pin_relocation,
     pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine, pin_visible_nan,
+    pin_combine_lse,
     pin_selection_order, pin_fp16_decode, pin_bf16_decode,
 ]
