@@ -101,6 +101,36 @@ class DenseBench:
         self.pa.paged_attn_combine_fp32(self.ws, self.plan.num_splits, self.rows,
                                         self.w.head_dim, self.w.v_scale, self.out)
 
+    def combine_lse(self, out32, lse):
+        self.pa.paged_attn_combine_fp32_lse(self.ws, self.plan.num_splits, self.rows,
+                                            self.w.head_dim, self.w.v_scale, out32=out32,
+                                            lse=lse)
+
+    def time_combines(self, reps: int = 50) -> dict:
+        """Back-to-back combines over the workspace of the last verify (so the
+        partials are in cache): FP16 output, and FP32 output + base-2 LSE."""
+        torch = self.torch
+        D = self.w.head_dim
+        out32 = torch.empty(self.rows * D, dtype=torch.float32, device="cuda:0")
+        lse = torch.empty(self.rows, dtype=torch.float32, device="cuda:0")
+        res = {}
+        for name, fn in (("combine_us", self.combine),
+                         ("combine_lse_us", lambda: self.combine_lse(out32, lse))):
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 3)
+        S = self.plan.num_splits
+        res["workspace_bytes"] = S * self.rows * (D + 2) * 4
+        res["timing"] = f"{reps} back-to-back eager launches, events around them"
+        return res
+
     def run_graph(self, steps: int, warmup: int, rotate: bool):
         """Per-call time of verify + combine replayed from a HIP graph.
 
@@ -358,6 +388,8 @@ def main():
         f"verify {m['hot_verify_us']:.2f} us")
     gbs = b.kv_bytes / (m["us"] * 1e-6) / 1e9
     achieved = b.kv_bytes / (m["verify_us"] * 1e-6) / 1e9
+    combines = b.time_combines()
+    log(f"[bench] combine {combines['combine_us']:.2f} us, with LSE {combines['combine_lse_us']:.2f} us")
     plan = b.plan
     del b
     torch.cuda.empty_cache()
@@ -423,6 +455,7 @@ def main():
                      "verify_us_median": round(m["verify_med_us"], 3),
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
+        "combine": combines,
         "cpu_baseline": cpu,
         "sweep": sweep,
         "source_hash": src_hash,

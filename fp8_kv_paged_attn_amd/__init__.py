@@ -56,7 +56,8 @@ class PaWorkspace(ctypes.Structure):
 
 EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
-           "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe")
+           "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
+           "paged_attn_combine_fp32_lse")
 
 _LIB = None
 
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_verify_e4m3.restype = i32
     L.paged_attn_combine_fp32.argtypes = [p, p, p, i32, i32, i32, f32, p, p]
     L.paged_attn_combine_fp32.restype = i32
+    L.paged_attn_combine_fp32_lse.argtypes = [p, p, p, i32, i32, i32, f32, p, p, p, p]
+    L.paged_attn_combine_fp32_lse.restype = i32
     L.qsa_sparse_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, p, i32,
                                          i32, i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                          ctypes.POINTER(PaWorkspace), p]
@@ -257,6 +260,34 @@ def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, o
                                        _scale(out_scale, out.device, "out_scale"),
                                        out.data_ptr(), _stream(out.device))
     _check(rc, "paged_attn_combine_fp32")
+
+
+def paged_attn_combine_fp32_lse(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,
+                                out=None, out32=None, lse=None) -> None:
+    """FP32 combine writing any of: out (float16), out32 (float32), both
+    [num_rows][head_dim] elements, and lse (float32, num_rows): the base-2 LSE of
+    each row, for a merge across ranks."""
+    torch = _torch()
+    acc, mx, sm = ws
+    if out is None and out32 is None and lse is None:
+        raise ValueError("give at least one of out, out32, lse")
+    dev = acc.device
+    for t, dt, n in ((out, torch.float16, num_rows * head_dim),
+                     (out32, torch.float32, num_rows * head_dim), (lse, torch.float32, num_rows)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous() or t.numel() < n
+                              or t.device != dev):
+            raise ValueError(f"outputs must be contiguous {dt} tensors of {n} elements on {dev}")
+    for t in (acc, mx, sm):
+        if t.device != dev or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("workspace must be contiguous float32 on one device")
+    if acc.numel() < num_splits * num_rows * head_dim or min(mx.numel(), sm.numel()) < num_splits * num_rows:
+        raise ValueError("workspace smaller than num_splits x num_rows")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    rc = lib().paged_attn_combine_fp32_lse(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
+                                           int(num_splits), int(num_rows), int(head_dim),
+                                           _scale(out_scale, dev, "out_scale"), ptr(out),
+                                           ptr(out32), ptr(lse), _stream(dev))
+    _check(rc, "paged_attn_combine_fp32_lse")
 
 
 def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,

@@ -123,6 +123,31 @@ int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows
     return PA_OK;
 }
 
+// Checks shared by the combine entry points; any of the three outputs may be
+// null (the caller checks that one is not).
+int32_t combine_checked(const float *ws_acc, const float *ws_max, const float *ws_sum,
+                        int32_t num_splits, int32_t num_rows, int32_t head_dim, float out_scale,
+                        void *out_fp16, float *out_fp32, float *lse, void *stream)
+{
+    if (!ws_acc || !ws_max || !ws_sum)
+        return PA_EINVAL;
+    if (num_splits < 1 || num_rows < 0 || head_dim < 4 || head_dim > 4096 ||
+        head_dim % 4 != 0 || !std::isfinite(out_scale))
+        return PA_EINVAL;
+    if (!aligned16(ws_acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0 ||
+        !aligned16(out_fp32) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return PA_EALIGN;
+    if (num_rows > 0x7FFFFFFF / 2)
+        return PA_EINVAL;
+    int32_t rc = check_device();
+    if (rc != PA_OK)
+        return rc;
+    hipError_t err = pa::launch_combine(ws_acc, ws_max, ws_sum, num_splits, num_rows, head_dim,
+                                        out_scale, static_cast<uint16_t *>(out_fp16), out_fp32,
+                                        lse, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
 // Kernel timer: (begin, end) event pairs handed to the next `armed` verify
 // launches on the device the timer was armed on, passed with the dispatch.
 struct KernelTimer {
@@ -300,22 +325,21 @@ int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const 
                                 int32_t num_splits, int32_t num_rows, int32_t head_dim,
                                 float out_scale, void *out_fp16, void *stream)
 {
-    if (!ws_acc || !ws_max || !ws_sum || !out_fp16)
+    if (!out_fp16)
         return PA_EINVAL;
-    if (num_splits < 1 || num_rows < 0 || head_dim < 4 || head_dim > 4096 ||
-        head_dim % 4 != 0 || !std::isfinite(out_scale))
+    return combine_checked(ws_acc, ws_max, ws_sum, num_splits, num_rows, head_dim, out_scale,
+                           out_fp16, nullptr, nullptr, stream);
+}
+
+int32_t paged_attn_combine_fp32_lse(const float *ws_acc, const float *ws_max,
+                                    const float *ws_sum, int32_t num_splits, int32_t num_rows,
+                                    int32_t head_dim, float out_scale, void *out_fp16,
+                                    float *out_fp32, float *lse, void *stream)
+{
+    if (!out_fp16 && !out_fp32 && !lse)
         return PA_EINVAL;
-    if (!aligned16(ws_acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0)
-        return PA_EALIGN;
-    if (num_rows > 0x7FFFFFFF / 2)
-        return PA_EINVAL;
-    int32_t rc = check_device();
-    if (rc != PA_OK)
-        return rc;
-    hipError_t err = pa::launch_combine(ws_acc, ws_max, ws_sum, num_splits, num_rows, head_dim,
-                                        out_scale, static_cast<uint16_t *>(out_fp16),
-                                        static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? PA_OK : PA_EHIP;
+    return combine_checked(ws_acc, ws_max, ws_sum, num_splits, num_rows, head_dim, out_scale,
+                           out_fp16, out_fp32, lse, stream);
 }
 
 int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,

@@ -25,6 +25,11 @@
 // host so that the grid has about 128 K threads: many splits over few rows
 // (one request, long context) get 16 groups; many rows over few splits (a
 // batch of sparse requests) get 1 or 2.  All arithmetic is FP32.
+//
+// The same kernel can also write the unrounded FP32 output and the base-2 LSE
+// of each row, M + log2(sum_s w_s l_s), for a merge across ranks (1Cat-vLLM PR
+// "Qualify calibrated E4M3 and disk PLE with QSA DCP2": base-2 LSE and FP32
+// partial output exported for cross-rank merging).
 #include "pa_internal.h"
 
 #include <math.h>
@@ -56,7 +61,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                                                            const float *__restrict__ sm,
                                                            int S, int R, int D,
                                                            float out_scale,
-                                                           uint16_t *__restrict__ out)
+                                                           uint16_t *__restrict__ out,
+                                                           float *__restrict__ out32,
+                                                           float *__restrict__ lse)
 {
     constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
     __shared__ float gm[GROUPS > 1 ? kThreads : 1];
@@ -112,25 +119,33 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                         gn[base + k * kLanes]);
     }
     if (ok) {
-        uint16_t h[4];
-        for (int k = 0; k < 4; ++k) {
-            const float o = l != 0.0f ? (num[k] / l) * out_scale : 0.0f;
-            h[k] = __builtin_bit_cast(uint16_t, (_Float16)o);
+        f32x4 o;
+        for (int k = 0; k < 4; ++k)
+            o[k] = l != 0.0f ? (num[k] / l) * out_scale : 0.0f;
+        if (out) {
+            uint16_t h[4];
+            for (int k = 0; k < 4; ++k)
+                h[k] = __builtin_bit_cast(uint16_t, (_Float16)o[k]);
+            uint2 packed = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+            *(uint2 *)(out + (int64_t)r * D + d0) = packed;
         }
-        uint2 packed = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-        *(uint2 *)(out + (int64_t)r * D + d0) = packed;
+        if (out32)
+            *(f32x4 *)(out32 + (int64_t)r * D + d0) = o;
+        // every column chunk of the row holds the same (m, l); chunk 0 writes
+        if (lse && blockIdx.y == 0 && lane == 0)
+            lse[r] = l != 0.0f ? m + log2f(l) : -INFINITY;
     }
 }
 
 template <int GROUPS, int BATCH>
 hipError_t launch_g(const float *acc, const float *mx, const float *sm, int num_splits,
-                    int num_rows, int head_dim, float out_scale, uint16_t *out,
-                    hipStream_t stream)
+                    int num_rows, int head_dim, float out_scale, uint16_t *out, float *out32,
+                    float *lse, hipStream_t stream)
 {
     constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
     dim3 grid((num_rows + kRowsPerWG - 1) / kRowsPerWG, (head_dim + 4 * kLanes - 1) / (4 * kLanes));
     hipLaunchKernelGGL((combine_kernel<GROUPS, BATCH>), grid, dim3(kThreads), 0, stream, acc, mx,
-                       sm, num_splits, num_rows, head_dim, out_scale, out);
+                       sm, num_splits, num_rows, head_dim, out_scale, out, out32, lse);
     return hipGetLastError();
 }
 
@@ -138,7 +153,7 @@ hipError_t launch_g(const float *acc, const float *mx, const float *sm, int num_
 
 hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
                           int num_rows, int head_dim, float out_scale, uint16_t *out,
-                          hipStream_t stream)
+                          float *out32, float *lse, hipStream_t stream)
 {
     if (num_rows == 0)
         return hipSuccess;
@@ -153,9 +168,9 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
     const bool big = (num_splits + groups - 1) / groups > 8;   // splits per thread
 #define PA_COMBINE(G)                                                                          \
     return big ? launch_g<G, 16>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,  \
-                                 stream)                                                       \
+                                 out32, lse, stream)                                           \
                : launch_g<G, 8>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,   \
-                                stream)
+                                out32, lse, stream)
     switch (groups) {
     case 1: PA_COMBINE(1);
     case 2: PA_COMBINE(2);

@@ -45,8 +45,9 @@ hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse,
                               hipStream_t stream, const hipEvent_t *ev = nullptr);
 // Streaming read of bytes (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t stream);
+// Any of out (FP16), out32 (FP32) and lse (base-2 LSE per row) may be null.
 hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
                           int num_rows, int head_dim, float out_scale, uint16_t *out,
-                          hipStream_t stream);
+                          float *out32, float *lse, hipStream_t stream);
 
 }  // namespace pa

@@ -186,6 +186,26 @@ int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const 
                                 int32_t num_splits, int32_t num_rows, int32_t head_dim,
                                 float out_scale, void *out_fp16, void *stream);
 
+/* Combine for a merge across ranks ([NB] commit exposing an optional base-2
+ * LSE and FP32 partial output for cross-rank merging, with the output gate
+ * applied after the merge): the FP32 combination of paged_attn_combine_fp32,
+ * writing any of
+ *   out_fp16 [num_rows][head_dim]  as paged_attn_combine_fp32
+ *   out_fp32 [num_rows][head_dim]  the same values before FP16 rounding
+ *   lse      [num_rows]            M + log2(sum_s w_s sum[s][r]): the base-2 log
+ *                                  of the row's whole softmax sum,
+ *                                  log2 sum_t 2^(y_t), y_t = s_t * log2(e);
+ *                                  -inf for a row whose splits are all empty
+ * Null outputs are skipped; at least one must be given (PA_EINVAL otherwise).
+ * out_fp16 8-byte, out_fp32 16-byte, lse 4-byte aligned (PA_EALIGN otherwise).
+ * Two ranks holding disjoint tokens of the same rows merge as
+ *   LSE = log2(2^lse_1 + 2^lse_2),  o = 2^(lse_1 - LSE) o_1 + 2^(lse_2 - LSE) o_2.
+ * Other arguments as for paged_attn_combine_fp32. */
+int32_t paged_attn_combine_fp32_lse(const float *ws_acc, const float *ws_max,
+                                    const float *ws_sum, int32_t num_splits, int32_t num_rows,
+                                    int32_t head_dim, float out_scale, void *out_fp16,
+                                    float *out_fp32, float *lse, void *stream);
+
 /* Sparse (QSA) verify of a batch over selected blocks ([QSA] sparse split-K
  * paged GQA kernel), writing split partials.  A block is one page.
  *   q_bf16       [batch][q_rows][num_heads][head_dim] BF16, contiguous

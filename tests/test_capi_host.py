@@ -182,6 +182,25 @@ def test_valid_call_without_device_reports_edevice(L):
     assert Call()(L) == PA_EDEVICE
 
 
+def test_combine_lse_rejects_bad_arguments(L):
+    A = ctypes.c_void_p(0x10000)
+    f = L.paged_attn_combine_fp32_lse
+    assert f(A, A, A, 4, 48, 256, 1.0, None, None, None, None) == PA_EINVAL   # no output
+    assert f(None, A, A, 4, 48, 256, 1.0, A, None, None, None) == PA_EINVAL
+    assert f(A, A, A, 0, 48, 256, 1.0, A, None, None, None) == PA_EINVAL
+    assert f(A, A, A, 4, 48, 254, 1.0, A, None, None, None) == PA_EINVAL
+    assert f(A, A, A, 4, 48, 256, float("inf"), None, A, None, None) == PA_EINVAL
+    assert f(A, A, A, 4, 48, 256, 1.0, None, ctypes.c_void_p(0x10008), None, None) == PA_EALIGN
+    assert f(A, A, A, 4, 48, 256, 1.0, None, None, ctypes.c_void_p(0x10002), None) == PA_EALIGN
+    assert f(A, A, A, 4, 48, 256, 1.0, ctypes.c_void_p(0x10004), None, None, None) == PA_EALIGN
+
+
+@no_device
+def test_combine_lse_without_device_reports_edevice(L):
+    A = ctypes.c_void_p(0x10000)
+    assert L.paged_attn_combine_fp32_lse(A, A, A, 4, 48, 256, 1.0, None, None, A, None) == PA_EDEVICE
+
+
 def test_timer_rejects_bad_arguments(L):
     n = ctypes.c_int32(7)
     ms = (ctypes.c_float * 4)()

@@ -14,6 +14,7 @@ import torch
 import fp8_kv_paged_attn_amd as pa
 from fp8_kv_paged_attn_amd import workloads as wl
 from tests import gpu_util as gu
+from tests.oracle_pins import lse_merge
 
 pytestmark = pytest.mark.gpu
 
@@ -382,3 +383,75 @@ def test_stream_read_probe_runs():
     pa.stream_read_probe(buf, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+# ---------------------------------------------------------------------------
+# combine with the base-2 LSE (merge across ranks)
+# ---------------------------------------------------------------------------
+
+def _c3_workspace():
+    w = wl.cached("c3")
+    d = gu.dense_to_dev(w)
+    p = gu.dense_plan(w, "mfma")
+    ws = pa.make_workspace(p, w.q_rows * w.num_heads, w.head_dim, gu.DEV)
+    pa.paged_attn_verify_e4m3(d.q, d.k, d.v, d.table, d.lens, w.max_tokens, w.sm_scale,
+                              w.k_scale, p, ws)
+    return w, p, ws
+
+
+def test_combine_lse_matches_oracle(orc):
+    """The LSE combine's FP16 output is bit-identical to the plain combine's; its
+    FP32 output and LSE match the FP64 oracle merge of the same FP32 partials
+    (FP32 rounding only); empty rows give LSE -inf and zeros."""
+    announce("combine lse c3")
+    w, p, ws = _c3_workspace()
+    R, D = w.q_rows * w.num_heads, w.head_dim
+    out16 = torch.empty(R * D, dtype=torch.float16, device=gu.DEV)
+    ref16 = torch.empty(R * D, dtype=torch.float16, device=gu.DEV)
+    out32 = torch.empty(R * D, dtype=torch.float32, device=gu.DEV)
+    lse = torch.empty(R, dtype=torch.float32, device=gu.DEV)
+    pa.paged_attn_combine_fp32(ws, p.num_splits, R, D, w.v_scale, ref16)
+    pa.paged_attn_combine_fp32_lse(ws, p.num_splits, R, D, w.v_scale, out=out16, out32=out32,
+                                   lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, ref16)
+    S = p.num_splits
+    acc = ws[0].cpu().numpy().reshape(S, R, D)
+    mx = ws[1].cpu().numpy().reshape(S, R)
+    sm = ws[2].cpu().numpy().reshape(S, R)
+    ref_out, ref_lse = orc.combine(acc, mx, sm, w.v_scale, with_lse=True)
+    got = out32.cpu().numpy().astype(np.float64).reshape(R, D)
+    gl = lse.cpu().numpy().astype(np.float64)
+    empty = ~np.isfinite(ref_lse)
+    assert empty.sum() == 18                  # rows 5-7 of 8, 6 heads each
+    assert np.all(gl[empty] == -np.inf) and not got[empty].any()
+    scale = np.abs(ref_out).max()
+    assert np.abs(got - ref_out).max() <= 2e-6 * scale
+    assert np.all(np.abs(gl[~empty] - ref_lse[~empty]) <= 2e-6 * np.maximum(1.0, np.abs(ref_lse[~empty])))
+
+
+@pytest.mark.parametrize("cut", [1, 100, 255])
+def test_cross_rank_merge(orc, cut):
+    """Two groups of splits standing for two ranks, each combined with its LSE
+    and merged by the LSE rule on the host, give the one-pass combine and the
+    oracle's output at the parity bar."""
+    announce("cross-rank merge c3", cut)
+    w, p, ws = _c3_workspace()
+    R, D, S = w.q_rows * w.num_heads, w.head_dim, p.num_splits
+    acc, mx, sm = ws
+    parts = []
+    for lo, hi in ((0, cut), (cut, S)):
+        o32 = torch.empty(R * D, dtype=torch.float32, device=gu.DEV)
+        l32 = torch.empty(R, dtype=torch.float32, device=gu.DEV)
+        part = (acc[lo:hi], mx[lo:hi], sm[lo:hi])         # workspace is [S][rows](...)
+        pa.paged_attn_combine_fp32_lse(part, hi - lo, R, D, w.v_scale, out32=o32, lse=l32)
+        parts.append((o32, l32))
+    full = torch.empty(R * D, dtype=torch.float32, device=gu.DEV)
+    pa.paged_attn_combine_fp32_lse(ws, S, R, D, w.v_scale, out32=full)
+    torch.cuda.synchronize()
+    merged, _ = lse_merge([(o.cpu().numpy().astype(np.float64).reshape(R, D),
+                            l.cpu().numpy().astype(np.float64)) for o, l in parts])
+    one = full.cpu().numpy().astype(np.float64).reshape(R, D)
+    assert np.abs(merged - one).max() <= 4e-6 * np.abs(one).max()
+    ref = orc.dense_workload(w).reshape(R, D)
+    gu.assert_parity(merged.astype(np.float16), ref, f"cross-rank merge cut {cut}")
