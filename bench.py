@@ -106,9 +106,10 @@ class DenseBench:
                                             self.w.head_dim, self.w.v_scale, out32=out32,
                                             lse=lse)
 
-    def time_combines(self, reps: int = 50) -> dict:
-        """Back-to-back combines over the workspace of the last verify (so the
-        partials are in cache): FP16 output, and FP32 output + base-2 LSE."""
+    def time_combines(self, reps: int = 20) -> dict:
+        """Combines over the workspace of the last verify (so the partials are
+        in cache), from graph replays of GRAPH_CALLS back-to-back launches: FP16
+        output, and FP32 output + base-2 LSE."""
         torch = self.torch
         D = self.w.head_dim
         out32 = torch.empty(self.rows * D, dtype=torch.float32, device="cuda:0")
@@ -116,19 +117,30 @@ class DenseBench:
         res = {}
         for name, fn in (("combine_us", self.combine),
                          ("combine_lse_us", lambda: self.combine_lse(out32, lse))):
-            fn()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(GRAPH_CALLS):
+                    fn()
+            g.replay()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
-                fn()
+                g.replay()
             e1.record()
             torch.cuda.synchronize()
-            res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 3)
+            res[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * GRAPH_CALLS), 3)
+            del g
         S = self.plan.num_splits
         res["workspace_bytes"] = S * self.rows * (D + 2) * 4
-        res["timing"] = f"{reps} back-to-back eager launches, events around them"
+        res["timing"] = f"{reps} replays of a graph of {GRAPH_CALLS} launches"
         return res
 
     def run_graph(self, steps: int, warmup: int, rotate: bool):
