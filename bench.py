@@ -286,6 +286,40 @@ def sweep_entry(name: str, kv_bytes: int, plan, m: dict, **extra) -> dict:
             "hot_verify_us": round(m["hot_verify_us"], 3)}
 
 
+class BatchBench(DenseBench):
+    """A batch of independent dense requests resident on the device."""
+
+    def __init__(self, w, n_copies: int, kernel: str):
+        import numpy as np
+        import torch
+
+        import fp8_kv_paged_attn_amd as pa
+
+        self.w, self.pa, self.torch = w, pa, torch
+        dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(np.ascontiguousarray(w.q_bits).view(np.int16)).view(
+            torch.float16).to(dev)
+        k = torch.from_numpy(w.k_pool).to(dev)
+        v = torch.from_numpy(w.v_pool).to(dev)
+        self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
+        self.table = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
+        self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
+        G = w.num_heads // w.num_kv_heads
+        self.plan = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
+                            splits=w.num_splits, kernel=kernel)
+        self.rows = w.num_rows
+        self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
+        self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),
+                               dtype=torch.float16, device=dev)
+        self.kv_bytes = w.kv_bytes()
+
+    def verify(self, i: int):
+        k, v = self.pools[i % len(self.pools)]
+        w = self.w
+        self.pa.paged_attn_verify_batch_e4m3(self.q, k, v, self.table, self.lens, w.sm_scale,
+                                             w.k_scale, self.plan, self.ws)
+
+
 def read_ceiling(torch, pa, nbytes: int = 2 << 30, reps: int = 5):
     """Read bandwidth (GB/s) of the plain streaming-read probe over nbytes."""
     buf = torch.zeros(nbytes // 16, 4, dtype=torch.int32, device="cuda:0")
@@ -423,6 +457,13 @@ def main():
         sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, measure(bq, steps, args.warmup),
                                  units=wq.batch * wq.num_kv_heads))
         del bq
+        torch.cuda.empty_cache()
+        log("[bench] sweep batch (independent requests)")
+        wb = wl.cached("batch")
+        bb = BatchBench(wb, copies_for(2 * wb.k_pool.size), args.kernel)
+        sweep.append(sweep_entry(wb.name, bb.kv_bytes, bb.plan, measure(bb, steps, args.warmup),
+                                 units=wb.batch * wb.num_kv_heads))
+        del bb
         torch.cuda.empty_cache()
         sweep.append(sweep_entry(w.name, w.kv_bytes(), plan, m, ctx=w.max_tokens))
 

@@ -57,7 +57,7 @@ class PaWorkspace(ctypes.Structure):
 EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
-           "paged_attn_combine_fp32_lse")
+           "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3")
 
 _LIB = None
 
@@ -84,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_verify_e4m3.restype = i32
     L.paged_attn_combine_fp32.argtypes = [p, p, p, i32, i32, i32, f32, p, p]
     L.paged_attn_combine_fp32.restype = i32
+    L.paged_attn_verify_batch_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, i32,
+                                               i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
+                                               ctypes.POINTER(PaWorkspace), p]
+    L.paged_attn_verify_batch_e4m3.restype = i32
     L.paged_attn_combine_fp32_lse.argtypes = [p, p, p, i32, i32, i32, f32, p, p, p, p]
     L.paged_attn_combine_fp32_lse.restype = i32
     L.qsa_sparse_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, p, i32,
@@ -243,6 +247,30 @@ def paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens:
     _check(rc, "paged_attn_verify_e4m3")
 
 
+def paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_scale, k_scale,
+                                 p: PaPlan, ws) -> None:
+    """Dense verify of a batch of independent requests into the FP32 split workspace."""
+    torch = _torch()
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous float16 tensor [batch][q_rows][heads][head_dim]")
+    dev = q.device
+    pool = _pool(k_pool, v_pool, dev)
+    B, qr, H, D = q.shape
+    if k_pool.shape[3] != D:
+        raise ValueError("head_dim of q and the pool differ")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch][max_blocks]")
+    if tuple(row_lens.shape) != (B, qr):
+        raise ValueError("row_lens must be [batch][q_rows]")
+    Hkv = k_pool.shape[2]
+    rc = lib().paged_attn_verify_batch_e4m3(
+        q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
+        block_table.shape[1], _i32(row_lens, "row_lens", dev), B, qr, H, Hkv, D,
+        _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"), ctypes.byref(p),
+        ctypes.byref(_ws(*ws)), _stream(dev))
+    _check(rc, "paged_attn_verify_batch_e4m3")
+
+
 def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,
                             out) -> None:
     """FP32 combine of split partials into out (float16, [num_rows][head_dim] elements)."""
@@ -337,6 +365,26 @@ def verify(q, k_pool, v_pool, block_table, row_lens, max_tokens: int, *, sm_scal
     paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens, sm_scale,
                            k_scale, p, ws)
     paged_attn_combine_fp32(ws, p.num_splits, qr * H, D, v_scale, out)
+    return out
+
+
+def verify_batch(q, k_pool, v_pool, block_table, row_lens, *, sm_scale, k_scale, v_scale,
+                 splits: int = 0, kernel: str = "auto", p: Optional[PaPlan] = None,
+                 ws: Optional[Tuple] = None, out=None):
+    """Dense verify of a batch of requests; returns FP16 [batch][q_rows][heads][head_dim]."""
+    torch = _torch()
+    B, qr, H, D = q.shape
+    Hkv = k_pool.shape[2]
+    cap = block_table.shape[1] * k_pool.shape[1]
+    if p is None:
+        p = plan(cap, qr * (H // Hkv), B * Hkv, D, splits=splits, kernel=kernel)
+    if ws is None:
+        ws = make_workspace(p, B * qr * H, D, q.device)
+    if out is None:
+        out = torch.empty((B, qr, H, D), dtype=torch.float16, device=q.device)
+    paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_scale, k_scale,
+                                 p, ws)
+    paged_attn_combine_fp32(ws, p.num_splits, B * qr * H, D, v_scale, out)
     return out
 
 

@@ -20,6 +20,10 @@ namespace {
 constexpr int kTileTokens = 64;
 constexpr int kMaxRowsPerUnit = 48;
 constexpr int kMaxQRows = 8;
+// the batched entry: up to 16 query rows, up to 96 rows per KV unit (two
+// 48-row chunks, one workgroup each)
+constexpr int kMaxRowsPerUnitBatch = 96;
+constexpr int kMaxQRowsBatch = 16;
 constexpr int kDefaultCUs = 256;
 // Fewest tokens a split should read, so that the FP32 partial it writes
 // (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.
@@ -65,16 +69,17 @@ int32_t check_pool(const pa_kv_pool *kv)
 }
 
 int32_t check_shape(int32_t q_rows, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t *rows_per_unit)
+                    int32_t *rows_per_unit, int32_t max_q_rows = kMaxQRows,
+                    int32_t max_rows = kMaxRowsPerUnit)
 {
     if (q_rows < 1 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0)
         return PA_EINVAL;
-    if (q_rows > kMaxQRows)
+    if (q_rows > max_q_rows)
         return PA_EUNSUPPORTED;
     if (head_dim != 128 && head_dim != 256)
         return PA_EUNSUPPORTED;
     int64_t rows = (int64_t)q_rows * (num_heads / num_kv_heads);
-    if (rows > kMaxRowsPerUnit)
+    if (rows > max_rows)
         return PA_EUNSUPPORTED;
     *rows_per_unit = (int32_t)rows;
     return PA_OK;
@@ -318,6 +323,73 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     (void)kLog2e;
+    return dispatch(a, plan, head_dim, false, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                                     const int32_t *block_table, int32_t max_blocks_per_req,
+                                     const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float sm_scale, float k_scale, const pa_plan *plan,
+                                     const pa_workspace *ws, void *stream)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!q_fp16 || !block_table || !row_lens)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit,
+                          kMaxQRowsBatch, kMaxRowsPerUnitBatch)) != PA_OK)
+        return rc;
+    if (!aligned16(q_fp16))
+        return PA_EALIGN;
+    if (batch < 1 || max_blocks_per_req < 1)
+        return PA_EINVAL;
+    const int64_t cap = (int64_t)max_blocks_per_req * kv->page_size;
+    if (cap > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((int64_t)batch * num_kv_heads > 65535)
+        return PA_EUNSUPPORTED;
+    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
+        return rc;
+    if ((rc = check_plan(plan, (int32_t)cap, rows_per_unit, batch * num_kv_heads, head_dim)) !=
+        PA_OK)
+        return rc;
+    const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
+    if (total_rows > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
+        return rc;
+
+    pa::VerifyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q_fp16);
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.page_stride = kv->page_stride;
+    a.token_stride = kv->token_stride;
+    a.head_stride = kv->head_stride;
+    a.page_size = kv->page_size;
+    a.block_table = block_table;
+    a.table_stride = max_blocks_per_req;
+    a.sel = nullptr;
+    a.topk = 0;
+    a.row_lens = row_lens;
+    a.len_cap = (int32_t)cap;
+    a.list_len = (int32_t)cap;
+    a.batch = batch;
+    a.q_rows = q_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.rows = rows_per_unit;
+    a.num_splits = plan->num_splits;
+    a.tokens_per_split = plan->tokens_per_split;
+    a.total_rows = (int32_t)total_rows;
+    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    a.ws_acc = ws->acc;
+    a.ws_max = ws->max;
+    a.ws_sum = ws->sum;
     return dispatch(a, plan, head_dim, false, static_cast<hipStream_t>(stream));
 }
 

@@ -237,12 +237,13 @@ __device__ __forceinline__ void scale_in_place(f32x4 &x, float f)
     x = t;
 }
 
-// Max over lanes 0..7 (the row lengths of one request), broadcast to the wave.
-__device__ __forceinline__ int max8_broadcast(int v)
+// Max over lanes 0..15 (the row lengths of one request), broadcast to the wave.
+__device__ __forceinline__ int max16_broadcast(int v)
 {
     v = max(v, __shfl_xor(v, 1, 64));
     v = max(v, __shfl_xor(v, 2, 64));
     v = max(v, __shfl_xor(v, 4, 64));
+    v = max(v, __shfl_xor(v, 8, 64));
     return __builtin_amdgcn_readfirstlane(v);
 }
 
@@ -298,7 +299,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int unit = blockIdx.y;
     const int b = unit / a.num_kv_heads;
     const int kvh = unit - b * a.num_kv_heads;
-    const int R = a.rows, G = a.group;
+    // rows of a KV unit beyond 48 go to further workgroups (grid z): this one
+    // takes rows row0 .. row0 + R - 1 of the unit
+    const int row0 = blockIdx.z * (16 * kRowBlocks);
+    const int R = min(a.rows - row0, 16 * kRowBlocks), G = a.group;
     const int ps = a.page_size;
 
     uint8_t *const k_st = smem;                               // [2][kWaves][BLOCK]
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         for (int i = w; i < nq; i += kWaves) {
             const int r = i * kQRowsPerDma + r_in;
             if (r < R) {
-                const int qi = r / G, h = kvh * G + (r - qi * G);
+                const int qi = (row0 + r) / G, h = kvh * G + (row0 + r - qi * G);
                 const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + qi) * a.num_heads + h) * D;
                 dma16((const uint8_t *)qrow + 16 * (c ^ (r & 15)),
                       __builtin_amdgcn_readfirstlane(lds_addr(smem + i * 1024)));
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     const int lo = split * a.tokens_per_split;
     const int hi_list = min(lo + a.tokens_per_split, a.list_len);
-    const int32_t *table = SPARSE ? a.block_table + (int64_t)b * a.table_stride : a.block_table;
+    const int32_t *table = a.block_table + (int64_t)b * a.table_stride;
     int slot0 = 0, nslots = 0;
     if (hi_list > lo) {
         slot0 = divp(lo, dm);
@@ -347,12 +351,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             ent[k] = SPARSE ? a.sel[((int64_t)b * a.num_kv_heads + kvh) * a.topk + slot0 + i]
                             : table[slot0 + i];
     }
-    const int lmax = max8_broadcast(lmine);
+    const int lmax = max16_broadcast(lmine);
     int lrow[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r = rb * 16 + n;
-        const int lr = __shfl(lmine, r < R ? r / G : 0, 64);
+        const int lr = __shfl(lmine, r < R ? (row0 + r) / G : 0, 64);
         lrow[rb] = r < R ? lr : 0;
     }
     // row blocks up to the last one with a row that sees a token
@@ -882,7 +886,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
                 fv[v] = xf[v][r] * kPUnscale;
-            const int i = r / G, h = kvh * G + (r - i * G);
+            const int i = (row0 + r) / G, h = kvh * G + (row0 + r - i * G);
             const int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             float *dst = a.ws_acc + (ws_base + orow) * D;
 #pragma unroll
@@ -934,7 +938,9 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
     const int64_t slots = (int64_t)(a.tokens_per_split - 1) / a.page_size + 2;
     if (slots > max_slots<D>())
         return hipErrorNotSupported;
-    dim3 grid(a.num_splits, a.batch * a.num_kv_heads);
+    // grid z: chunks of 48 rows of a KV unit (one chunk up to 48 rows)
+    dim3 grid(a.num_splits, a.batch * a.num_kv_heads,
+              (a.rows + 16 * kRowBlocks - 1) / (16 * kRowBlocks));
     hipExtLaunchKernelGGL((verify_mfma_kernel<D, SPARSE>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
                           make_magic(a.page_size));
@@ -946,7 +952,7 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
 hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse, hipStream_t stream,
                               const hipEvent_t *ev)
 {
-    if (a.rows > 16 * kRowBlocks)
+    if (a.rows < 1 || a.rows > 65535 * 16 * kRowBlocks)
         return hipErrorNotSupported;
     if (head_dim == 256)
         return sparse ? launch_t<256, true>(a, stream, ev) : launch_t<256, false>(a, stream, ev);

@@ -53,7 +53,7 @@ __device__ inline bool resolve(const VerifyArgs &a, int b, int g, int pos, int l
         u = pos - blk * ps;
         if (t >= lmax)
             return false;
-        off = (int64_t)a.block_table[blk] * a.page_stride;
+        off = (int64_t)a.block_table[(int64_t)b * a.table_stride + blk] * a.page_stride;
     } else {
         int j = pos / ps;
         u = pos - j * ps;
@@ -78,12 +78,14 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
     __shared__ float p_s[kMaxRows][kTile + 1];
     __shared__ int32_t tok_s[kTile];
     __shared__ float m_s[kMaxRows], l_s[kMaxRows], alpha_s[kMaxRows];
-    __shared__ int32_t len_s[8];
+    __shared__ int32_t len_s[16];
 
     const int tid = threadIdx.x;
     const int split = blockIdx.x, unit = blockIdx.y;
     const int b = unit / a.num_kv_heads, g = unit - b * a.num_kv_heads;
-    const int R = a.rows, G = a.group;
+    // rows of a KV unit beyond 48 go to further workgroups (grid z)
+    const int row0 = blockIdx.z * kMaxRows;
+    const int R = min(a.rows - row0, kMaxRows), G = a.group;
 
     if (tid < a.q_rows) {
         int L = a.row_lens[(int64_t)b * a.q_rows + tid];
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
     }
     for (int idx = tid; idx < R * D; idx += kThreads) {
         int r = idx / D, d = idx - r * D;
-        int i = r / G, h = g * G + (r - i * G);
+        int i = (row0 + r) / G, h = g * G + (row0 + r - i * G);
         uint16_t bits = a.q[(((int64_t)b * a.q_rows + i) * a.num_heads + h) * D + d];
         q_s[r][d] = SPARSE ? bf16_to_float(bits) : fp16_to_float(bits);
     }
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
             int r = idx / kTile, j = idx - r * kTile;
             int t = tok_s[j];
             float s = -INFINITY;
-            if (t >= 0 && t < len_s[r / G]) {
+            if (t >= 0 && t < len_s[(row0 + r) / G]) {
                 float dot = 0.0f;
                 for (int d = 0; d < D; ++d)
                     dot += q_s[r][d] * e4m3_to_float(k_s[j][d]);
@@ -181,13 +183,13 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 #pragma unroll
     for (int r = 0; r < kMaxRows; ++r) {
         if (r < R && tid < D) {
-            int i = r / G, h = g * G + (r - i * G);
+            int i = (row0 + r) / G, h = g * G + (row0 + r - i * G);
             int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             a.ws_acc[(ws_base + orow) * D + tid] = acc[r];
         }
     }
     if (tid < R) {
-        int i = tid / G, h = g * G + (tid - i * G);
+        int i = (row0 + tid) / G, h = g * G + (row0 + tid - i * G);
         int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
         a.ws_max[ws_base + orow] = m_s[tid];
         a.ws_sum[ws_base + orow] = l_s[tid];
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
                                 hipStream_t stream, const hipEvent_t *ev)
 {
-    dim3 grid(a.num_splits, a.batch * a.num_kv_heads);
+    dim3 grid(a.num_splits, a.batch * a.num_kv_heads, (a.rows + kMaxRows - 1) / kMaxRows);
     dim3 block(kThreads);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     if (head_dim == 256 && !sparse)

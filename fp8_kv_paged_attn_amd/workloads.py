@@ -309,6 +309,99 @@ def make_dense(name: str, seed: int, *, q_rows: int, num_heads: int,
         num_splits=num_splits)
 
 
+@dataclasses.dataclass
+class DenseBatchWorkload:
+    """A batch of independent dense verify requests sharing one pool."""
+
+    name: str
+    q_bits: np.ndarray         # uint16 fp16 bits, [batch][q_rows][num_heads][head_dim]
+    k_pool: np.ndarray         # uint8, [num_pages][page_size][num_kv_heads][head_dim]
+    v_pool: np.ndarray
+    block_table: np.ndarray    # int32 [batch][max_blocks]
+    row_lens: np.ndarray       # int32 [batch][q_rows]
+    batch: int
+    q_rows: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_blocks: int
+    sm_scale: float
+    k_scale: float
+    v_scale: float
+    num_splits: int = 0
+
+    @property
+    def num_rows(self) -> int:
+        return self.batch * self.q_rows * self.num_heads
+
+    @property
+    def cap(self) -> int:
+        return self.max_blocks * self.page_size
+
+    def request(self, b: int) -> DenseWorkload:
+        """Request b as a single-request workload over the shared pool."""
+        return DenseWorkload(
+            name=f"{self.name}[{b}]", q_bits=self.q_bits[b], k_pool=self.k_pool,
+            v_pool=self.v_pool, block_table=self.block_table[b], row_lens=self.row_lens[b],
+            max_tokens=self.cap, q_rows=self.q_rows, num_heads=self.num_heads,
+            num_kv_heads=self.num_kv_heads, head_dim=self.head_dim, page_size=self.page_size,
+            sm_scale=self.sm_scale, k_scale=self.k_scale, v_scale=self.v_scale)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes: per request, longest visible prefix x heads x D x 2."""
+        lmax = np.clip(self.row_lens, 0, self.cap).max(axis=1)
+        return int(lmax.sum()) * self.num_kv_heads * self.head_dim * 2
+
+
+def make_dense_batch(name: str, seed: int, *, ctxs: List[int], q_rows: int, num_heads: int,
+                     num_kv_heads: int, head_dim: int, page_size: int, sigma: float,
+                     k_scale: float, v_scale: float, max_blocks: Optional[int] = None,
+                     row_lens: Optional[List[List[int]]] = None,
+                     num_splits: int = 0) -> DenseBatchWorkload:
+    """A batch of requests of context ctxs[b], each built like make_dense (its
+    own seeded sub-stream), their pages concatenated into one pool.  Table rows
+    are padded to max_blocks with the request's first page; rows see
+    ctx - q_rows + 1 + i tokens unless row_lens is given."""
+    B = len(ctxs)
+    need = [-(-c // page_size) for c in ctxs]
+    max_blocks = max_blocks or max(need)
+    assert max_blocks >= max(need)
+    reqs = []
+    for b, c in enumerate(ctxs):
+        lens = None if row_lens is None else row_lens[b]
+        reqs.append(make_dense(f"{name}_{b}", substream_seed(seed, f"req{b}"), q_rows=q_rows,
+                               num_heads=num_heads, num_kv_heads=num_kv_heads,
+                               head_dim=head_dim, ctx=c, page_size=page_size,
+                               pool_pages=need[b] + 1, sigma=sigma, k_scale=k_scale,
+                               v_scale=v_scale, row_lens=lens))
+    k_pool = np.concatenate([r.k_pool for r in reqs])
+    v_pool = np.concatenate([r.v_pool for r in reqs])
+    table = np.zeros((B, max_blocks), np.int32)
+    base = 0
+    for b, r in enumerate(reqs):
+        t = r.block_table.astype(np.int64) + base
+        table[b, :t.size] = t
+        table[b, t.size:] = t[0]
+        base += r.k_pool.shape[0]
+    return DenseBatchWorkload(
+        name=name, q_bits=np.stack([r.q_bits for r in reqs]), k_pool=k_pool, v_pool=v_pool,
+        block_table=table, row_lens=np.stack([r.row_lens for r in reqs]).astype(np.int32),
+        batch=B, q_rows=q_rows, num_heads=num_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, page_size=page_size, max_blocks=max_blocks,
+        sm_scale=reqs[0].sm_scale, k_scale=reqs[0].k_scale, v_scale=reqs[0].v_scale,
+        num_splits=num_splits)
+
+
+def config_batch() -> DenseBatchWorkload:
+    """Independent-request batch: 8 requests, q16 rows, H6/Hkv1/D256, E4M3 pages of
+    3296 tokens, contexts 4K..32K (mixed lengths), k 0.37, v 1.9."""
+    ctxs = [32768, 4096, 16384, 24576, 8192, 28672, 12288, 20480]
+    return make_dense_batch("batch_b8_q16_h6_kv1_d256_4k-32k", BASE_SEED + 5, ctxs=ctxs,
+                            q_rows=16, num_heads=6, num_kv_heads=1, head_dim=256,
+                            page_size=3296, sigma=1.5, k_scale=0.37, v_scale=1.9)
+
+
 def make_qsa(name: str, seed: int, *, batch: int, q_rows: int, num_heads: int,
              num_kv_heads: int, head_dim: int, ctx: int, page_size: int,
              topk: int, k_scale: float, v_scale: float, sigma: float = 1.0,
@@ -448,4 +541,5 @@ CONFIGS: Dict[str, object] = {
     "c2_128k": lambda: config_c2(131072),
     "c3": config_c3,
     "c4": config_c4,
+    "batch": config_batch,
 }

@@ -171,6 +171,30 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream);
 
+/* Dense verify of a batch of independent requests ([DN] first section: shapes
+ * outside the single-request q2-8 route -- independent-request batches, q16,
+ * other grouped shapes -- take a path with FP32 accumulation and the FP32
+ * split workspace), writing split partials.
+ *   q_fp16       [batch][q_rows][num_heads][head_dim] FP16, contiguous, 16-byte aligned
+ *   block_table  [batch][max_blocks_per_req] int32: request b's logical page ->
+ *                physical page; entries up to the longest row of each request
+ *                must name pages in the pool
+ *   row_lens     [batch][q_rows] int32: row i of request b sees its tokens
+ *                t < clamp(len, 0, max_blocks_per_req*page_size); zero allowed
+ *   q_rows 1..16; num_heads % num_kv_heads == 0; q_rows*num_heads/num_kv_heads
+ *   <= 96 rows per KV head (more than 48 run as two row chunks, each reading
+ *   the unit's K/V); batch*num_kv_heads <= 65535; head_dim 128 or 256
+ *   plan         (host) from paged_attn_plan(max_blocks_per_req*page_size,
+ *                q_rows*num_heads/num_kv_heads, batch*num_kv_heads, head_dim, ...)
+ *   rows of the workspace and of the combined output: (b, i, h).
+ * Other arguments, masking and errors as for paged_attn_verify_e4m3. */
+int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                                     const int32_t *block_table, int32_t max_blocks_per_req,
+                                     const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     float sm_scale, float k_scale, const pa_plan *plan,
+                                     const pa_workspace *ws, void *stream);
+
 /* FP32 combination of split partials into FP16 rows ([DN] first section):
  *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),
  *   out[r][d] = fp16_rne(out_scale * sum_s w_s acc[s][r][d] / sum_s w_s sum[s][r]),

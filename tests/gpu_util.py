@@ -73,6 +73,30 @@ def run_dense(w, kernel="auto", splits: Optional[int] = None, d: Optional[DenseD
     return res
 
 
+def run_batch(w, kernel="auto", splits: Optional[int] = None):
+    """A DenseBatchWorkload through paged_attn_verify_batch_e4m3 + combine."""
+    q = fp16_tensor(w.q_bits).to(DEV)
+    k = torch.from_numpy(w.k_pool).to(DEV)
+    v = torch.from_numpy(w.v_pool).to(DEV)
+    bt = torch.from_numpy(w.block_table.astype(np.int32)).to(DEV)
+    lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(DEV)
+    G = w.num_heads // w.num_kv_heads
+    s = w.num_splits if splits is None else splits
+    p = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, splits=s,
+                kernel=kernel)
+    out = pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
+                          v_scale=w.v_scale, p=p)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_batch(orc, w, nthreads=1) -> np.ndarray:
+    """The oracle request by request (each over the shared pool, capped at the
+    table width)."""
+    return np.stack([orc.dense_workload(w.request(b), nthreads=nthreads)
+                     for b in range(w.batch)])
+
+
 def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     q = bf16_tensor(w.q_bits).to(DEV)
     k = torch.from_numpy(w.k_pool).to(DEV)

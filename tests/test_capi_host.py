@@ -182,6 +182,51 @@ def test_valid_call_without_device_reports_edevice(L):
     assert Call()(L) == PA_EDEVICE
 
 
+def test_verify_batch_rejects_bad_arguments(L):
+    pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
+                       head_stride=256, num_pages=64, page_size=64)
+    p = pa.PaPlan()
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 0, 0, ctypes.byref(p)) == PA_OK
+    ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
+                        stat_bytes=1 << 40)
+    A = ctypes.c_void_p(0x60000)
+    f = L.paged_attn_verify_batch_e4m3
+
+    def call(q=A, table=A, mb=8, lens=A, B=4, qr=16, H=6, Hkv=1, D=256, sm=0.0625, ks=1.0,
+             plan=p, w=ws):
+        return f(q, ctypes.byref(pool), table, mb, lens, B, qr, H, Hkv, D, sm, ks,
+                 ctypes.byref(plan), ctypes.byref(w), None)
+
+    assert call(q=None) == PA_EINVAL
+    assert call(table=None) == PA_EINVAL
+    assert call(B=0) == PA_EINVAL
+    assert call(mb=0) == PA_EINVAL
+    assert call(qr=17) == PA_EUNSUPPORTED
+    assert call(qr=16, H=12, Hkv=1) == PA_EUNSUPPORTED        # 192 rows per KV head
+    assert call(H=7, Hkv=2) == PA_EINVAL
+    assert call(D=192) == PA_EUNSUPPORTED
+    assert call(q=ctypes.c_void_p(0x60008)) == PA_EALIGN
+    assert call(sm=-1.0) == PA_EINVAL
+    assert call(mb=9) == PA_EPLAN                              # plan made for 8 blocks
+    assert call(B=3) == PA_EPLAN                               # plan made for 4 units
+    small = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=16, stat_bytes=16)
+    assert call(w=small) == PA_EWORKSPACE
+
+
+@no_device
+def test_verify_batch_without_device_reports_edevice(L):
+    pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
+                       head_stride=256, num_pages=64, page_size=64)
+    p = pa.PaPlan()
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 0, 0, ctypes.byref(p)) == PA_OK
+    ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
+                        stat_bytes=1 << 40)
+    A = ctypes.c_void_p(0x60000)
+    assert L.paged_attn_verify_batch_e4m3(A, ctypes.byref(pool), A, 8, A, 4, 16, 6, 1, 256,
+                                          0.0625, 1.0, ctypes.byref(p), ctypes.byref(ws),
+                                          None) == PA_EDEVICE
+
+
 def test_combine_lse_rejects_bad_arguments(L):
     A = ctypes.c_void_p(0x10000)
     f = L.paged_attn_combine_fp32_lse

@@ -455,3 +455,54 @@ def test_cross_rank_merge(orc, cut):
     assert np.abs(merged - one).max() <= 4e-6 * np.abs(one).max()
     ref = orc.dense_workload(w).reshape(R, D)
     gu.assert_parity(merged.astype(np.float16), ref, f"cross-rank merge cut {cut}")
+
+
+# ---------------------------------------------------------------------------
+# batches of independent requests (q up to 16, row chunks, Hkv > 1)
+# ---------------------------------------------------------------------------
+
+BATCHES = [
+    # (ctxs, q_rows, H, Hkv, D, page, row_lens, splits)
+    ([700, 130, 1], 16, 6, 1, 256, 96, None, 0),
+    ([300, 64, 517, 1000], 4, 8, 2, 128, 64, [[300, 0, 299, 1], [64, 64, 0, 63],
+                                                [517, 500, 1, 2], [0, 0, 0, 0]], 3),
+    ([2500, 900], 12, 4, 1, 256, 848, None, 5),
+    ([129, 64, 200], 16, 6, 2, 256, 1, None, 2),
+]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", range(len(BATCHES)))
+def test_batch_small(orc, case, kernel):
+    ctxs, qr, H, Hkv, D, page, lens, splits = BATCHES[case]
+    w = wl.make_dense_batch(f"batch{case}", 0xBA7C0 + case, ctxs=ctxs, q_rows=qr,
+                            num_heads=H, num_kv_heads=Hkv, head_dim=D, page_size=page,
+                            sigma=1.2, k_scale=0.45, v_scale=1.6, row_lens=lens,
+                            num_splits=splits)
+    announce("batch", case, ctxs, qr, H, Hkv, D, page, kernel)
+    got = gu.run_batch(w, kernel)
+    gu.assert_parity(got, gu.oracle_batch(orc, w), f"batch{case}/{kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_batch_matches_single_requests(kernel):
+    """With equal split boundaries (256 tokens), each request of the batch entry
+    is bit-identical to the single-request entry on that request alone."""
+    w = wl.make_dense_batch("bsingle", 0xB51, ctxs=[1000, 300, 770], q_rows=8, num_heads=6,
+                            num_kv_heads=1, head_dim=256, page_size=96, sigma=1.0,
+                            k_scale=0.5, v_scale=1.5, max_blocks=12)
+    announce("batch vs single", kernel)
+    got = gu.run_batch(w, kernel, splits=w.cap // 256)
+    for b in range(w.batch):
+        r = dataclasses.replace(w.request(b), max_tokens=w.cap)
+        single = gu.run_dense(r, kernel, splits=w.cap // 256)
+        assert np.array_equal(got[b], single), b
+
+
+def test_batch_config(orc):
+    """The named batch configuration (8 requests, q16, contexts 4K-32K) at full
+    size, the MFMA kernel in the benchmark's plan."""
+    w = wl.cached("batch")
+    announce("batch config", w.name)
+    got = gu.run_batch(w, "mfma")
+    gu.assert_parity(got, gu.oracle_batch(orc, w, nthreads=16), "batch config")
