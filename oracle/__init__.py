@@ -40,6 +40,9 @@ class Oracle:
         lib.orc_e4m3_encode.restype = ctypes.c_uint8
         lib.orc_e4m3_encode_array.argtypes = [_p, _i64, _p]
         lib.orc_e4m3_encode_array.restype = None
+        lib.orc_cache_write.argtypes = [_p, _p, _i64, _i32, _i32, _p, _p, _p, _i64, _i64, _i64,
+                                        _i32, _i32, ctypes.c_float, ctypes.c_float]
+        lib.orc_cache_write.restype = ctypes.c_int
         lib.orc_fp16_value.argtypes = [ctypes.c_uint16]
         lib.orc_fp16_value.restype = _f64
         lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
@@ -73,6 +76,24 @@ class Oracle:
         t = np.empty(256, np.float64)
         self.lib.orc_e4m3_table(_ptr(t))
         return t
+
+    def cache_write(self, k_bits, v_bits, slot_mapping, k_pool, v_pool, k_scale, v_scale):
+        """Write FP16 K/V tokens ([T][Hkv][D] bit patterns) into copies of the
+        E4M3 pools ([pages][page_size][Hkv][D], contiguous) by slot; returns
+        the new (k_pool, v_pool)."""
+        k_bits = np.ascontiguousarray(k_bits, np.uint16)
+        v_bits = np.ascontiguousarray(v_bits, np.uint16)
+        slots = np.ascontiguousarray(slot_mapping, np.int64)
+        kp = np.array(k_pool, np.uint8, copy=True, order="C")
+        vp = np.array(v_pool, np.uint8, copy=True, order="C")
+        T, Hkv, D = k_bits.shape
+        P, ps = kp.shape[0], kp.shape[1]
+        rc = self.lib.orc_cache_write(_ptr(k_bits), _ptr(v_bits), T, Hkv, D, _ptr(slots),
+                                      _ptr(kp), _ptr(vp), ps * Hkv * D, Hkv * D, D, P, ps,
+                                      float(k_scale), float(v_scale))
+        if rc != 0:
+            raise ValueError("orc_cache_write: slot out of range")
+        return kp, vp
 
     def e4m3_encode(self, x) -> np.ndarray:
         x = np.ascontiguousarray(np.asarray(x, np.float64).ravel())

@@ -21,6 +21,10 @@
  *    max and sum and a final combination ([DN] first section).  Here they are
  *    FP64 and use base 2 (logits times log2(e)), the base of the LSE that the
  *    DCP merge of [NB] exchanges.
+ *  - The cache write quantises each FP16 K/V element x as E4M3(x / scale),
+ *    the quotient formed in FP32 and rounded to the nearest code (ties to
+ *    even, saturation at 448): [QSA] writes the uint8 cache with the layer's
+ *    per-tensor scales through the unchanged write path.
  *
  * Plain loops, no blocking, no reordering: a reader can check each function
  * against the definition above.  The ORC_MUTANT switch plants one known
@@ -92,6 +96,38 @@ void orc_e4m3_encode_array(const double *x, int64_t n, uint8_t *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = orc_e4m3_encode(x[i]);
+}
+
+/* Cache write: token t of k/v ([num_tokens][num_kv_heads][head_dim] FP16 bits)
+ * goes to slot slot_mapping[t] (page = slot / page_size, row = slot % page_size;
+ * negative = skip), element (g, d) to byte page*page_stride + row*token_stride
+ * + g*head_stride + d of each plane, as E4M3(fp32(x) / fp32(scale)).  Returns
+ * -1 if a slot lies past num_pages * page_size. */
+int orc_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_tokens,
+                    int32_t num_kv_heads, int32_t head_dim, const int64_t *slot_mapping,
+                    uint8_t *k_pool, uint8_t *v_pool, int64_t page_stride, int64_t token_stride,
+                    int64_t head_stride, int32_t num_pages, int32_t page_size, float k_scale,
+                    float v_scale)
+{
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slot_mapping[t];
+        if (slot < 0)
+            continue;
+        if (slot >= (int64_t)num_pages * page_size)
+            return -1;
+        int64_t page = slot / page_size, row = slot % page_size;
+        for (int32_t g = 0; g < num_kv_heads; ++g) {
+            for (int32_t d = 0; d < head_dim; ++d) {
+                int64_t src = (t * num_kv_heads + g) * head_dim + d;
+                int64_t dst = page * page_stride + row * token_stride + g * head_stride + d;
+                float xk = (float)orc_fp16_value(k[src]) / k_scale;
+                float xv = (float)orc_fp16_value(v[src]) / v_scale;
+                k_pool[dst] = orc_e4m3_encode((double)xk);
+                v_pool[dst] = orc_e4m3_encode((double)xv);
+            }
+        }
+    }
+    return 0;
 }
 
 /* binary16: 5 exponent bits (bias 15), 10 mantissa bits. */

@@ -33,6 +33,15 @@ void orc_e4m3_table(double tab[256]);
  * to 0x7F, sign kept (so -0.0 gives 0x80). */
 uint8_t orc_e4m3_encode(double x);
 void orc_e4m3_encode_array(const double *x, int64_t n, uint8_t *out);
+
+/* Cache write of FP16 K/V tokens into E4M3 pages by slot: each element x
+ * becomes E4M3(fp32(x) / fp32(scale)) (nearest code, ties to even, saturating
+ * at 448, NaN to 0x7F).  Slots < 0 are skipped; -1 if a slot is out of range. */
+int orc_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_tokens,
+                    int32_t num_kv_heads, int32_t head_dim, const int64_t *slot_mapping,
+                    uint8_t *k_pool, uint8_t *v_pool, int64_t page_stride, int64_t token_stride,
+                    int64_t head_stride, int32_t num_pages, int32_t page_size, float k_scale,
+                    float v_scale);
 /* Closed-form values of IEEE binary16 / bfloat16 bit patterns. */
 double orc_fp16_value(uint16_t bits);
 double orc_bf16_value(uint16_t bits);

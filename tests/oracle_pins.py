@@ -541,6 +541,51 @@ def pin_combine_lse(o):
         assert_close_rel(ml[live], lse[live], 1e-12, f"merged lse, cut {cut}")
 
 
+def pin_cache_write(o):
+    """The cache write puts E4M3(fp32(x) / fp32(scale)) at each slot's bytes and
+    touches nothing else: PyTorch's float8_e4m3fn cast of the same FP32 quotient
+    gives the same code below 448, saturation gives 0x7E at and above it, NaN
+    gives 0x7F, -0 gives 0x80, and ties go to the even code."""
+    rng = np.random.Generator(np.random.PCG64(0xCAC4E))
+    T, Hkv, D, P, ps = 37, 2, 16, 6, 8
+    vals = rng.standard_normal((T, Hkv, D)) * np.array([0.3, 40.0])[None, :, None]
+    vals = vals.astype(np.float16)
+    vals[0, 0, :6] = [0.0, -0.0, np.nan, np.inf, -np.inf, 60000.0]
+    vals[1, 0, :4] = [1.0625, 1.1875, -1.0625, 2 ** -10]      # ties, and a subnormal half-step
+    k_bits = vals.view(np.uint16)
+    v_bits = (-vals).view(np.uint16)
+    slots = rng.permutation(P * ps)[:T].astype(np.int64)
+    slots[[5, 11]] = -1
+    k0 = rng.integers(0, 256, (P, ps, Hkv, D), dtype=np.uint8)
+    v0 = rng.integers(0, 256, (P, ps, Hkv, D), dtype=np.uint8)
+    ks, vs = np.float32(0.5), np.float32(1.0)
+    kp, vp = o.cache_write(k_bits, v_bits, slots, k0, v0, ks, vs)
+    written = np.zeros((P, ps), bool)
+    for t, sl in enumerate(slots):
+        if sl >= 0:
+            written[sl // ps, sl % ps] = True
+    assert np.array_equal(kp[~written], k0[~written]) and np.array_equal(vp[~written], v0[~written])
+    for plane, bits, scale in ((kp, k_bits, ks), (vp, v_bits, vs)):
+        x = torch.from_numpy(bits.view(np.float16).astype(np.float32)) / float(scale)
+        ref = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        xa = x.numpy()
+        for t, sl in enumerate(slots):
+            if sl < 0:
+                continue
+            got = plane[sl // ps, sl % ps]
+            fin = np.isfinite(xa[t]) & (np.abs(xa[t]) < 448)
+            assert np.array_equal(got[fin], ref[t][fin]), f"token {t} vs torch"
+            sat = np.abs(xa[t]) >= 448
+            assert np.all(got[sat] == (0x7E | np.where(xa[t][sat] < 0, 0x80, 0))), f"token {t} sat"
+            assert np.all(got[np.isnan(xa[t])] == 0x7F), f"token {t} nan"
+    # specials of token 0 (K plane, scale 0.5) and the ties of token 1
+    k_tok = lambda t: kp[slots[t] // ps, slots[t] % ps, 0]
+    assert list(k_tok(0)[:6]) == [0x00, 0x80, 0x7F, 0x7E, 0xFE, 0x7E]
+    # x/0.5: 2.125 -> tie of 2.0 / 2.25 -> 2.0 (0x40); 2.375 -> tie of 2.25 / 2.5 -> 2.5 (0x42);
+    # -2.125 -> 0xC0; 2^-9 (exactly the smallest subnormal) -> 0x01
+    assert list(k_tok(1)[:4]) == [0x40, 0x42, 0xC0, 0x01]
+
+
 def pin_selection_order(o):
     import dataclasses
 
@@ -564,6 +609,6 @@ ALL_PINS = [
     pin_e4m3_golden, pin_e4m3_structure, pin_e4m3_vs_torch, pin_encoder_roundtrip,
     pin_encoder_vs_torch, pin_one_hot_probe, pin_closed_forms, pin_relocation,
     pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine, pin_visible_nan,
-    pin_combine_lse,
+    pin_combine_lse, pin_cache_write,
     pin_selection_order, pin_fp16_decode, pin_bf16_decode,
 ]
