@@ -320,6 +320,44 @@ class BatchBench(DenseBench):
                                              w.k_scale, self.plan, self.ws)
 
 
+def time_cache_write(torch, pa, tokens: int, reps: int = 20) -> dict:
+    """E4M3 cache write of `tokens` FP16 K/V tokens (H1, D256, pages of 3456) into
+    shuffled slots, from graph replays of GRAPH_CALLS writes."""
+    D, ps = 256, 3456
+    pages = -(-tokens // ps) + 1
+    g = torch.Generator(device="cpu").manual_seed(0xCAC4E)
+    k = torch.randn((tokens, 1, D), generator=g).to(torch.float16).to("cuda:0")
+    v = torch.randn((tokens, 1, D), generator=g).to(torch.float16).to("cuda:0")
+    slots = torch.randperm(pages * ps, generator=g)[:tokens].to(torch.int64).to("cuda:0")
+    kp = torch.zeros((pages, ps, 1, D), dtype=torch.uint8, device="cuda:0")
+    vp = torch.zeros_like(kp)
+    fn = lambda: pa.paged_attn_cache_write_e4m3(k, v, slots, kp, vp, 0.5, 2.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(GRAPH_CALLS):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * GRAPH_CALLS)
+    nbytes = tokens * D * (2 * 2 + 2 * 1)          # FP16 K, V read; E4M3 K, V written
+    del graph
+    return {"tokens": tokens, "us": round(us, 3), "bytes": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def read_ceiling(torch, pa, nbytes: int = 2 << 30, reps: int = 5):
     """Read bandwidth (GB/s) of the plain streaming-read probe over nbytes."""
     buf = torch.zeros(nbytes // 16, 4, dtype=torch.int32, device="cuda:0")
@@ -467,6 +505,12 @@ def main():
         torch.cuda.empty_cache()
         sweep.append(sweep_entry(w.name, w.kv_bytes(), plan, m, ctx=w.max_tokens))
 
+    cache_write = None
+    if not args.no_sweep:
+        log("[bench] E4M3 cache write")
+        cache_write = [time_cache_write(torch, pa, t) for t in (8, 4096, 65536)]
+        torch.cuda.empty_cache()
+
     log("[bench] streaming-read ceiling")
     ceiling = read_ceiling(torch, pa)
 
@@ -509,6 +553,7 @@ def main():
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
         "combine": combines,
+        "cache_write": cache_write,
         "cpu_baseline": cpu,
         "sweep": sweep,
         "source_hash": src_hash,

@@ -57,7 +57,8 @@ class PaWorkspace(ctypes.Structure):
 EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
-           "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3")
+           "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
+           "paged_attn_cache_write_e4m3")
 
 _LIB = None
 
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                                ctypes.POINTER(PaWorkspace), p]
     L.paged_attn_verify_batch_e4m3.restype = i32
+    L.paged_attn_cache_write_e4m3.argtypes = [p, p, i64, i32, i32, p, ctypes.POINTER(PaKvPool),
+                                              f32, f32, p]
+    L.paged_attn_cache_write_e4m3.restype = i32
     L.paged_attn_combine_fp32_lse.argtypes = [p, p, p, i32, i32, i32, f32, p, p, p, p]
     L.paged_attn_combine_fp32_lse.restype = i32
     L.qsa_sparse_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, p, i32,
@@ -269,6 +273,31 @@ def paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_sc
         _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"), ctypes.byref(p),
         ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "paged_attn_verify_batch_e4m3")
+
+
+def paged_attn_cache_write_e4m3(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale) -> None:
+    """Write FP16 K/V tokens (contiguous [num_tokens][kv_heads][head_dim]) into the
+    E4M3 pools ([pages][page_size][kv_heads][head_dim] uint8 views) by slot
+    (int64 [num_tokens]; < 0 skipped)."""
+    torch = _torch()
+    for t in (k, v):
+        if t.dtype != torch.float16 or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError("k and v must be contiguous float16 [num_tokens][kv_heads][head_dim]")
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    dev = k.device
+    T, Hkv, D = k.shape
+    if slot_mapping.dtype != torch.int64 or slot_mapping.device != dev or \
+            not slot_mapping.is_contiguous() or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be a contiguous int64 tensor of num_tokens on k's device")
+    if k_pool.shape[2] != Hkv or k_pool.shape[3] != D:
+        raise ValueError("pool heads or head_dim differ from k")
+    pool = _pool(k_pool, v_pool, dev)
+    rc = lib().paged_attn_cache_write_e4m3(k.data_ptr(), v.data_ptr(), T, Hkv, D,
+                                           slot_mapping.data_ptr(), ctypes.byref(pool),
+                                           _scale(k_scale, dev, "k_scale"),
+                                           _scale(v_scale, dev, "v_scale"), _stream(dev))
+    _check(rc, "paged_attn_cache_write_e4m3")
 
 
 def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,

@@ -482,6 +482,38 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
     return dispatch(a, plan, head_dim, true, static_cast<hipStream_t>(stream));
 }
 
+int32_t paged_attn_cache_write_e4m3(const void *k_fp16, const void *v_fp16, int64_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    const int64_t *slot_mapping, const pa_kv_pool *kv,
+                                    float k_scale, float v_scale, void *stream)
+{
+    int32_t rc;
+    if (!k_fp16 || !v_fp16 || !slot_mapping)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 8 || head_dim % 8 != 0)
+        return PA_EINVAL;
+    if (num_tokens > ((int64_t)1 << 40) / ((int64_t)num_kv_heads * head_dim))
+        return PA_EINVAL;
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || !(k_scale > 0.0f) ||
+        !(v_scale > 0.0f))
+        return PA_EINVAL;
+    if (!aligned16(k_fp16) || !aligned16(v_fp16))
+        return PA_EALIGN;
+    rc = check_device();
+    if (rc != PA_OK)
+        return rc;
+    // the verify entries only read the pool (const in pa_kv_pool); this one writes it
+    hipError_t err = pa::launch_cache_write(
+        static_cast<const uint16_t *>(k_fp16), static_cast<const uint16_t *>(v_fp16), num_tokens,
+        num_kv_heads, head_dim, slot_mapping, const_cast<uint8_t *>(kv->k_pool),
+        const_cast<uint8_t *>(kv->v_pool), kv->page_stride, kv->token_stride, kv->head_stride,
+        kv->page_size, (int64_t)kv->num_pages * kv->page_size, k_scale, v_scale,
+        static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
 int32_t paged_attn_stream_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream)
 {
     if (!buf || !sink || bytes < 0 || bytes % 16 != 0)

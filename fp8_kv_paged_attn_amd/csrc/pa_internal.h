@@ -45,6 +45,13 @@ hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse,
                               hipStream_t stream, const hipEvent_t *ev = nullptr);
 // Streaming read of bytes (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t stream);
+// FP16 K/V tokens [num_tokens][num_kv_heads][head_dim] into the E4M3 pool by
+// slot; slots < 0 or >= num_slots are skipped.  head_dim a multiple of 8.
+hipError_t launch_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_tokens,
+                              int num_kv_heads, int head_dim, const int64_t *slots, uint8_t *kp,
+                              uint8_t *vp, int64_t page_stride, int64_t token_stride,
+                              int64_t head_stride, int page_size, int64_t num_slots,
+                              float k_scale, float v_scale, hipStream_t stream);
 // Any of out (FP16), out32 (FP32) and lse (base-2 LSE per row) may be null.
 hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
                           int num_rows, int head_dim, float out_scale, uint16_t *out,

@@ -253,6 +253,26 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream);
 
+/* E4M3 cache write ([QSA]: the uint8 cache is written with the layer's
+ * per-tensor scales through the write path): FP16 K/V tokens into the pool's
+ * pages by slot.  This entry writes the bytes of kv->k_pool and kv->v_pool.
+ *   k_fp16, v_fp16 [num_tokens][num_kv_heads][head_dim] FP16, contiguous,
+ *                16-byte aligned; head_dim a multiple of 8 (<= the pool's
+ *                head_stride in practice; the layout is the caller's)
+ *   slot_mapping [num_tokens] int64: token t goes to page slot / page_size,
+ *                row slot % page_size; slots < 0 or >= num_pages*page_size are
+ *                skipped (nothing is written for them)
+ *   kv           (host) the pool layout, as for the verify entries
+ *   k_scale, v_scale (host) finite and > 0 (PA_EINVAL otherwise)
+ * Each element x becomes E4M3(fp32(x) / scale), the quotient rounded once in
+ * FP32: the nearest code, ties to even, saturating at +-448 (also for +-inf),
+ * NaN to 0x7F, -0 to 0x80.  Tokens with equal slots race (last writer wins in
+ * no defined order). */
+int32_t paged_attn_cache_write_e4m3(const void *k_fp16, const void *v_fp16, int64_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    const int64_t *slot_mapping, const pa_kv_pool *kv,
+                                    float k_scale, float v_scale, void *stream);
+
 /* Kernel timer, for measurement harnesses; no result depends on it.
  *
  * paged_attn_timer_arm(n), 0 <= n <= PA_TIMER_MAX_LAUNCHES: the next n verify

@@ -227,6 +227,37 @@ def test_verify_batch_without_device_reports_edevice(L):
                                           None) == PA_EDEVICE
 
 
+def test_cache_write_rejects_bad_arguments(L):
+    pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 16, token_stride=256,
+                       head_stride=256, num_pages=8, page_size=16)
+    A = ctypes.c_void_p(0x60000)
+    f = L.paged_attn_cache_write_e4m3
+
+    def call(k=A, v=A, T=4, Hkv=1, D=256, slots=A, ks=0.5, vs=2.0, kv=pool):
+        return f(k, v, T, Hkv, D, slots, ctypes.byref(kv), ks, vs, None)
+
+    assert call(k=None) == PA_EINVAL
+    assert call(slots=None) == PA_EINVAL
+    assert call(T=-1) == PA_EINVAL
+    assert call(Hkv=0) == PA_EINVAL
+    assert call(D=12) == PA_EINVAL
+    assert call(ks=0.0) == PA_EINVAL
+    assert call(vs=float("nan")) == PA_EINVAL
+    assert call(k=ctypes.c_void_p(0x60008)) == PA_EALIGN
+    bad = pa.PaKvPool(k_pool=0x10008, v_pool=0x20000, page_stride=256 * 16, token_stride=256,
+                      head_stride=256, num_pages=8, page_size=16)
+    assert call(kv=bad) == PA_EALIGN
+
+
+@no_device
+def test_cache_write_without_device_reports_edevice(L):
+    pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 16, token_stride=256,
+                       head_stride=256, num_pages=8, page_size=16)
+    A = ctypes.c_void_p(0x60000)
+    assert L.paged_attn_cache_write_e4m3(A, A, 4, 1, 256, A, ctypes.byref(pool), 0.5, 2.0,
+                                         None) == PA_EDEVICE
+
+
 def test_combine_lse_rejects_bad_arguments(L):
     A = ctypes.c_void_p(0x10000)
     f = L.paged_attn_combine_fp32_lse

@@ -506,3 +506,78 @@ def test_batch_config(orc):
     announce("batch config", w.name)
     got = gu.run_batch(w, "mfma")
     gu.assert_parity(got, gu.oracle_batch(orc, w, nthreads=16), "batch config")
+
+
+# ---------------------------------------------------------------------------
+# E4M3 cache write
+# ---------------------------------------------------------------------------
+
+def _write_and_compare(orc, k_bits, v_bits, slots, k0, v0, ks, vs, view=None):
+    """GPU write into (a view of) device copies of k0/v0; returns host pools."""
+    kd = torch.from_numpy(k0).to(gu.DEV)
+    vd = torch.from_numpy(v0).to(gu.DEV)
+    kv_k, kv_v = (kd, vd) if view is None else (view(kd), view(vd))
+    pa.paged_attn_cache_write_e4m3(gu.fp16_tensor(k_bits).to(gu.DEV),
+                                   gu.fp16_tensor(v_bits).to(gu.DEV),
+                                   torch.from_numpy(slots).to(gu.DEV), kv_k, kv_v, ks, vs)
+    torch.cuda.synchronize()
+    return kd.cpu().numpy(), vd.cpu().numpy()
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 2.25])
+def test_cache_write_every_fp16_value(orc, scale):
+    """Every FP16 bit pattern, written with k_scale = scale (and v_scale =
+    1/scale), gives the oracle encoder's byte for the FP32 quotient, bit for bit."""
+    announce("cache write all fp16", scale)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 1, 16)
+    T, P, ps = 4096, 256, 16                 # 16-byte token rows: the pool's stride rule
+    slots = np.arange(T, dtype=np.int64)
+    k0 = np.zeros((P, ps, 1, 16), np.uint8)
+    v0 = np.zeros((P, ps, 1, 16), np.uint8)
+    ks, vs = np.float32(scale), np.float32(1.0 / scale)
+    gk, gv = _write_and_compare(orc, bits, bits, slots, k0, v0, ks, vs)
+    rk, rv = orc.cache_write(bits, bits, slots, k0, v0, ks, vs)
+    assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+
+
+def test_cache_write_slots_and_specials(orc):
+    """Random tokens with specials into shuffled slots of a pool with random
+    bytes: skipped (-1) and out-of-range slots write nothing, everything else is
+    bit-exact with the oracle."""
+    rng = np.random.Generator(np.random.PCG64(0xCA11))
+    T, Hkv, D, P, ps = 300, 2, 128, 24, 16
+    vals = (rng.standard_normal((T, Hkv, D)) * 30.0).astype(np.float16)
+    vals[0, 0, :8] = [0.0, -0.0, np.nan, np.inf, -np.inf, 60000.0, 2 ** -16, -448.0]
+    slots = rng.permutation(P * ps)[:T].astype(np.int64)
+    slots[[3, 77, 150]] = -1
+    slots[[4, 200]] = P * ps + 5                      # past the pool: skipped on the device
+    k0 = rng.integers(0, 256, (P, ps, Hkv, D), dtype=np.uint8)
+    v0 = rng.integers(0, 256, (P, ps, Hkv, D), dtype=np.uint8)
+    announce("cache write slots")
+    gk, gv = _write_and_compare(orc, vals.view(np.uint16), (-vals).view(np.uint16), slots,
+                                k0, v0, np.float32(0.45), np.float32(1.6))
+    ok_slots = np.where(slots >= P * ps, -1, slots)
+    rk, rv = orc.cache_write(vals.view(np.uint16), (-vals).view(np.uint16), ok_slots, k0, v0,
+                             np.float32(0.45), np.float32(1.6))
+    assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+
+
+def test_cache_write_strided_view(orc):
+    """A packed allocation (K of one pool interleaved with other data): only the
+    view's bytes change, and they match the oracle on the view."""
+    rng = np.random.Generator(np.random.PCG64(0xCA12))
+    T, Hkv, D, P, ps = 40, 1, 256, 6, 8
+    vals = (rng.standard_normal((T, Hkv, D)) * 4.0).astype(np.float16)
+    slots = rng.permutation(P * ps)[:T].astype(np.int64)
+    big_k = rng.integers(0, 256, (P, ps, 2, Hkv, D), dtype=np.uint8)   # [.., plane, ..]
+    big_v = rng.integers(0, 256, (P, ps, 2, Hkv, D), dtype=np.uint8)
+    announce("cache write strided view")
+    gk, gv = _write_and_compare(orc, vals.view(np.uint16), vals.view(np.uint16), slots, big_k,
+                                big_v, np.float32(0.5), np.float32(0.5),
+                                view=lambda t: t[:, :, 1])
+    rk, rv = orc.cache_write(vals.view(np.uint16), vals.view(np.uint16), slots,
+                             np.ascontiguousarray(big_k[:, :, 1]),
+                             np.ascontiguousarray(big_v[:, :, 1]), np.float32(0.5),
+                             np.float32(0.5))
+    assert np.array_equal(gk[:, :, 1], rk) and np.array_equal(gv[:, :, 1], rv)
+    assert np.array_equal(gk[:, :, 0], big_k[:, :, 0]) and np.array_equal(gv[:, :, 0], big_v[:, :, 0])
