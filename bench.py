@@ -46,7 +46,7 @@ METRIC = "µs/call and KV-read GB/s (% HBM peak), q8 H6/Hkv1/D256 E4M3, 8K–256
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MALL_BYTES = 256 << 20         # Infinity Cache
 PMC_FILE = os.path.join(ROOT, "profiles", "verify_kernel_pmc.json")
-KERNEL_SOURCES = ("verify_mfma.hip", "pa_internal.h")
+KERNEL_SOURCES = ("verify_mfma.hip", "pa_verify.h")
 
 
 def log(*a):

@@ -7,8 +7,8 @@
 // code, ties to even, saturating at +-448, NaN to 0x7F, -0 to 0x80.  Token t
 // goes to page slot / page_size, row slot % page_size of both planes.
 //
-// One thread per 8 elements: a 16-byte FP16 load and an 8-byte store per
-// plane.  The encoder is exact: the quotient is scaled by a power of two so
+// One thread per 16 elements of a token: two 16-byte FP16 loads and one
+// 16-byte store per plane.  The encoder is exact: the quotient is scaled by a power of two so
 // that the code's step is 1, then rounded half to even (v_rndne).
 #include "pa_internal.h"
 
@@ -44,13 +44,13 @@ __device__ __forceinline__ uint32_t e4m3_code(float x)
     return sign | code;
 }
 
-// 8 FP16 values (16 bytes) -> 8 E4M3 codes (8 bytes), each divided by scale.
-__device__ __forceinline__ uint2 encode8(uint4 in, float scale)
+// 16 FP16 values (32 bytes) -> 16 E4M3 codes (16 bytes), each divided by scale.
+__device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale)
 {
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    uint32_t out[2] = {0u, 0u};
+    const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint16_t bits = (uint16_t)(w[j] >> (16 * h));
@@ -59,33 +59,42 @@ __device__ __forceinline__ uint2 encode8(uint4 in, float scale)
             out[j >> 1] |= c << (8 * (2 * (j & 1) + h));
         }
     }
-    return make_uint2(out[0], out[1]);
+    return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// Thread layout: a token's chunks (num_kv_heads x head_dim/16 of them) are
+// consecutive threads; a workgroup covers 256 / chunks tokens per iteration
+// (chunks <= 256), and loops over chunks itself when a token has more.
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t num_tokens,
     int num_kv_heads, int head_dim, const int64_t *__restrict__ slots, uint8_t *__restrict__ kp,
     uint8_t *__restrict__ vp, int64_t page_stride, int64_t token_stride, int64_t head_stride,
     int page_size, int64_t num_slots, float k_scale, float v_scale)
 {
-    const int chunks = head_dim / 8;
-    const int64_t per_token = (int64_t)num_kv_heads * chunks;
-    const int64_t total = num_tokens * per_token;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * kThreads) {
-        const int64_t t = i / per_token;
-        const int rem = (int)(i - t * per_token);
-        const int g = rem / chunks, c = rem - g * chunks;
+    const int per_head = head_dim / 16;
+    const int chunks = num_kv_heads * per_head;          // 16-element chunks per token
+    const int tpw = chunks <= kThreads ? kThreads / chunks : 1;   // tokens per iteration
+    const int tt = chunks <= kThreads ? (int)threadIdx.x / chunks : 0;
+    const int c0 = chunks <= kThreads ? (int)threadIdx.x - tt * chunks : (int)threadIdx.x;
+    const int cstep = chunks <= kThreads ? chunks : kThreads;
+    if (tt >= tpw)
+        return;
+    for (int64_t t = (int64_t)blockIdx.x * tpw + tt; t < num_tokens; t += (int64_t)gridDim.x * tpw) {
         const int64_t slot = slots[t];
         if (slot < 0 || slot >= num_slots)
             continue;
         const int64_t page = slot / page_size, row = slot - page * page_size;
-        const int64_t src = ((t * num_kv_heads + g) * head_dim) + 8 * c;
-        const int64_t dst = page * page_stride + row * token_stride + g * head_stride + 8 * c;
-        const uint4 kin = *(const uint4 *)(k + src);
-        const uint4 vin = *(const uint4 *)(v + src);
-        *(uint2 *)(kp + dst) = encode8(kin, k_scale);
-        *(uint2 *)(vp + dst) = encode8(vin, v_scale);
+        const int64_t base = page * page_stride + row * token_stride;
+        for (int c = c0; c < chunks; c += cstep) {
+            const int g = c / per_head, e = 16 * (c - g * per_head);
+            const int64_t src = (t * num_kv_heads + g) * head_dim + e;
+            const uint4 *ks = (const uint4 *)(k + src);
+            const uint4 *vs = (const uint4 *)(v + src);
+            const uint4 k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
+            const int64_t dst = base + g * head_stride + e;
+            *(uint4 *)(kp + dst) = encode16(k0, k1, k_scale);
+            *(uint4 *)(vp + dst) = encode16(v0, v1, v_scale);
+        }
     }
 }
 
@@ -97,10 +106,11 @@ hipError_t launch_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_
                               int64_t head_stride, int page_size, int64_t num_slots,
                               float k_scale, float v_scale, hipStream_t stream)
 {
-    const int64_t total = num_tokens * num_kv_heads * (head_dim / 8);
-    if (total == 0)
+    if (num_tokens == 0)
         return hipSuccess;
-    int64_t blocks = (total + kThreads - 1) / kThreads;
+    const int chunks = num_kv_heads * (head_dim / 16);
+    const int64_t tpw = chunks <= kThreads ? kThreads / chunks : 1;
+    int64_t blocks = (num_tokens + tpw - 1) / tpw;
     if (blocks > kMaxBlocks)
         blocks = kMaxBlocks;
     hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, k, v,

@@ -492,7 +492,7 @@ int32_t paged_attn_cache_write_e4m3(const void *k_fp16, const void *v_fp16, int6
         return PA_EINVAL;
     if ((rc = check_pool(kv)) != PA_OK)
         return rc;
-    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 8 || head_dim % 8 != 0)
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 16 || head_dim % 16 != 0)
         return PA_EINVAL;
     if (num_tokens > ((int64_t)1 << 40) / ((int64_t)num_kv_heads * head_dim))
         return PA_EINVAL;

@@ -1,52 +1,15 @@
-// pa_internal.h - shared declarations of the gfx950 verify-attention kernels.
-// Internal to libpaged_attn_e4m3; the public interface is include/paged_attn_e4m3.h.
+// pa_internal.h - declarations shared by the sources of libpaged_attn_e4m3.
+// Internal; the public interface is include/paged_attn_e4m3.h.
 #pragma once
 
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "pa_verify.h"
 
 namespace pa {
 
-// Everything a verify kernel needs, resolved on the host.  One struct serves
-// the dense path (one request, token = list position) and the sparse path
-// (list position -> selected block -> token).
-struct VerifyArgs {
-    const uint16_t *q;          // fp16 (dense) or bf16 (sparse) bits [B][q_rows][H][D]
-    const uint8_t *k_pool;
-    const uint8_t *v_pool;
-    int64_t page_stride;
-    int64_t token_stride;
-    int64_t head_stride;
-    int32_t page_size;
-    const int32_t *block_table; // dense: [entries]; sparse: [B][max_blocks]
-    int32_t table_stride;       // sparse: max_blocks (entries per request); dense: 0
-    const int32_t *sel;         // sparse: [B][Hkv][topk]; dense: nullptr
-    int32_t topk;
-    const int32_t *row_lens;    // [B][q_rows]
-    int32_t len_cap;            // lengths are clamped to [0, len_cap]
-    int32_t list_len;           // positions per KV unit (dense: max_tokens; sparse: topk*page)
-    int32_t batch, q_rows, num_heads, num_kv_heads, group;  // group = H / Hkv
-    int32_t rows;               // rows per KV unit = q_rows * group
-    int32_t num_splits, tokens_per_split;
-    int32_t total_rows;         // rows of the workspace = B * q_rows * H
-    float logit_scale;          // sm_scale * k_scale * log2(e)
-    float *ws_acc, *ws_max, *ws_sum;
-};
-
-enum class Variant : int { kSimple = 0, kMfma = 1 };
-
-// Launchers return hipSuccess or the launch error.  Grid = (num_splits, units).
-// `ev`, when not null, is a (begin, end) pair of HIP events bound to the
-// kernel's own dispatch (hipExtLaunchKernel), for the kernel timer.
-hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
-                                hipStream_t stream, const hipEvent_t *ev = nullptr);
-hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse,
-                              hipStream_t stream, const hipEvent_t *ev = nullptr);
 // Streaming read of bytes (a multiple of 16) from a 16-byte aligned buffer.
 hipError_t launch_stream_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t stream);
 // FP16 K/V tokens [num_tokens][num_kv_heads][head_dim] into the E4M3 pool by
-// slot; slots < 0 or >= num_slots are skipped.  head_dim a multiple of 8.
+// slot; slots < 0 or >= num_slots are skipped.  head_dim a multiple of 16.
 hipError_t launch_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_tokens,
                               int num_kv_heads, int head_dim, const int64_t *slots, uint8_t *kp,
                               uint8_t *vp, int64_t page_stride, int64_t token_stride,

@@ -36,7 +36,7 @@
 //  * Tokens a row must not see get score -inf by select, and V bytes of
 //    positions no row sees are zeroed by select before P.V, so NaN bytes in
 //    padding pages cannot leak (null-block fix of 1Cat-vLLM PR #702).
-#include "pa_internal.h"
+#include "pa_verify.h"
 
 #include <math.h>
 #include <stdint.h>

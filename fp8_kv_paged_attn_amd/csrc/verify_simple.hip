@@ -7,7 +7,7 @@
 // computation (design note "DFlash2 E4M3 attention with FP32 state", first
 // section: FP32 unnormalised partition numerators, separate FP32 max/sum),
 // kept as the A/B baseline of the MFMA kernel and for shapes it does not take.
-#include "pa_internal.h"
+#include "pa_verify.h"
 
 #include <math.h>
 

@@ -257,8 +257,8 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
  * per-tensor scales through the write path): FP16 K/V tokens into the pool's
  * pages by slot.  This entry writes the bytes of kv->k_pool and kv->v_pool.
  *   k_fp16, v_fp16 [num_tokens][num_kv_heads][head_dim] FP16, contiguous,
- *                16-byte aligned; head_dim a multiple of 8 (<= the pool's
- *                head_stride in practice; the layout is the caller's)
+ *                16-byte aligned; head_dim a multiple of 16 (the pool's
+ *                layout must hold head_dim bytes per head; it is the caller's)
  *   slot_mapping [num_tokens] int64: token t goes to page slot / page_size,
  *                row slot % page_size; slots < 0 or >= num_pages*page_size are
  *                skipped (nothing is written for them)

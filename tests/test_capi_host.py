@@ -241,6 +241,7 @@ def test_cache_write_rejects_bad_arguments(L):
     assert call(T=-1) == PA_EINVAL
     assert call(Hkv=0) == PA_EINVAL
     assert call(D=12) == PA_EINVAL
+    assert call(D=24) == PA_EINVAL
     assert call(ks=0.0) == PA_EINVAL
     assert call(vs=float("nan")) == PA_EINVAL
     assert call(k=ctypes.c_void_p(0x60008)) == PA_EALIGN
