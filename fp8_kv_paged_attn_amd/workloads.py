@@ -393,6 +393,15 @@ def make_dense_batch(name: str, seed: int, *, ctxs: List[int], q_rows: int, num_
         num_splits=num_splits)
 
 
+def config_c4_tokens() -> QsaTokensWorkload:
+    """The QSA batch of c4 with a token-id selection: 2048 ids per (request, KV
+    head), the newest 4 tokens always included, 32 of them -1."""
+    return make_qsa_tokens("c4tok_qsa_b16_q4_h24_kv2_d128_r2048", BASE_SEED + 6, batch=16,
+                           q_rows=4, num_heads=24, num_kv_heads=2, head_dim=128, ctx=32768,
+                           page_size=64, num_sel=2048, num_empty=32, k_scale=0.5,
+                           v_scale=2.0)
+
+
 def config_batch() -> DenseBatchWorkload:
     """Independent-request batch: 8 requests, q16 rows, H6/Hkv1/D256, E4M3 pages of
     3296 tokens, contexts 4K..32K (mixed lengths), k 0.37, v 1.9."""
@@ -464,6 +473,85 @@ def make_qsa(name: str, seed: int, *, batch: int, q_rows: int, num_heads: int,
         head_dim=head_dim, page_size=page_size, max_blocks=nblk, topk=topk,
         sm_scale=float(np.float32(sm_scale)), k_scale=float(np.float32(k_scale)),
         v_scale=float(np.float32(v_scale)), num_splits=num_splits)
+
+
+@dataclasses.dataclass
+class QsaTokensWorkload:
+    """A batch of sparse verify requests over selected token ids (-1 = empty)."""
+
+    name: str
+    q_bits: np.ndarray         # uint16 bf16 bits, [batch][q_rows][num_heads][head_dim]
+    k_pool: np.ndarray         # uint8, [num_pages][page_size][num_kv_heads][head_dim]
+    v_pool: np.ndarray
+    block_table: np.ndarray    # int32 [batch][max_blocks]
+    sel_tokens: np.ndarray     # int32 [batch][num_kv_heads][num_sel], -1 = empty
+    row_lens: np.ndarray       # int32 [batch][q_rows]
+    batch: int
+    q_rows: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    max_blocks: int
+    num_sel: int
+    sm_scale: float
+    k_scale: float
+    v_scale: float
+    num_splits: int = 0
+
+    @property
+    def num_rows(self) -> int:
+        return self.batch * self.q_rows * self.num_heads
+
+    def kv_bytes(self) -> int:
+        """Algorithmic bytes: selected token ids x D x 2 per (request, KV head)."""
+        return int((self.sel_tokens >= 0).sum()) * self.head_dim * 2
+
+
+def tokens_from_blocks(w: QsaWorkload) -> np.ndarray:
+    """The token-id form of a block selection: block s becomes ids s*page ..
+    s*page + page - 1 in list order; an empty block slot becomes page -1s."""
+    ps = w.page_size
+    out = np.full((w.batch, w.num_kv_heads, w.topk * ps), -1, np.int32)
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            for j, blk in enumerate(w.sel_blocks[b, g]):
+                if blk >= 0:
+                    out[b, g, j * ps:(j + 1) * ps] = np.arange(blk * ps, (blk + 1) * ps)
+    return out
+
+
+def make_qsa_tokens(name: str, seed: int, *, batch: int, q_rows: int, num_heads: int,
+                    num_kv_heads: int, head_dim: int, ctx: int, page_size: int, num_sel: int,
+                    k_scale: float, v_scale: float, num_empty: int = 0, sigma: float = 1.0,
+                    num_splits: int = 0,
+                    row_lens: Optional[np.ndarray] = None) -> QsaTokensWorkload:
+    """Build a seeded token-id selection batch.  Every block of every request
+    holds data (a block selection of all blocks, unpoisoned); each (request, KV
+    head) selects the newest q_rows tokens plus num_sel - q_rows - num_empty
+    distinct older ones, with num_empty -1 entries, in a shuffled order."""
+    nblk = -(-ctx // page_size)
+    base = make_qsa(name, seed, batch=batch, q_rows=q_rows, num_heads=num_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, ctx=ctx, page_size=page_size,
+                    topk=nblk, k_scale=k_scale, v_scale=v_scale, sigma=sigma,
+                    poison_unselected=False, row_lens=row_lens)
+    ss = substream_seed(seed, "tokens")
+    n_old = num_sel - q_rows - num_empty
+    assert 0 <= n_old <= ctx - q_rows
+    sel = np.empty((batch, num_kv_heads, num_sel), np.int32)
+    for b in range(batch):
+        for g in range(num_kv_heads):
+            sub = substream_seed(ss, f"{b}/{g}")
+            old = permutation(sub, ctx - q_rows)[:n_old]
+            new = np.arange(ctx - q_rows, ctx)
+            chosen = np.concatenate([old, new, np.full(num_empty, -1)])
+            sel[b, g] = chosen[permutation(substream_seed(sub, "order"), num_sel)]
+    return QsaTokensWorkload(
+        name=name, q_bits=base.q_bits, k_pool=base.k_pool, v_pool=base.v_pool,
+        block_table=base.block_table, sel_tokens=sel, row_lens=base.row_lens, batch=batch,
+        q_rows=q_rows, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        page_size=page_size, max_blocks=nblk, num_sel=num_sel, sm_scale=base.sm_scale,
+        k_scale=base.k_scale, v_scale=base.v_scale, num_splits=num_splits)
 
 
 # ---------------------------------------------------------------------------
@@ -542,4 +630,5 @@ CONFIGS: Dict[str, object] = {
     "c3": config_c3,
     "c4": config_c4,
     "batch": config_batch,
+    "c4tok": config_c4_tokens,
 }

@@ -61,6 +61,12 @@ class Oracle:
         lib.orc_qsa_split.argtypes = pool + [_p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                              _i32, _f64, _f64, _i32, _i32, _i32, _p, _p, _p]
         lib.orc_qsa_split.restype = ctypes.c_int
+        lib.orc_qsa_tokens_verify.argtypes = pool + [_p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                              _i32, _f64, _f64, _f64, _i32, _p]
+        lib.orc_qsa_tokens_verify.restype = ctypes.c_int
+        lib.orc_qsa_tokens_split.argtypes = pool + [_p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                             _i32, _f64, _f64, _i32, _i32, _i32, _p, _p, _p]
+        lib.orc_qsa_tokens_split.restype = ctypes.c_int
         lib.orc_combine.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f64, _p]
         lib.orc_combine.restype = ctypes.c_int
         lib.orc_combine_f32.argtypes = [_p, _p, _p, _i32, _i32, _i32, _f64, _p]
@@ -199,6 +205,45 @@ class Oracle:
             raise ValueError(f"orc_qsa_split precondition failed ({rc})")
         return acc, mx, sm
 
+    def qsa_tokens_verify(self, q_bits, k_pool, v_pool, block_table, sel_tokens, row_lens,
+                          sm_scale, k_scale, v_scale, nthreads=1, strides=None) -> np.ndarray:
+        q_bits = np.ascontiguousarray(q_bits, np.uint16)
+        bt = np.ascontiguousarray(block_table, np.int32)
+        sel = np.ascontiguousarray(sel_tokens, np.int32)
+        rl = np.ascontiguousarray(row_lens, np.int32)
+        B, qr, H, D = q_bits.shape
+        Hkv, topk = sel.shape[1], sel.shape[2]
+        out = np.empty((B, qr, H, D), np.float64)
+        rc = self.lib.orc_qsa_tokens_verify(
+            _ptr(q_bits), *self._pool_args(k_pool, v_pool, strides), _ptr(bt), bt.shape[1],
+            _ptr(sel), topk, _ptr(rl), B, qr, H, Hkv, D, float(sm_scale), float(k_scale),
+            float(v_scale), int(nthreads), _ptr(out))
+        if rc != 0:
+            raise ValueError(f"orc_qsa_tokens_verify precondition failed ({rc})")
+        return out
+
+    def qsa_tokens_split(self, q_bits, k_pool, v_pool, block_table, sel_tokens, row_lens,
+                         sm_scale, k_scale, num_splits, tokens_per_split, nthreads=1,
+                         strides=None):
+        q_bits = np.ascontiguousarray(q_bits, np.uint16)
+        bt = np.ascontiguousarray(block_table, np.int32)
+        sel = np.ascontiguousarray(sel_tokens, np.int32)
+        rl = np.ascontiguousarray(row_lens, np.int32)
+        B, qr, H, D = q_bits.shape
+        Hkv, topk = sel.shape[1], sel.shape[2]
+        R = B * qr * H
+        acc = np.empty((num_splits, R, D), np.float64)
+        mx = np.empty((num_splits, R), np.float64)
+        sm = np.empty((num_splits, R), np.float64)
+        rc = self.lib.orc_qsa_tokens_split(
+            _ptr(q_bits), *self._pool_args(k_pool, v_pool, strides), _ptr(bt), bt.shape[1],
+            _ptr(sel), topk, _ptr(rl), B, qr, H, Hkv, D, float(sm_scale), float(k_scale),
+            int(num_splits), int(tokens_per_split), int(nthreads), _ptr(acc), _ptr(mx),
+            _ptr(sm))
+        if rc != 0:
+            raise ValueError(f"orc_qsa_tokens_split precondition failed ({rc})")
+        return acc, mx, sm
+
     def combine(self, acc, mx, sm, v_scale, with_lse: bool = False):
         """Merge split partials (FP64 or FP32 arrays) into FP64 rows; with
         with_lse, also the base-2 LSE of each row: returns (out, lse)."""
@@ -230,6 +275,11 @@ class Oracle:
         return self.qsa_verify(w.q_bits, w.k_pool, w.v_pool, w.block_table, w.sel_blocks,
                                w.row_lens, w.sm_scale, w.k_scale, w.v_scale,
                                nthreads=nthreads)
+
+    def qsa_tokens_workload(self, w, nthreads=1) -> np.ndarray:
+        return self.qsa_tokens_verify(w.q_bits, w.k_pool, w.v_pool, w.block_table,
+                                      w.sel_tokens, w.row_lens, w.sm_scale, w.k_scale,
+                                      w.v_scale, nthreads=nthreads)
 
 
 _DEFAULT: Optional[Oracle] = None

@@ -248,7 +248,8 @@ static void split_row(const pool_t *pl, const double *tab, const double *qv,
 /* ------------------------------------------------------------------ */
 
 typedef struct {
-    int sparse;                 /* 0: dense one request, 1: QSA batch */
+    int sparse;                 /* 0: dense one request, 1: QSA batch over selected
+                                   blocks, 2: QSA batch over selected token ids */
     const uint16_t *q;
     pool_t pool;
     const int32_t *block_table;
@@ -310,6 +311,29 @@ static int64_t token_list(const problem_t *pb, int b, int i, int g, int64_t *off
             pos[n] = t;
             ++n;
         }
+    } else if (pb->sparse == 2) {
+        /* list entry j is a logical token id (-1: empty); the row sees it when
+         * id < its length; the entry's block is located through the table */
+        int64_t cap = (int64_t)pb->num_entries * pl->page_size;
+        L = pb->row_lens[(int64_t)b * pb->q_rows + i];
+        if (L < 0)
+            L = 0;
+        if (L > cap)
+            L = cap;
+        for (int j = 0; j < pb->topk; ++j) {
+            int64_t t = pb->sel[((int64_t)b * pb->num_kv_heads + g) * pb->topk + j];
+            int64_t lp, u, phys;
+            if (t < 0 || (ORC_MUTANT == 15 ? t > L : t >= L))
+                continue;
+            lp = t / pl->page_size;
+            u = t % pl->page_size;
+            phys = pb->block_table[(ORC_MUTANT == 16 ? 0 : (int64_t)b * pb->num_entries) + lp];
+            if (phys < 0 || phys >= pl->num_pages)
+                return -1;
+            off[n] = kv_offset(pl, phys, u, g);
+            pos[n] = j;
+            ++n;
+        }
     } else {
         int64_t cap = (int64_t)pb->num_entries * pl->page_size;
         L = pb->row_lens[(int64_t)b * pb->q_rows + i];
@@ -348,7 +372,8 @@ static void *worker(void *arg)
     problem_t *pb = (problem_t *)arg;
     const pool_t *pl = &pb->pool;
     int D = pl->head_dim, H = pb->num_heads;
-    int64_t cap = pb->sparse ? (int64_t)pb->topk * pl->page_size : pb->max_tokens;
+    int64_t cap = pb->sparse == 2 ? (int64_t)pb->topk
+                  : pb->sparse ? (int64_t)pb->topk * pl->page_size : pb->max_tokens;
     int num_rows = pb->batch * pb->q_rows * H;
     double tab[256], *qv, *s;
     int64_t *off, *pos;
@@ -550,6 +575,67 @@ int orc_qsa_split(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_poo
     pb.num_entries = max_blocks;
     pb.sel = sel;
     pb.topk = topk;
+    pb.row_lens = row_lens;
+    pb.batch = batch;
+    pb.q_rows = q_rows;
+    pb.num_heads = num_heads;
+    pb.num_kv_heads = num_kv_heads;
+    pb.sm_scale = sm_scale;
+    pb.k_scale = k_scale;
+    pb.split = 1;
+    pb.num_splits = num_splits;
+    pb.tokens_per_split = tokens_per_split;
+    pb.nthreads = nthreads;
+    pb.ws_acc = ws_acc;
+    pb.ws_max = ws_max;
+    pb.ws_sum = ws_sum;
+    return run(&pb);
+}
+
+int orc_qsa_tokens_verify(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                          int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                          int32_t num_pages, int32_t page_size,
+                          const int32_t *block_table, int32_t max_blocks,
+                          const int32_t *sel_tokens, int32_t num_sel, const int32_t *row_lens,
+                          int32_t batch, int32_t q_rows, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, double sm_scale,
+                          double k_scale, double v_scale, int32_t nthreads, double *out)
+{
+    problem_t pb = base_problem(2, q, k_pool, v_pool, page_stride, token_stride, head_stride,
+                                num_pages, page_size, head_dim);
+    pb.block_table = block_table;
+    pb.num_entries = max_blocks;
+    pb.sel = sel_tokens;
+    pb.topk = num_sel;
+    pb.row_lens = row_lens;
+    pb.batch = batch;
+    pb.q_rows = q_rows;
+    pb.num_heads = num_heads;
+    pb.num_kv_heads = num_kv_heads;
+    pb.sm_scale = sm_scale;
+    pb.k_scale = k_scale;
+    pb.v_scale = v_scale;
+    pb.nthreads = nthreads;
+    pb.out = out;
+    return run(&pb);
+}
+
+int orc_qsa_tokens_split(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                         int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                         int32_t num_pages, int32_t page_size,
+                         const int32_t *block_table, int32_t max_blocks,
+                         const int32_t *sel_tokens, int32_t num_sel, const int32_t *row_lens,
+                         int32_t batch, int32_t q_rows, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, double sm_scale,
+                         double k_scale, int32_t num_splits, int32_t tokens_per_split,
+                         int32_t nthreads, double *ws_acc, double *ws_max, double *ws_sum)
+{
+    problem_t pb = base_problem(2, q, k_pool, v_pool, page_stride, token_stride, head_stride,
+                                num_pages, page_size, head_dim);
+    pb.block_table = block_table;
+    pb.num_entries = max_blocks;
+    pb.sel = sel_tokens;
+    pb.topk = num_sel;
     pb.row_lens = row_lens;
     pb.batch = batch;
     pb.q_rows = q_rows;

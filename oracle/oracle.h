@@ -133,6 +133,32 @@ int orc_qsa_split(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_poo
                   int32_t num_splits, int32_t tokens_per_split, int32_t nthreads,
                   double *ws_acc, double *ws_max, double *ws_sum);
 
+/* Sparse verify over selected token ids (the token-id selection with -1
+ * padding that 1Cat-vLLM PR "Qualify calibrated E4M3 and disk PLE with QSA
+ * DCP2" keeps): sel_tokens [batch][num_kv_heads][num_sel] logical token ids,
+ * -1 = empty.  Entry j with id t >= 0 is token t of request b: block t /
+ * page_size through block_table, row t % page_size.  Row i keeps the entries
+ * with t < clamp(len, 0, max_blocks*page_size), so each row gets its own mask
+ * in any block.  Other arguments as for orc_qsa_verify; the split form splits
+ * by list entry: split s covers entries [s*T, (s+1)*T). */
+int orc_qsa_tokens_verify(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                          int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                          int32_t num_pages, int32_t page_size,
+                          const int32_t *block_table, int32_t max_blocks,
+                          const int32_t *sel_tokens, int32_t num_sel, const int32_t *row_lens,
+                          int32_t batch, int32_t q_rows, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, double sm_scale,
+                          double k_scale, double v_scale, int32_t nthreads, double *out);
+int orc_qsa_tokens_split(const uint16_t *q, const uint8_t *k_pool, const uint8_t *v_pool,
+                         int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                         int32_t num_pages, int32_t page_size,
+                         const int32_t *block_table, int32_t max_blocks,
+                         const int32_t *sel_tokens, int32_t num_sel, const int32_t *row_lens,
+                         int32_t batch, int32_t q_rows, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, double sm_scale,
+                         double k_scale, int32_t num_splits, int32_t tokens_per_split,
+                         int32_t nthreads, double *ws_acc, double *ws_max, double *ws_sum);
+
 #ifdef __cplusplus
 }
 #endif

@@ -117,6 +117,29 @@ def qsa_reference(w) -> np.ndarray:
     return out * w.v_scale
 
 
+def qsa_tokens_reference(w) -> np.ndarray:
+    """Library reference for a QsaTokensWorkload: per (b, g) gather the selected
+    token ids (a multiset, -1 skipped) through the block table, decode with
+    PyTorch, mask id >= len per row, SDPA."""
+    B, qr, H, D = w.q_bits.shape
+    G = H // w.num_kv_heads
+    q = torch_bf16(w.q_bits)
+    out = np.zeros(q.shape, np.float64)
+    cap = w.max_blocks * w.page_size
+    for b in range(B):
+        L = np.clip(w.row_lens[b].astype(np.int64), 0, cap)
+        for g in range(w.num_kv_heads):
+            toks = np.array([int(t) for t in w.sel_tokens[b, g] if 0 <= t < cap], np.int64)
+            phys = w.block_table[b][toks // w.page_size].astype(np.int64)
+            u = toks % w.page_size
+            k = torch_e4m3(w.k_pool[phys, u, g])
+            v = torch_e4m3(w.v_pool[phys, u, g])
+            mask = toks[None, :] < L[:, None]
+            for h in range(g * G, (g + 1) * G):
+                out[b, :, h, :] = sdpa_rows(q[b, :, h, :], k, v, mask, w.sm_scale * w.k_scale)
+    return out * w.v_scale
+
+
 def assert_close_rel(a, b, rtol, what=""):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
@@ -604,11 +627,63 @@ def pin_selection_order(o):
     assert_close_rel(got, qsa_reference(qd), 1e-12, "all blocks selected")
 
 
+def _tokens_case(seed, **over):
+    kw = dict(batch=2, q_rows=3, num_heads=4, num_kv_heads=2, head_dim=16, ctx=100,
+              page_size=16, num_sel=20, num_empty=3, k_scale=0.5, v_scale=2.0)
+    kw.update(over)
+    return wl.make_qsa_tokens(f"pintok{seed}", seed, **kw)
+
+
+def pin_qsa_tokens(o):
+    """Token-id selection: (1) a block selection written out as its token ids
+    gives bit-for-bit the block-selection result, one pass and split (NaN
+    bytes in every unselected page); (2) against SDPA over the selected ids
+    with a per-row mask, including a duplicated id, a zero-length row, a row
+    past the table and an id past the table; (3) split partials combined give
+    the one-pass result."""
+    import dataclasses
+
+    q = _qsa_case(0xB10)
+    tok = wl.tokens_from_blocks(q)
+    one = o.qsa_tokens_verify(q.q_bits, q.k_pool, q.v_pool, q.block_table, tok, q.row_lens,
+                              q.sm_scale, q.k_scale, q.v_scale)
+    assert np.all(np.isfinite(one)), "token ids reached a poisoned page"
+    assert np.array_equal(one, o.qsa_workload(q)), "token ids of a block selection"
+    for S, T in [(3, 11), (8, 4)]:
+        a = o.qsa_tokens_split(q.q_bits, q.k_pool, q.v_pool, q.block_table, tok, q.row_lens,
+                               q.sm_scale, q.k_scale, S, T)
+        b = o.qsa_split(q.q_bits, q.k_pool, q.v_pool, q.block_table, q.sel_blocks,
+                        q.row_lens, q.sm_scale, q.k_scale, S, T)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), f"token-id split S={S}"
+
+    w = _tokens_case(0xB11)
+    assert_close_rel(o.qsa_tokens_workload(w), qsa_tokens_reference(w), 1e-12, "tokens basic")
+    sel = w.sel_tokens.copy()
+    sel[0, 1, 4] = sel[0, 1, 7]                  # a duplicated id counts twice
+    sel[1, 0, 2] = 7 * w.page_size + 3           # id past the table: never seen
+    lens = w.row_lens.copy()
+    lens[0, 1] = 0
+    lens[1, 2] = 10 ** 6                         # clamped to the table's capacity
+    w2 = dataclasses.replace(w, sel_tokens=sel, row_lens=lens)
+    got = o.qsa_tokens_workload(w2)
+    assert_close_rel(got, qsa_tokens_reference(w2), 1e-12, "tokens edge")
+    assert not got[0, 1].any(), "zero-length row"
+    R = w2.num_rows
+    for S, T in [(1, 20), (4, 5), (3, 7), (25, 1)]:
+        acc, mx, sm = o.qsa_tokens_split(w2.q_bits, w2.k_pool, w2.v_pool, w2.block_table,
+                                         w2.sel_tokens, w2.row_lens, w2.sm_scale,
+                                         w2.k_scale, S, T)
+        assert acc.shape == (S, R, w2.head_dim)
+        comb = o.combine(acc, mx, sm, w2.v_scale).reshape(got.shape)
+        assert_close_rel(comb, got, 1e-12, f"tokens split S={S}")
+
+
 # Cheap pins first: the planted-mistake test stops at the first failure.
 ALL_PINS = [
     pin_e4m3_golden, pin_e4m3_structure, pin_e4m3_vs_torch, pin_encoder_roundtrip,
     pin_encoder_vs_torch, pin_one_hot_probe, pin_closed_forms, pin_relocation,
     pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine, pin_visible_nan,
-    pin_combine_lse, pin_cache_write,
+    pin_combine_lse, pin_cache_write, pin_qsa_tokens,
     pin_selection_order, pin_fp16_decode, pin_bf16_decode,
 ]

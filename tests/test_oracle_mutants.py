@@ -16,7 +16,7 @@ import pytest
 from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-MUTANTS = list(range(1, 15))
+MUTANTS = list(range(1, 17))
 
 _RUNNER = r"""
 import sys, traceback
