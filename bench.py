@@ -230,6 +230,9 @@ class QsaBench(DenseBench):
     """The sparse (QSA) batch resident on the device, with n_copies of its pool."""
 
     def __init__(self, w, n_copies: int, kernel: str):
+        self._setup(w, n_copies, w.sel_blocks, w.topk * w.page_size, kernel)
+
+    def _setup(self, w, n_copies: int, sel, list_len: int, kernel: str):
         import numpy as np
         import torch
 
@@ -243,11 +246,11 @@ class QsaBench(DenseBench):
         v = torch.from_numpy(w.v_pool).to(dev)
         self.pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(n_copies - 1)]
         self.table = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
-        self.sel = torch.from_numpy(w.sel_blocks.astype(np.int32)).to(dev)
+        self.sel = torch.from_numpy(sel.astype(np.int32)).to(dev)
         self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
         G = w.num_heads // w.num_kv_heads
-        self.plan = pa.plan(w.topk * w.page_size, w.q_rows * G, w.batch * w.num_kv_heads,
-                            w.head_dim, splits=w.num_splits, kernel=kernel)
+        self.plan = pa.plan(list_len, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
+                            splits=w.num_splits, kernel=kernel)
         self.rows = w.num_rows
         self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
         self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),
@@ -259,6 +262,19 @@ class QsaBench(DenseBench):
         w = self.w
         self.pa.qsa_sparse_verify_e4m3(self.q, k, v, self.table, self.sel, self.lens, w.sm_scale,
                                        w.k_scale, self.plan, self.ws)
+
+
+class QsaTokensBench(QsaBench):
+    """The sparse batch over selected token ids, resident on the device."""
+
+    def __init__(self, w, n_copies: int, kernel: str):
+        self._setup(w, n_copies, w.sel_tokens, w.num_sel, kernel)
+
+    def verify(self, i: int):
+        k, v = self.pools[i % len(self.pools)]
+        w = self.w
+        self.pa.qsa_sparse_verify_tokens_e4m3(self.q, k, v, self.table, self.sel, self.lens,
+                                              w.sm_scale, w.k_scale, self.plan, self.ws)
 
 
 def measure(b, steps: int, warmup: int) -> dict:
@@ -495,6 +511,13 @@ def main():
         sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, measure(bq, steps, args.warmup),
                                  units=wq.batch * wq.num_kv_heads))
         del bq
+        torch.cuda.empty_cache()
+        log("[bench] sweep c4tok (QSA over token ids)")
+        wt = wl.cached("c4tok")
+        bt = QsaTokensBench(wt, copies_for(2 * wt.k_pool.size), args.kernel)
+        sweep.append(sweep_entry(wt.name, bt.kv_bytes, bt.plan, measure(bt, steps, args.warmup),
+                                 units=wt.batch * wt.num_kv_heads))
+        del bt
         torch.cuda.empty_cache()
         log("[bench] sweep batch (independent requests)")
         wb = wl.cached("batch")

@@ -11,7 +11,9 @@ Entry points (same names as the C ABI):
   paged_attn_verify_e4m3(...)    dense verify, writes FP32 split partials
   paged_attn_combine_fp32(...)   merges partials into FP16 rows
   qsa_sparse_verify_e4m3(...)    sparse verify over selected blocks
-and the conveniences ``verify`` and ``qsa_verify`` (verify + combine).
+  qsa_sparse_verify_tokens_e4m3(...)  sparse verify over selected token ids
+and the conveniences ``verify``, ``verify_batch``, ``qsa_verify`` and
+``qsa_verify_tokens`` (verify + combine).
 """
 
 from __future__ import annotations
@@ -58,7 +60,7 @@ EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_pla
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
            "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
-           "paged_attn_cache_write_e4m3")
+           "paged_attn_cache_write_e4m3", "qsa_sparse_verify_tokens_e4m3")
 
 _LIB = None
 
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
                                          i32, i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                          ctypes.POINTER(PaWorkspace), p]
     L.qsa_sparse_verify_e4m3.restype = i32
+    L.qsa_sparse_verify_tokens_e4m3.argtypes = L.qsa_sparse_verify_e4m3.argtypes
+    L.qsa_sparse_verify_tokens_e4m3.restype = i32
     L.paged_attn_timer_arm.argtypes = [i32]
     L.paged_attn_timer_arm.restype = i32
     L.paged_attn_timer_read.argtypes = [ctypes.POINTER(ctypes.c_float), i32,
@@ -347,9 +351,7 @@ def paged_attn_combine_fp32_lse(ws, num_splits: int, num_rows: int, head_dim: in
     _check(rc, "paged_attn_combine_fp32_lse")
 
 
-def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,
-                           k_scale, p: PaPlan, ws) -> None:
-    """Sparse verify of a batch over selected blocks into the FP32 split workspace."""
+def _sparse_args(q, k_pool, v_pool, block_table, sel, row_lens, name):
     torch = _torch()
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
         raise ValueError("q must be a contiguous bfloat16 tensor [batch][q_rows][heads][head_dim]")
@@ -361,16 +363,36 @@ def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens,
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [batch][max_blocks]")
     Hkv = k_pool.shape[2]
-    if sel_blocks.dim() != 3 or tuple(sel_blocks.shape[:2]) != (B, Hkv):
-        raise ValueError("sel_blocks must be [batch][kv_heads][topk]")
+    if sel.dim() != 3 or tuple(sel.shape[:2]) != (B, Hkv):
+        raise ValueError(f"{name} must be [batch][kv_heads][n]")
     if tuple(row_lens.shape) != (B, qr):
         raise ValueError("row_lens must be [batch][q_rows]")
+    return (q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
+            block_table.shape[1], _i32(sel, name, dev), sel.shape[2],
+            _i32(row_lens, "row_lens", dev), B, qr, H, Hkv, D), dev
+
+
+def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,
+                           k_scale, p: PaPlan, ws) -> None:
+    """Sparse verify of a batch over selected blocks into the FP32 split workspace."""
+    args, dev = _sparse_args(q, k_pool, v_pool, block_table, sel_blocks, row_lens,
+                             "sel_blocks")
     rc = lib().qsa_sparse_verify_e4m3(
-        q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
-        block_table.shape[1], _i32(sel_blocks, "sel_blocks", dev), sel_blocks.shape[2],
-        _i32(row_lens, "row_lens", dev), B, qr, H, Hkv, D, _scale(sm_scale, dev, "sm_scale"),
-        _scale(k_scale, dev, "k_scale"), ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
+        *args, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "qsa_sparse_verify_e4m3")
+
+
+def qsa_sparse_verify_tokens_e4m3(q, k_pool, v_pool, block_table, sel_tokens, row_lens,
+                                  sm_scale, k_scale, p: PaPlan, ws) -> None:
+    """Sparse verify of a batch over selected token ids (-1 = empty) into the
+    FP32 split workspace."""
+    args, dev = _sparse_args(q, k_pool, v_pool, block_table, sel_tokens, row_lens,
+                             "sel_tokens")
+    rc = lib().qsa_sparse_verify_tokens_e4m3(
+        *args, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
+    _check(rc, "qsa_sparse_verify_tokens_e4m3")
 
 
 # ---------------------------------------------------------------------------
@@ -434,5 +456,25 @@ def qsa_verify(q, k_pool, v_pool, block_table, sel_blocks, row_lens, *, sm_scale
         out = torch.empty((B, qr, H, D), dtype=torch.float16, device=q.device)
     qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens, sm_scale,
                            k_scale, p, ws)
+    paged_attn_combine_fp32(ws, p.num_splits, B * qr * H, D, v_scale, out)
+    return out
+
+
+def qsa_verify_tokens(q, k_pool, v_pool, block_table, sel_tokens, row_lens, *, sm_scale,
+                      k_scale, v_scale, splits: int = 0, kernel: str = "auto",
+                      p: Optional[PaPlan] = None, ws: Optional[Tuple] = None, out=None):
+    """Sparse verify of a batch over selected token ids; returns FP16
+    [batch][q_rows][heads][head_dim]."""
+    torch = _torch()
+    B, qr, H, D = q.shape
+    Hkv = k_pool.shape[2]
+    if p is None:
+        p = plan(sel_tokens.shape[2], qr * (H // Hkv), B * Hkv, D, splits=splits, kernel=kernel)
+    if ws is None:
+        ws = make_workspace(p, B * qr * H, D, q.device)
+    if out is None:
+        out = torch.empty((B, qr, H, D), dtype=torch.float16, device=q.device)
+    qsa_sparse_verify_tokens_e4m3(q, k_pool, v_pool, block_table, sel_tokens, row_lens,
+                                  sm_scale, k_scale, p, ws)
     paged_attn_combine_fp32(ws, p.num_splits, B * qr * H, D, v_scale, out)
     return out

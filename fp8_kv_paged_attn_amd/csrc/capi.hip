@@ -176,8 +176,8 @@ const hipEvent_t *timer_take()
     return &g_timer.ev[2 * g_timer.used++];
 }
 
-int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim, bool sparse,
-                 hipStream_t stream)
+int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim,
+                 pa::VerifyMode mode, hipStream_t stream)
 {
     int32_t rc = check_device();
     if (rc != PA_OK)
@@ -186,20 +186,90 @@ int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim, boo
     hipError_t err;
     switch (plan->kernel) {
     case PA_KERNEL_SIMPLE:
-        err = pa::launch_verify_simple(a, head_dim, sparse, stream, ev);
+        err = pa::launch_verify_simple(a, head_dim, mode, stream, ev);
         break;
     case PA_KERNEL_MFMA:
-        err = pa::launch_verify_mfma(a, head_dim, sparse, stream, ev);
+        err = pa::launch_verify_mfma(a, head_dim, mode, stream, ev);
         if (err == hipErrorNotSupported)
             return PA_EUNSUPPORTED;
         break;
     default:
-        err = pa::launch_verify_mfma(a, head_dim, sparse, stream, ev);
+        err = pa::launch_verify_mfma(a, head_dim, mode, stream, ev);
         if (err == hipErrorNotSupported)
-            err = pa::launch_verify_simple(a, head_dim, sparse, stream, ev);
+            err = pa::launch_verify_simple(a, head_dim, mode, stream, ev);
         break;
     }
     return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+// The two sparse entries: a selection list of blocks (positions topk * page)
+// or of token ids (positions topk), -1 = empty.
+int32_t sparse_verify(pa::VerifyMode mode, const void *q_bf16, const pa_kv_pool *kv,
+                      const int32_t *block_table, int32_t max_blocks_per_req,
+                      const int32_t *sel, int32_t topk, const int32_t *row_lens,
+                      int32_t batch, int32_t q_rows, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float sm_scale, float k_scale, const pa_plan *plan,
+                      const pa_workspace *ws, void *stream)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!q_bf16 || !block_table || !sel || !row_lens)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
+        return rc;
+    if (!aligned16(q_bf16))
+        return PA_EALIGN;
+    if (batch < 1 || max_blocks_per_req < 1 || topk < 1)
+        return PA_EINVAL;
+    const int64_t list_len =
+        mode == pa::kModeTokens ? (int64_t)topk : (int64_t)topk * kv->page_size;
+    const int64_t cap = (int64_t)max_blocks_per_req * kv->page_size;
+    if (list_len > 0x7FFFFFFF || cap > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((int64_t)batch * num_kv_heads > 65535)
+        return PA_EUNSUPPORTED;
+    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
+        return rc;
+    if ((rc = check_plan(plan, (int32_t)list_len, rows_per_unit, batch * num_kv_heads,
+                         head_dim)) != PA_OK)
+        return rc;
+    const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
+    if (total_rows > 0x7FFFFFFF)
+        return PA_EINVAL;
+    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
+        return rc;
+
+    pa::VerifyArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q_bf16);
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.page_stride = kv->page_stride;
+    a.token_stride = kv->token_stride;
+    a.head_stride = kv->head_stride;
+    a.page_size = kv->page_size;
+    a.block_table = block_table;
+    a.table_stride = max_blocks_per_req;
+    a.sel = sel;
+    a.topk = topk;
+    a.row_lens = row_lens;
+    a.len_cap = (int32_t)cap;
+    a.list_len = (int32_t)list_len;
+    a.batch = batch;
+    a.q_rows = q_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.rows = rows_per_unit;
+    a.num_splits = plan->num_splits;
+    a.tokens_per_split = plan->tokens_per_split;
+    a.total_rows = (int32_t)total_rows;
+    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    a.ws_acc = ws->acc;
+    a.ws_max = ws->max;
+    a.ws_sum = ws->sum;
+    return dispatch(a, plan, head_dim, mode, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -323,7 +393,7 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     (void)kLog2e;
-    return dispatch(a, plan, head_dim, false, static_cast<hipStream_t>(stream));
+    return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
@@ -390,7 +460,7 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.ws_acc = ws->acc;
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
-    return dispatch(a, plan, head_dim, false, static_cast<hipStream_t>(stream));
+    return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
 }
 
 int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,
@@ -422,64 +492,22 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream)
 {
-    int32_t rc, rows_per_unit = 0;
-    if (!q_bf16 || !block_table || !sel_blocks || !row_lens)
-        return PA_EINVAL;
-    if ((rc = check_pool(kv)) != PA_OK)
-        return rc;
-    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
-        return rc;
-    if (!aligned16(q_bf16))
-        return PA_EALIGN;
-    if (batch < 1 || max_blocks_per_req < 1 || topk < 1)
-        return PA_EINVAL;
-    const int64_t list_len = (int64_t)topk * kv->page_size;
-    const int64_t cap = (int64_t)max_blocks_per_req * kv->page_size;
-    if (list_len > 0x7FFFFFFF || cap > 0x7FFFFFFF)
-        return PA_EINVAL;
-    if ((int64_t)batch * num_kv_heads > 65535)
-        return PA_EUNSUPPORTED;
-    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
-        return rc;
-    if ((rc = check_plan(plan, (int32_t)list_len, rows_per_unit, batch * num_kv_heads,
-                         head_dim)) != PA_OK)
-        return rc;
-    const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
-    if (total_rows > 0x7FFFFFFF)
-        return PA_EINVAL;
-    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
-        return rc;
+    return sparse_verify(pa::kModeBlocks, q_bf16, kv, block_table, max_blocks_per_req,
+                         sel_blocks, topk, row_lens, batch, q_rows, num_heads, num_kv_heads,
+                         head_dim, sm_scale, k_scale, plan, ws, stream);
+}
 
-    pa::VerifyArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.q = static_cast<const uint16_t *>(q_bf16);
-    a.k_pool = kv->k_pool;
-    a.v_pool = kv->v_pool;
-    a.page_stride = kv->page_stride;
-    a.token_stride = kv->token_stride;
-    a.head_stride = kv->head_stride;
-    a.page_size = kv->page_size;
-    a.block_table = block_table;
-    a.table_stride = max_blocks_per_req;
-    a.sel = sel_blocks;
-    a.topk = topk;
-    a.row_lens = row_lens;
-    a.len_cap = (int32_t)cap;
-    a.list_len = (int32_t)list_len;
-    a.batch = batch;
-    a.q_rows = q_rows;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = num_heads / num_kv_heads;
-    a.rows = rows_per_unit;
-    a.num_splits = plan->num_splits;
-    a.tokens_per_split = plan->tokens_per_split;
-    a.total_rows = (int32_t)total_rows;
-    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
-    a.ws_acc = ws->acc;
-    a.ws_max = ws->max;
-    a.ws_sum = ws->sum;
-    return dispatch(a, plan, head_dim, true, static_cast<hipStream_t>(stream));
+int32_t qsa_sparse_verify_tokens_e4m3(const void *q_bf16, const pa_kv_pool *kv,
+                                      const int32_t *block_table, int32_t max_blocks_per_req,
+                                      const int32_t *sel_tokens, int32_t num_sel,
+                                      const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float sm_scale, float k_scale, const pa_plan *plan,
+                                      const pa_workspace *ws, void *stream)
+{
+    return sparse_verify(pa::kModeTokens, q_bf16, kv, block_table, max_blocks_per_req,
+                         sel_tokens, num_sel, row_lens, batch, q_rows, num_heads, num_kv_heads,
+                         head_dim, sm_scale, k_scale, plan, ws, stream);
 }
 
 int32_t paged_attn_cache_write_e4m3(const void *k_fp16, const void *v_fp16, int64_t num_tokens,

@@ -8,9 +8,15 @@
 
 namespace pa {
 
+// How a list position maps to a token.
+enum VerifyMode : int {
+    kModeDense = 0,     // position p of request b is token p
+    kModeBlocks = 1,    // position p is row p % page of selected block sel[p / page]
+    kModeTokens = 2,    // position p is token sel[p] (-1: empty)
+};
+
 // Everything a verify kernel needs, resolved on the host.  One struct serves
-// the dense path (one request, token = list position) and the sparse path
-// (list position -> selected block -> token).
+// the dense path and both sparse selections.
 struct VerifyArgs {
     const uint16_t *q;          // fp16 (dense) or bf16 (sparse) bits [B][q_rows][H][D]
     const uint8_t *k_pool;
@@ -21,11 +27,12 @@ struct VerifyArgs {
     int32_t page_size;
     const int32_t *block_table; // [B][table_stride] (one request: [entries])
     int32_t table_stride;       // entries per request (one dense request: 0)
-    const int32_t *sel;         // sparse: [B][Hkv][topk]; dense: nullptr
+    const int32_t *sel;         // sparse: [B][Hkv][topk] blocks or token ids; dense: nullptr
     int32_t topk;
     const int32_t *row_lens;    // [B][q_rows]
     int32_t len_cap;            // lengths are clamped to [0, len_cap]
-    int32_t list_len;           // positions per KV unit (dense: max_tokens; sparse: topk*page)
+    int32_t list_len;           // positions per KV unit (dense: max_tokens; blocks:
+                                // topk*page; tokens: topk)
     int32_t batch, q_rows, num_heads, num_kv_heads, group;  // group = H / Hkv
     int32_t rows;               // rows per KV unit = q_rows * group
     int32_t num_splits, tokens_per_split;
@@ -38,8 +45,8 @@ struct VerifyArgs {
 // row chunks of 48).
 // `ev`, when not null, is a (begin, end) pair of HIP events bound to the
 // kernel's own dispatch (hipExtLaunchKernel), for the kernel timer.
-hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
+hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, VerifyMode mode,
                                 hipStream_t stream, const hipEvent_t *ev = nullptr);
-hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse,
+hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, VerifyMode mode,
                               hipStream_t stream, const hipEvent_t *ev = nullptr);
 }  // namespace pa

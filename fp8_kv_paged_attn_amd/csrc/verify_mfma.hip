@@ -272,9 +272,14 @@ constexpr int max_slots()
     return D == 256 ? kMaxSlotsD256 : kMaxSlotsD128;
 }
 
-template <int D, bool SPARSE>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, DivMagic dm)
 {
+    // SPARSE: bf16 queries and a selection list (blocks or token ids); TOK:
+    // the list holds token ids, one slot per position, and dm divides by the
+    // page size to place a token (in the other modes positions are divided)
+    constexpr bool SPARSE = MODE != kModeDense;
+    constexpr bool TOK = MODE == kModeTokens;
     typedef Cfg<D> C;
     typedef typename Frag<SPARSE>::T QFrag;
     constexpr int kSlots = max_slots<D>();
@@ -338,10 +343,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int32_t *table = a.block_table + (int64_t)b * a.table_stride;
     int slot0 = 0, nslots = 0;
     if (hi_list > lo) {
-        slot0 = divp(lo, dm);
-        nslots = min(divp(hi_list - 1, dm) + 1 - slot0, kSlots);
+        slot0 = TOK ? lo : divp(lo, dm);
+        nslots = min(TOK ? hi_list - lo : divp(hi_list - 1, dm) + 1 - slot0, kSlots);
     }
-    // table entries of this split's slots (dense) or its selected blocks (sparse)
+    // table entries of this split's slots (dense), its selected blocks or its
+    // selected token ids (sparse)
     int ent[kEnt];
 #pragma unroll
     for (int k = 0; k < kEnt; ++k) {
@@ -394,6 +400,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             if (!SPARSE) {
                 phys = ent[k];
                 tb = (slot0 + i) * ps;
+            } else if (TOK) {
+                // a token no row sees keeps phys -1; lmax <= the table's
+                // capacity, so a token below it has a table entry
+                const int t = ent[k];
+                if (t >= 0 && t < lmax) {
+                    phys = table[divp(t, dm)];
+                    tb = t;
+                }
             } else {
                 const int blk = ent[k];
                 if (blk >= 0 && (int64_t)blk * ps < lmax) {
@@ -436,6 +450,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // Position -> (byte offset of the K/V head row, token, valid).  Branch-free;
     // the slot cache is the only table read.
     auto resolve = [&](int pos, int64_t &off, int &t) __attribute__((always_inline)) -> bool {
+        if (TOK) {
+            const int2v e = slots[min(max(pos - slot0, 0), kSlots - 1)];
+            t = e.y;
+            const bool ok = pos < hi && e.x >= 0;
+            const int u = t - divp(t, dm) * ps;
+            off = ok ? (int64_t)e.x * a.page_stride + (int64_t)u * a.token_stride + head_off : 0;
+            return ok;
+        }
         const int slot = divp(pos, dm);
         const int u = pos - slot * ps;
         const int si = min(max(slot - slot0, 0), kSlots - 1);
@@ -453,12 +475,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // position l%LANES_PER_ROW.  With pages of at least 32 tokens a block spans
     // at most two page slots, so the page lookup is done once per block
     // (wave-uniform) and a lane only adds its precomputed row offset; small
-    // pages or very large token strides take the per-row resolve.  Positions
-    // past the end load an in-bounds dummy address, so that every step issues
-    // the same number of loads.  tokst (sparse, V loads only) receives the
-    // token of each row, INT32_MAX for rows no query sees.
+    // pages, very large token strides and token-id lists take the per-row
+    // resolve.  Positions past the end load an in-bounds dummy address, so that
+    // every step issues the same number of loads.  tokst (sparse, V loads only)
+    // receives the token of each row, INT32_MAX for rows no query sees, and
+    // blk_tmax the largest of them when it is known (INT32_MAX otherwise).
     const int cp = lane % C::LANES_PER_ROW;
-    const bool two_slot = ps >= kSub && a.token_stride < (1 << 25);
+    const bool two_slot = !TOK && ps >= kSub && a.token_stride < (1 << 25);
     int32_t loff[C::DMA];
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
@@ -540,6 +563,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             }
         } else {
             const int pos0 = lo + (j * kWaves + w) * kSub;
+            int tm = 0;
 #pragma unroll
             for (int i = 0; i < C::DMA; ++i) {
                 const int row = i * C::ROWS_PER_DMA + lane / C::LANES_PER_ROW;
@@ -550,9 +574,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 dma16(pool + src, dst + i * 1024);
                 if (SPARSE && tokst != nullptr && cp == 0)
                     tokst[row] = ok ? t : INT32_MAX;
+                tm = max(tm, ok ? t : INT32_MAX);
+            }
+            if (TOK && tokst != nullptr) {
+                // token ids are unordered: the block's largest comes from the wave
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1)
+                    tm = max(tm, __shfl_xor(tm, o, 64));
             }
             if (SPARSE && tokst != nullptr && lane == 0)
-                *tmaxp = INT32_MAX;
+                *tmaxp = TOK ? tm : INT32_MAX;
         }
     };
 
@@ -931,17 +962,18 @@ DivMagic make_magic(int d)
     return dm;
 }
 
-template <int D, bool SPARSE>
+template <int D, int MODE>
 hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
 {
-    // every split's page slots must fit the LDS slot cache
-    const int64_t slots = (int64_t)(a.tokens_per_split - 1) / a.page_size + 2;
+    // every split's page slots (token ids: positions) must fit the LDS slot cache
+    const int64_t slots = MODE == kModeTokens ? (int64_t)a.tokens_per_split
+                                              : (int64_t)(a.tokens_per_split - 1) / a.page_size + 2;
     if (slots > max_slots<D>())
         return hipErrorNotSupported;
     // grid z: chunks of 48 rows of a KV unit (one chunk up to 48 rows)
     dim3 grid(a.num_splits, a.batch * a.num_kv_heads,
               (a.rows + 16 * kRowBlocks - 1) / (16 * kRowBlocks));
-    hipExtLaunchKernelGGL((verify_mfma_kernel<D, SPARSE>), grid, dim3(kThreads), 0, stream,
+    hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
                           make_magic(a.page_size));
     return hipGetLastError();
@@ -949,16 +981,20 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
 
 }  // namespace
 
-hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, bool sparse, hipStream_t stream,
-                              const hipEvent_t *ev)
+hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, VerifyMode mode,
+                              hipStream_t stream, const hipEvent_t *ev)
 {
     if (a.rows < 1 || a.rows > 65535 * 16 * kRowBlocks)
         return hipErrorNotSupported;
-    if (head_dim == 256)
-        return sparse ? launch_t<256, true>(a, stream, ev) : launch_t<256, false>(a, stream, ev);
-    if (head_dim == 128)
-        return sparse ? launch_t<128, true>(a, stream, ev) : launch_t<128, false>(a, stream, ev);
-    return hipErrorNotSupported;
+    switch (head_dim * 4 + mode) {
+    case 256 * 4 + kModeDense: return launch_t<256, kModeDense>(a, stream, ev);
+    case 256 * 4 + kModeBlocks: return launch_t<256, kModeBlocks>(a, stream, ev);
+    case 256 * 4 + kModeTokens: return launch_t<256, kModeTokens>(a, stream, ev);
+    case 128 * 4 + kModeDense: return launch_t<128, kModeDense>(a, stream, ev);
+    case 128 * 4 + kModeBlocks: return launch_t<128, kModeBlocks>(a, stream, ev);
+    case 128 * 4 + kModeTokens: return launch_t<128, kModeTokens>(a, stream, ev);
+    default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace pa

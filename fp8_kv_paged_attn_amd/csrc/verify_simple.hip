@@ -1,4 +1,5 @@
-// verify_simple.hip - straightforward FP32 verify kernel (dense and sparse).
+// verify_simple.hip - straightforward FP32 verify kernel (dense, and sparse over
+// selected blocks or selected token ids).
 //
 // One workgroup per (split, KV unit).  Each 64-position tile of the split is
 // gathered into LDS as raw E4M3 bytes, scores are FP32 dot products, the
@@ -40,19 +41,27 @@ __device__ inline float bf16_to_float(uint16_t bits)
 }
 
 // List position -> (logical token, byte offset of its K/V head row).  False for
-// an empty selection slot or a token no row of this unit sees.
-template <bool SPARSE>
+// an empty selection slot or a token no row of this unit sees.  lmax is at
+// most the table's capacity, so a token below it has a table entry.
+template <int MODE>
 __device__ inline bool resolve(const VerifyArgs &a, int b, int g, int pos, int lmax,
                                int32_t &t, int64_t &off)
 {
     const int ps = a.page_size;
     int blk, u;
-    if (!SPARSE) {
+    if (MODE == kModeDense) {
         t = pos;
         blk = pos / ps;
         u = pos - blk * ps;
         if (t >= lmax)
             return false;
+        off = (int64_t)a.block_table[(int64_t)b * a.table_stride + blk] * a.page_stride;
+    } else if (MODE == kModeTokens) {
+        t = a.sel[((int64_t)b * a.num_kv_heads + g) * a.topk + pos];
+        if (t < 0 || t >= lmax)
+            return false;
+        blk = t / ps;
+        u = t - blk * ps;
         off = (int64_t)a.block_table[(int64_t)b * a.table_stride + blk] * a.page_stride;
     } else {
         int j = pos / ps;
@@ -69,7 +78,7 @@ __device__ inline bool resolve(const VerifyArgs &a, int b, int g, int pos, int l
     return true;
 }
 
-template <int D, bool SPARSE>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 {
     __shared__ float q_s[kMaxRows][D];
@@ -95,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
         int r = idx / D, d = idx - r * D;
         int i = (row0 + r) / G, h = g * G + (row0 + r - i * G);
         uint16_t bits = a.q[(((int64_t)b * a.q_rows + i) * a.num_heads + h) * D + d];
-        q_s[r][d] = SPARSE ? bf16_to_float(bits) : fp16_to_float(bits);
+        q_s[r][d] = MODE != kModeDense ? bf16_to_float(bits) : fp16_to_float(bits);
     }
     if (tid < R) {
         m_s[tid] = -INFINITY;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 
     const int lo = split * a.tokens_per_split;
     int hi = min(lo + a.tokens_per_split, a.list_len);
-    if (!SPARSE)
+    if (MODE == kModeDense)
         hi = min(hi, lmax);
 
     float acc[kMaxRows];
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
             int pos = p0 + j;
             int32_t t = -1;
             int64_t off = 0;
-            bool ok = pos < hi && resolve<SPARSE>(a, b, g, pos, lmax, t, off);
+            bool ok = pos < hi && resolve<MODE>(a, b, g, pos, lmax, t, off);
             uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
             if (ok) {
                 kv = *(const uint4 *)(a.k_pool + off + piece * 16);
@@ -198,22 +207,29 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 
 }  // namespace
 
-hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, bool sparse,
+hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, VerifyMode mode,
                                 hipStream_t stream, const hipEvent_t *ev)
 {
     dim3 grid(a.num_splits, a.batch * a.num_kv_heads, (a.rows + kMaxRows - 1) / kMaxRows);
     dim3 block(kThreads);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-    if (head_dim == 256 && !sparse)
-        hipExtLaunchKernelGGL((verify_simple_kernel<256, false>), grid, block, 0, stream, e0, e1, 0, a);
-    else if (head_dim == 128 && !sparse)
-        hipExtLaunchKernelGGL((verify_simple_kernel<128, false>), grid, block, 0, stream, e0, e1, 0, a);
-    else if (head_dim == 256 && sparse)
-        hipExtLaunchKernelGGL((verify_simple_kernel<256, true>), grid, block, 0, stream, e0, e1, 0, a);
-    else if (head_dim == 128 && sparse)
-        hipExtLaunchKernelGGL((verify_simple_kernel<128, true>), grid, block, 0, stream, e0, e1, 0, a);
+#define PA_SIMPLE(D, M)                                                                        \
+    hipExtLaunchKernelGGL((verify_simple_kernel<D, M>), grid, block, 0, stream, e0, e1, 0, a)
+    if (head_dim == 256 && mode == kModeDense)
+        PA_SIMPLE(256, kModeDense);
+    else if (head_dim == 128 && mode == kModeDense)
+        PA_SIMPLE(128, kModeDense);
+    else if (head_dim == 256 && mode == kModeBlocks)
+        PA_SIMPLE(256, kModeBlocks);
+    else if (head_dim == 128 && mode == kModeBlocks)
+        PA_SIMPLE(128, kModeBlocks);
+    else if (head_dim == 256 && mode == kModeTokens)
+        PA_SIMPLE(256, kModeTokens);
+    else if (head_dim == 128 && mode == kModeTokens)
+        PA_SIMPLE(128, kModeTokens);
     else
         return hipErrorInvalidValue;
+#undef PA_SIMPLE
     return hipGetLastError();
 }
 

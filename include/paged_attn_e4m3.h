@@ -253,6 +253,37 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream);
 
+/* Sparse (QSA) verify of a batch over selected token ids: the token-id
+ * selection with -1 padding that [NB] keeps for its DCP2 operator.  The pages
+ * name this interface without spelling it out; the reading taken here: each
+ * (request, KV head) carries a list of logical token ids.
+ *   sel_tokens   [batch][num_kv_heads][num_sel] int32 token ids; -1 = empty
+ *                entry (skipped).  Id t is row t % page_size of logical block
+ *                t / page_size of the request (through block_table).  Ids
+ *                >= max_blocks_per_req*page_size are never seen and never
+ *                index the table; repeated ids are attended as often as listed.
+ *   row_lens     [batch][q_rows] int32: row i of request b sees the ids
+ *                t < clamp(len, 0, max_blocks_per_req*page_size), so each row
+ *                has its own mask at any position of the list
+ *   plan         (host) from paged_attn_plan(num_sel, q_rows*num_heads/num_kv_heads,
+ *                batch*num_kv_heads, head_dim, ...); split s covers list entries
+ *                [s*T, (s+1)*T).  The MFMA kernel takes T <= 1024 (head_dim 256)
+ *                or <= 2048 (head_dim 128); with PA_KERNEL_AUTO a longer split
+ *                runs on the plain kernel, with PA_KERNEL_MFMA it is
+ *                PA_EUNSUPPORTED.
+ * Other arguments, the workspace rows and the errors as for
+ * qsa_sparse_verify_e4m3.  A block selection written out as its token ids
+ * (block s -> ids s*page_size .. s*page_size + page_size - 1, an empty slot
+ * -> page_size entries of -1) attends the same tokens in the same list
+ * order. */
+int32_t qsa_sparse_verify_tokens_e4m3(const void *q_bf16, const pa_kv_pool *kv,
+                                      const int32_t *block_table, int32_t max_blocks_per_req,
+                                      const int32_t *sel_tokens, int32_t num_sel,
+                                      const int32_t *row_lens, int32_t batch, int32_t q_rows,
+                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float sm_scale, float k_scale, const pa_plan *plan,
+                                      const pa_workspace *ws, void *stream);
+
 /* E4M3 cache write ([QSA]: the uint8 cache is written with the layer's
  * per-tensor scales through the write path): FP16 K/V tokens into the pool's
  * pages by slot.  This entry writes the bytes of kv->k_pool and kv->v_pool.
@@ -276,7 +307,7 @@ int32_t paged_attn_cache_write_e4m3(const void *k_fp16, const void *v_fp16, int6
 /* Kernel timer, for measurement harnesses; no result depends on it.
  *
  * paged_attn_timer_arm(n), 0 <= n <= PA_TIMER_MAX_LAUNCHES: the next n verify
- * launches (paged_attn_verify_e4m3 or qsa_sparse_verify_e4m3, any stream) made
+ * launches (any of the four verify entry points, any stream) made
  * with the current device current get a pair of HIP events passed with the
  * kernel's dispatch (hipExtLaunchKernel): the interval runs from the point the
  * launch is processed on the stream to the kernel's completion, so it adds no

@@ -118,6 +118,24 @@ def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     return res
 
 
+def run_qsa_tokens(w, kernel="auto", splits: Optional[int] = None, k_pool=None, v_pool=None):
+    """Token-id selection batch through qsa_sparse_verify_tokens_e4m3 + combine."""
+    q = bf16_tensor(w.q_bits).to(DEV)
+    k = torch.from_numpy(w.k_pool if k_pool is None else k_pool).to(DEV)
+    v = torch.from_numpy(w.v_pool if v_pool is None else v_pool).to(DEV)
+    bt = torch.from_numpy(w.block_table.astype(np.int32)).to(DEV)
+    sel = torch.from_numpy(w.sel_tokens.astype(np.int32)).to(DEV)
+    lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(DEV)
+    G = w.num_heads // w.num_kv_heads
+    s = w.num_splits if splits is None else splits
+    p = pa.plan(w.num_sel, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, splits=s,
+                kernel=kernel)
+    out = pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
+                               v_scale=w.v_scale, p=p)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
 def metrics(gpu: np.ndarray, ref: np.ndarray) -> dict:
     g = gpu.astype(np.float64)
     err = g - ref

@@ -178,6 +178,35 @@ def test_qsa_and_combine_reject_bad_arguments(L):
 
 
 @no_device
+def test_qsa_tokens_rejects_bad_arguments(L):
+    """The token-id entry: the plan is made for num_sel list positions (not
+    num_sel * page_size), and a device-free valid call reaches PA_EDEVICE."""
+    pool = pa.PaKvPool(A * 2, A * 3, 64 * 256, 256, 128, 8192, 64)
+    p = pa.plan(2048, 48, 32, 128)
+    ws = pa.PaWorkspace(A * 6, A * 7, A * 8, p.ws_acc_bytes, p.ws_stat_bytes)
+
+    def tok(**kw):
+        a = dict(q=A, table=A * 4, maxb=512, sel=A * 9, n=2048, lens=A * 5, B=16, qr=4, H=24,
+                 Hkv=2, D=128, sm=0.088, ks=0.5, plan=p)
+        a.update(kw)
+        return L.qsa_sparse_verify_tokens_e4m3(a["q"], ctypes.byref(pool), a["table"],
+                                               a["maxb"], a["sel"], a["n"], a["lens"], a["B"],
+                                               a["qr"], a["H"], a["Hkv"], a["D"], a["sm"],
+                                               a["ks"], ctypes.byref(a["plan"]),
+                                               ctypes.byref(ws), None)
+
+    assert tok() == PA_EDEVICE
+    assert tok(sel=None) == PA_EINVAL
+    assert tok(n=0) == PA_EINVAL
+    assert tok(n=32) == PA_EPLAN                        # the block entry's list length
+    assert tok(plan=pa.plan(4096, 48, 32, 128)) == PA_EPLAN
+    assert tok(B=8) == PA_EPLAN
+    assert tok(q=A + 8) == PA_EALIGN
+    assert tok(ks=float("inf")) == PA_EINVAL
+    assert tok(H=96) == PA_EUNSUPPORTED
+
+
+@no_device
 def test_valid_call_without_device_reports_edevice(L):
     assert Call()(L) == PA_EDEVICE
 

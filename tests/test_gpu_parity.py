@@ -119,6 +119,116 @@ def test_qsa_d256(orc, kernel):
 
 
 # ---------------------------------------------------------------------------
+# sparse verify over selected token ids
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_tokens_config(orc, kernel):
+    w = wl.cached("c4tok")
+    announce("c4tok", kernel)
+    got = gu.run_qsa_tokens(w, kernel)
+    gu.assert_parity(got, orc.qsa_tokens_workload(w, nthreads=8), f"c4tok/{kernel}")
+
+
+def _tokens_edges(seed, **kw):
+    w = wl.make_qsa_tokens(f"tok_edges{seed}", seed, **kw)
+    sel = w.sel_tokens.copy()
+    cap = w.max_blocks * w.page_size
+    sel[0, 0, 5] = sel[0, 0, 9]             # an id listed twice
+    sel[0, -1, 3] = cap + 5                 # an id past the table: never seen
+    sel[-1, 0, :] = -1                      # nothing selected
+    lens = w.row_lens.copy()
+    lens[0, 1] = 0
+    lens[1, -1] = 10 ** 6                   # clamped to the table's capacity
+    return dataclasses.replace(w, sel_tokens=sel, row_lens=lens)
+
+
+TOKEN_EDGES = [
+    # (D, heads, kv heads, q rows, ctx, page, ids per list, -1 entries, splits)
+    (128, 12, 2, 4, 1500, 64, 300, 7, 3),
+    (128, 24, 2, 4, 2000, 16, 700, 0, None),
+    (256, 6, 1, 8, 900, 32, 250, 5, 2),
+    (256, 6, 1, 3, 700, 7, 129, 1, 1),
+]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", range(len(TOKEN_EDGES)))
+def test_qsa_tokens_small_edges(orc, case, kernel):
+    D, H, Hkv, qr, ctx, ps, n, empty, splits = TOKEN_EDGES[case]
+    w = _tokens_edges(0x70C0 + case, batch=3, q_rows=qr, num_heads=H, num_kv_heads=Hkv,
+                      head_dim=D, ctx=ctx, page_size=ps, num_sel=n, num_empty=empty,
+                      k_scale=0.5, v_scale=2.0, num_splits=splits or 0)
+    announce("qsa_tokens_edges", TOKEN_EDGES[case], kernel)
+    got = gu.run_qsa_tokens(w, kernel)
+    gu.assert_parity(got, orc.qsa_tokens_workload(w), f"tokens{case}/{kernel}")
+    G = H // Hkv
+    assert not got[2, :, :G].any(), "unit with an empty selection must give zeros"
+    assert not got[0, 1].any(), "zero-length row"
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_tokens_match_block_selection(kernel):
+    """A block selection written out as token ids gives the block entry's
+    output bit for bit: same tokens, same list order, same splits."""
+    qb = wl.make_qsa("tok_vs_blk", 0x70D0, batch=2, q_rows=4, num_heads=12, num_kv_heads=2,
+                     head_dim=128, ctx=2048, page_size=64, topk=6, k_scale=0.5, v_scale=2.0,
+                     num_splits=3)
+    sel = qb.sel_blocks.copy()
+    sel[1, 0, 2] = -1
+    qb = dataclasses.replace(qb, sel_blocks=sel)
+    tok = wl.tokens_from_blocks(qb)
+    qt = wl.QsaTokensWorkload(
+        name="tok_vs_blk_t", q_bits=qb.q_bits, k_pool=qb.k_pool, v_pool=qb.v_pool,
+        block_table=qb.block_table, sel_tokens=tok, row_lens=qb.row_lens, batch=qb.batch,
+        q_rows=qb.q_rows, num_heads=qb.num_heads, num_kv_heads=qb.num_kv_heads,
+        head_dim=qb.head_dim, page_size=qb.page_size, max_blocks=qb.max_blocks,
+        num_sel=tok.shape[2], sm_scale=qb.sm_scale, k_scale=qb.k_scale, v_scale=qb.v_scale,
+        num_splits=3)
+    announce("tokens_vs_blocks", kernel)
+    a = gu.run_qsa(qb, kernel)
+    b = gu.run_qsa_tokens(qt, kernel)
+    assert np.all(np.isfinite(b)), "token ids reached a poisoned page"
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_qsa_tokens_unseen_bytes_never_read(kernel):
+    """NaN bytes at every token no row of its (request, KV head) sees (not
+    selected, or selected at or past the longest row) change no output bit."""
+    w = _tokens_edges(0x70E0, batch=3, q_rows=4, num_heads=12, num_kv_heads=2, head_dim=128,
+                      ctx=1500, page_size=64, num_sel=300, num_empty=7, k_scale=0.5,
+                      v_scale=2.0, num_splits=3)
+    kp, vp = w.k_pool.copy(), w.v_pool.copy()
+    seen = np.zeros(kp.shape[:3], bool)
+    cap = w.max_blocks * w.page_size
+    for b in range(w.batch):
+        lmax = min(max(int(w.row_lens[b].max()), 0), cap)
+        for g in range(w.num_kv_heads):
+            for t in w.sel_tokens[b, g]:
+                if 0 <= t < lmax:
+                    seen[w.block_table[b, t // w.page_size], t % w.page_size, g] = True
+    kp[~seen] = 0x7F
+    vp[~seen] = 0xFF
+    announce("tokens_unseen_nan", kernel)
+    clean = gu.run_qsa_tokens(w, kernel)
+    dirty = gu.run_qsa_tokens(w, kernel, k_pool=kp, v_pool=vp)
+    assert np.array_equal(clean.view(np.uint16), dirty.view(np.uint16))
+
+
+def test_qsa_tokens_long_split_kernel_choice(orc):
+    """A split longer than the MFMA kernel's slot cache: auto runs the plain
+    kernel, a forced MFMA kernel is refused."""
+    w = wl.make_qsa_tokens("tok_long", 0x70F0, batch=1, q_rows=2, num_heads=6, num_kv_heads=1,
+                           head_dim=256, ctx=3000, page_size=64, num_sel=1100, num_empty=4,
+                           k_scale=0.5, v_scale=2.0, num_splits=1)
+    announce("tokens_long_split")
+    gu.assert_parity(gu.run_qsa_tokens(w, "auto"), orc.qsa_tokens_workload(w), "tok_long")
+    with pytest.raises(RuntimeError, match="-2|unsupported"):
+        gu.run_qsa_tokens(w, "mfma")
+
+
+# ---------------------------------------------------------------------------
 # workspace and combine
 # ---------------------------------------------------------------------------
 
