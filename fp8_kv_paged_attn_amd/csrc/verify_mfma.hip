@@ -13,8 +13,11 @@
 //    no barrier and no exchange between waves; the four partial states are
 //    merged once, through LDS, at the end of the split.
 //  * K/V bytes move HBM -> LDS with direct-to-LDS 16-byte loads (no VGPRs),
-//    into two stages per plane per wave, two blocks ahead, on a fixed issue
-//    schedule so that the wait counts are the same every step.  The 16-byte
+//    into two stages per plane per wave, one block ahead, on a fixed issue
+//    schedule so that the wait counts are the same every step.  Keeping the
+//    per-CU queue of loads short matters more than depth: a wave whose load
+//    issue finds the queue full stalls, and with two blocks ahead every wave
+//    sat in the issue of the first burst while its first block had landed.  The 16-byte
 //    chunks of each token row are XOR-swizzled so that the MFMA operand reads
 //    are free of LDS bank conflicts.
 //  * E4M3 -> FP16 (or BF16 for a BF16 query) with the hardware converter,
@@ -292,8 +295,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __shared__ __attribute__((aligned(16))) int32_t tok_s[kWaves][2][kSub];   // sparse tokens
     __shared__ int32_t blk_tmax[kWaves][2];         // sparse: last token of an all-valid block
     __shared__ float xm[kWaves][16 * kRowBlocks];   // merge: per-wave row max
-    __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave scaled row sum
-    __shared__ float xf[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator scale
+    __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave row sum
+    __shared__ float xr[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator reference
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -632,13 +635,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     };
 
     // One block of this wave (step j) with NRB live row blocks.  Block j uses K
-    // stage j%2 and V stage j%2.  Issue order: K0 V0 K1 V1 (prologue), then in
-    // step j: K(j+2) after QK(j), V(j+2) after P.V(j); blocks past the last
-    // step are not loaded.  Before QK(j) the groups issued after K(j) are
-    // V(j), and K(j+1), V(j+1) if block j+1 exists; before P.V(j) they are
-    // K(j+1), V(j+1) and K(j+2) where those blocks exist.  Loads complete in
-    // issue order, so allowing exactly that many groups in flight means the
-    // awaited group has landed.
+    // stage j%2 and V stage j%2.  Issue order: K0 V0 (prologue), then in step
+    // j: K(j+1) after QK(j) (its stage held K(j-1)), V(j+1) after P.V(j) (its
+    // stage held V(j-1)); blocks past the last step are not loaded.  Before
+    // QK(j) the only group issued after K(j) is V(j); before P.V(j) it is
+    // K(j+1), if block j+1 exists.  Loads complete in issue order, so
+    // allowing exactly that many groups in flight means the awaited group has
+    // landed.
     auto wait_groups = [&](int groups) __attribute__((always_inline)) {
         if (groups >= 3)
             wait_vmcnt<3 * C::DMA>();
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         int32_t *tok = &tok_s[w][st][0];
         const int pos0 = lo + (j * kWaves + w) * kSub;
         const bool any = pos0 < hi;                  // wave-uniform
-        wait_groups(j + 1 < nms ? 3 : 1);
+        wait_groups(1);                              // K(j); V(j) may be in flight
 
         // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
         f32x4 s[NRB][2];
@@ -697,10 +700,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 }
             }
         }
-        BlockRef br2 = {};
-        if (j + 2 < nms) {
-            br2 = lookup(j + 2);
-            issue_plane(br2, j + 2, a.k_pool, kst, nullptr);
+        BlockRef bnext = {};
+        if (j + 1 < nms) {
+            bnext = lookup(j + 1);
+            issue_plane(bnext, j + 1, a.k_pool, k_st + (st ^ 1) * (kWaves * C::BLOCK), nullptr);
         }
 
         // ---- visibility, online softmax, P = hi + lo -------------------------
@@ -799,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 pl[rb] = ll8;
             }
         }
-        wait_groups(j + 2 < nms ? 3 : (j + 1 < nms ? 2 : 0));   // V(j) landed
+        wait_groups(j + 1 < nms ? 1 : 0);            // V(j); K(j+1) may be in flight
 
         // ---- O^T += V^T P^T over the wave's 32 tokens, all D columns ---------
         if (any) {
@@ -824,8 +827,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][db], 0, 0, 0);
             }
         }
-        if (j + 2 < nms)
-            issue_plane(br2, j + 2, a.v_pool, vst, tok);
+        if (j + 1 < nms)
+            issue_plane(bnext, j + 1, a.v_pool, v_st + (st ^ 1) * (kWaves * C::BLOCK),
+                        &tok_s[w][st ^ 1][0]);
     };
 
     auto main_loop = [&](auto nrb_c) __attribute__((always_inline)) {
@@ -837,11 +841,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         const BlockRef br0 = lookup(0);
         issue_plane(br0, 0, a.k_pool, k_st, nullptr);
         issue_plane(br0, 0, a.v_pool, v_st, &tok_s[w][0][0]);
-        if (nms > 1) {
-            const BlockRef br1 = lookup(1);
-            issue_plane(br1, 1, a.k_pool, k_st + kWaves * C::BLOCK, nullptr);
-            issue_plane(br1, 1, a.v_pool, v_st + kWaves * C::BLOCK, &tok_s[w][1][0]);
-        }
         if (nrb == 1)
             main_loop(std::integral_constant<int, 1>());
         else if (nrb == 2)
@@ -871,10 +870,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     for (int rb = 0; rb < kRowBlocks; ++rb)
         lw[rb] = sum_over_groups(l_part[rb]);
     __syncthreads();   // every wave is done with the stages
+    // per wave and row: running max, accumulator reference and row sum
     if (g == 0) {
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
+        for (int rb = 0; rb < kRowBlocks; ++rb) {
             xm[w][rb * 16 + n] = m_true[rb];
+            xr[w][rb * 16 + n] = m_ref[rb];
+            xl[w][rb * 16 + n] = lw[rb];
+        }
     }
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
@@ -889,22 +892,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     *(f32x4 *)(dstq + ((rb * C::DQ + d) * 64 + lane) * 16) = acc[rb][q * C::DQ + d];
     }
     __syncthreads();
-    float M[kRowBlocks];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-        float mm = xm[0][r];
-#pragma unroll
-        for (int v = 1; v < kWaves; ++v)
-            mm = fmaxf(mm, xm[v][r]);
-        M[rb] = mm;
-        const float f = (m_ref[rb] == -INFINITY) ? 0.0f : exp2f(m_ref[rb] - mm);
-        if (g == 0) {
-            xf[w][r] = f;
-            xl[w][r] = lw[rb] * f;
-        }
-    }
-    __syncthreads();
+    // Every wave derives all four weights 2^(m_ref_v - M) itself, so that one
+    // barrier separates the exchange from its use.
     const int64_t ws_base = (int64_t)split * a.total_rows;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
@@ -913,10 +902,37 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb) {
             const int r = rb * 16 + n;
-            float fv[kWaves];
+            // the three foreign partials of this quarter: all LDS reads first
+            f32x4 xs[kWaves - 1][C::DQ];
+            if (rb < nrb) {
 #pragma unroll
-            for (int v = 0; v < kWaves; ++v)
-                fv[v] = xf[v][r] * kPUnscale;
+                for (int vi = 0; vi < kWaves - 1; ++vi) {
+                    const int v = vi < q ? vi : vi + 1;
+                    const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
+#pragma unroll
+                    for (int d = 0; d < C::DQ; ++d)
+                        xs[vi][d] = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
+                }
+            }
+            float mv[kWaves], rv[kWaves], lv[kWaves];
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                mv[v] = xm[v][r];
+                rv[v] = xr[v][r];
+                lv[v] = xl[v][r];
+            }
+            float M = mv[0];
+#pragma unroll
+            for (int v = 1; v < kWaves; ++v)
+                M = fmaxf(M, mv[v]);
+            float fv[kWaves];
+            float L = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kWaves; ++v) {
+                const float f = (rv[v] == -INFINITY) ? 0.0f : exp2f(rv[v] - M);
+                L += lv[v] * f;
+                fv[v] = f * kPUnscale;
+            }
             const int i = (row0 + r) / G, h = kvh * G + (row0 + r - i * G);
             const int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             float *dst = a.ws_acc + (ws_base + orow) * D;
@@ -926,24 +942,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 if (rb < nrb) {
                     o = acc[rb][q * C::DQ + d] * fv[q];
 #pragma unroll
-                    for (int v = 0; v < kWaves; ++v) {
-                        if (v == q)
-                            continue;
-                        const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
-                        const f32x4 x = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
-                        o += x * fv[v];
-                    }
+                    for (int vi = 0; vi < kWaves - 1; ++vi)
+                        o += xs[vi][d] * fv[vi < q ? vi : vi + 1];
                 }
                 // lane (n, g) of d-block db holds d = 16 db + 4 g + k
                 if (r < R)
                     *(f32x4 *)(dst + 16 * (q * C::DQ + d) + 4 * g) = o;
             }
             if (q == 0 && g == 0 && r < R) {
-                float L = 0.0f;
-#pragma unroll
-                for (int v = 0; v < kWaves; ++v)
-                    L += xl[v][r];
-                a.ws_max[ws_base + orow] = M[rb];
+                a.ws_max[ws_base + orow] = M;
                 a.ws_sum[ws_base + orow] = L * kPUnscale;
             }
         }
