@@ -394,6 +394,41 @@ def read_ceiling(torch, pa, nbytes: int = 2 << 30, reps: int = 5):
     return round(gbs, 1)
 
 
+def read_ceiling_at(torch, pa, nbytes: int, reps: int = 20) -> dict:
+    """The streaming-read probe over nbytes, cold like the verify timing
+    (rotating over enough buffers that one rotation exceeds twice the Infinity
+    Cache), timed from graph replays of GRAPH_CALLS probe launches: the best a
+    plain read kernel does on the same number of bytes."""
+    ncop = copies_for(nbytes)
+    bufs = [torch.zeros(nbytes // 16, 4, dtype=torch.int32, device="cuda:0") for _ in range(ncop)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(GRAPH_CALLS):
+            pa.stream_read_probe(bufs[i % ncop], sink)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(GRAPH_CALLS):
+            pa.stream_read_probe(bufs[i % ncop], sink)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * GRAPH_CALLS)
+    del g, bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def copies_for(pool_bytes: int) -> int:
     """Enough pool copies that one rotation exceeds twice the Infinity Cache."""
     return max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
@@ -536,6 +571,9 @@ def main():
 
     log("[bench] streaming-read ceiling")
     ceiling = read_ceiling(torch, pa)
+    same_size = read_ceiling_at(torch, pa, w.kv_bytes())
+    log(f"[bench] read probe over {w.kv_bytes()} B, cold: {same_size['us']:.2f} us, "
+        f"{same_size['gbs']:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -574,7 +612,9 @@ def main():
                      "traffic": traffic, "kernel": "verify", "verify_us": round(m["verify_us"], 3),
                      "verify_us_median": round(m["verify_med_us"], 3),
                      "read_ceiling": ceiling,
-                     "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None},
+                     "frac_of_read_ceiling": round(achieved / ceiling, 4) if ceiling else None,
+                     "read_probe_same_bytes": same_size,
+                     "frac_of_read_probe_same_bytes": round(same_size["us"] / m["verify_us"], 4)},
         "combine": combines,
         "cache_write": cache_write,
         "cpu_baseline": cpu,
