@@ -454,6 +454,132 @@ def test_graph_replay_changed_lengths(kernel):
         assert not replayed[zero_rows].any()
 
 
+def _capture(fn):
+    """fn captured into a HIP graph after one eager run on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _replays_match_eager(fn, outs, mutate):
+    """Replay the captured fn after each input change, then run fn eagerly on
+    the same buffers: every replay equals the eager result bit for bit."""
+    g = _capture(fn)
+    for k in range(3):
+        mutate(k)
+        for o in outs:                      # what a call leaves untouched stays zero
+            o.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = [o.cpu().clone() for o in outs]
+        for o in outs:
+            o.fill_(0)
+        fn()
+        torch.cuda.synchronize()
+        for r, o in zip(replayed, outs):
+            assert torch.equal(r.view(torch.uint8), o.cpu().view(torch.uint8)), k
+
+
+def test_graph_replay_sparse_and_batch_entries():
+    """Each remaining verify entry, with its combine, is graph-capturable (no
+    host synchronisation, no allocation) and replays with new device lengths."""
+    qb = wl.make_qsa("graph_qsa", 0x62B0, batch=2, q_rows=4, num_heads=12, num_kv_heads=2,
+                     head_dim=128, ctx=1024, page_size=64, topk=5, k_scale=0.5, v_scale=2.0,
+                     num_splits=3)
+    qt = wl.make_qsa_tokens("graph_tok", 0x62B1, batch=2, q_rows=4, num_heads=12,
+                            num_kv_heads=2, head_dim=128, ctx=1024, page_size=64, num_sel=300,
+                            num_empty=4, k_scale=0.5, v_scale=2.0, num_splits=3)
+    wb = BATCHES_GRAPH()
+    announce("graph capture: qsa blocks, qsa tokens, batch")
+    dev = gu.DEV
+    for kind, w in (("blocks", qb), ("tokens", qt), ("batch", wb)):
+        if kind == "batch":
+            q = gu.fp16_tensor(w.q_bits).to(dev)
+        else:
+            q = gu.bf16_tensor(w.q_bits).to(dev)
+        k = torch.from_numpy(w.k_pool).to(dev)
+        v = torch.from_numpy(w.v_pool).to(dev)
+        bt = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
+        lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
+        B, qr, H, D = w.q_bits.shape
+        out = torch.empty((B, qr, H, D), dtype=torch.float16, device=dev)
+        G = H // w.num_kv_heads
+        if kind == "blocks":
+            sel = torch.from_numpy(w.sel_blocks.astype(np.int32)).to(dev)
+            p = pa.plan(w.topk * w.page_size, qr * G, B * w.num_kv_heads, D, splits=3)
+            fn = lambda: pa.qsa_verify(q, k, v, bt, sel, lens, sm_scale=w.sm_scale,
+                                       k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws, out=out)
+        elif kind == "tokens":
+            sel = torch.from_numpy(w.sel_tokens.astype(np.int32)).to(dev)
+            p = pa.plan(w.num_sel, qr * G, B * w.num_kv_heads, D, splits=3)
+            fn = lambda: pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale,
+                                              k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
+                                              out=out)
+        else:
+            p = pa.plan(w.cap, qr * G, B * w.num_kv_heads, D, splits=4)
+            fn = lambda: pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale,
+                                         k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
+                                         out=out)
+        ws = pa.make_workspace(p, B * qr * H, D, dev)
+        base = w.row_lens.astype(np.int64)
+        trials = [base, np.zeros_like(base), np.maximum(base - 700, 0)]
+
+        def mutate(i, lens=lens, trials=trials):
+            lens.copy_(torch.from_numpy(trials[i].astype(np.int32)))
+
+        _replays_match_eager(fn, [out], mutate)
+
+
+def BATCHES_GRAPH():
+    return wl.make_dense_batch("graph_batch", 0x62B2, q_rows=12, num_heads=6, num_kv_heads=1,
+                               head_dim=256, ctxs=[900, 2500, 1700], page_size=256,
+                               sigma=1.0, k_scale=0.5, v_scale=2.0)
+
+
+def test_graph_replay_combine_lse_and_cache_write():
+    """The LSE combine and the cache writer replay from a graph bit for bit."""
+    announce("graph capture: combine with LSE, cache write")
+    dev = gu.DEV
+    S, R, D = 7, 40, 128
+    gen = torch.Generator().manual_seed(0x62B3)
+    acc = torch.randn((S, R, D), generator=gen).to(dev)
+    mx = torch.randn((S, R), generator=gen).to(dev)
+    sm = torch.rand((S, R), generator=gen).to(dev)
+    out16 = torch.empty((R, D), dtype=torch.float16, device=dev)
+    out32 = torch.empty((R, D), dtype=torch.float32, device=dev)
+    lse = torch.empty(R, dtype=torch.float32, device=dev)
+    fn = lambda: pa.paged_attn_combine_fp32_lse((acc, mx, sm), S, R, D, 1.7, out=out16,
+                                                out32=out32, lse=lse)
+
+    def mutate(i):
+        sm[:, i * 5:(i + 1) * 5] = 0.0          # some rows lose splits, one row all of them
+        sm[:, 39] = 0.0
+
+    _replays_match_eager(fn, [out16, out32, lse], mutate)
+
+    T, Hkv, Dh, page = 300, 2, 64, 16
+    kx = torch.randn((T, Hkv, Dh), generator=gen).to(torch.float16).to(dev)
+    vx = torch.randn((T, Hkv, Dh), generator=gen).to(torch.float16).to(dev)
+    slots = torch.randperm(40 * page, generator=gen)[:T].to(torch.int64).to(dev)
+    kp = torch.zeros((40, page, Hkv, Dh), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    fn2 = lambda: pa.paged_attn_cache_write_e4m3(kx, vx, slots, kp, vp, 0.37, 2.25)
+
+    def mutate2(i):
+        kx.mul_(-1.5)
+        slots[i::7] = -1                        # skipped tokens
+
+    _replays_match_eager(fn2, [kp, vp], mutate2)
+
+
 # ---------------------------------------------------------------------------
 # kernel timer
 # ---------------------------------------------------------------------------

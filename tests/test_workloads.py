@@ -1,6 +1,8 @@
 """The seeded input generator: determinism, shapes, and its test-data E4M3
 quantiser against the oracle's independently written encoder."""
 
+import dataclasses
+
 import numpy as np
 
 from fp8_kv_paged_attn_amd import workloads as wl
@@ -69,3 +71,31 @@ def test_qsa_selection_shape():
             s = w.sel_blocks[b, g]
             assert 9 in s and len(set(s.tolist())) == 4
     assert w.kv_bytes() == 3 * 2 * 4 * 64 * 16 * 2
+
+
+def test_token_selection_shape():
+    w = wl.make_qsa_tokens("t", 6, batch=2, q_rows=3, num_heads=4, num_kv_heads=2,
+                           head_dim=16, ctx=300, page_size=32, num_sel=40, num_empty=5,
+                           k_scale=0.5, v_scale=2.0)
+    assert w.sel_tokens.shape == (2, 2, 40) and w.max_blocks == 10
+    for b in range(2):
+        for g in range(2):
+            s = w.sel_tokens[b, g]
+            ids = s[s >= 0]
+            assert (s == -1).sum() == 5 and len(set(ids.tolist())) == 35
+            assert ids.max() < 300 and set(range(297, 300)) <= set(ids.tolist())
+    # every page of every request holds data (no NaN poison)
+    assert not (w.k_pool == 0x7F).all(axis=(1, 2, 3)).any()
+    assert w.kv_bytes() == 2 * 2 * 35 * 16 * 2
+
+
+def test_tokens_from_blocks():
+    q = wl.make_qsa("q", 7, batch=2, q_rows=2, num_heads=4, num_kv_heads=2, head_dim=16,
+                    ctx=256, page_size=16, topk=3, k_scale=0.5, v_scale=2.0)
+    sel = q.sel_blocks.copy()
+    sel[1, 0, 1] = -1
+    q = dataclasses.replace(q, sel_blocks=sel)
+    t = wl.tokens_from_blocks(q)
+    assert t.shape == (2, 2, 48)
+    assert list(t[0, 0, :16]) == list(range(sel[0, 0, 0] * 16, sel[0, 0, 0] * 16 + 16))
+    assert (t[1, 0, 16:32] == -1).all()
