@@ -306,8 +306,11 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     if (requested_splits > 0) {
         splits = requested_splits;
     } else {
-        // one workgroup per compute unit over all units ...
-        splits = (cus + num_kv_units - 1) / num_kv_units;
+        // one workgroup per compute unit over all units, a unit of more than
+        // 48 rows taking one workgroup per 48-row chunk ...
+        const int64_t chunks = ((int64_t)rows_per_kv_unit + 47) / 48;
+        const int64_t wgs = (int64_t)num_kv_units * chunks;
+        splits = (cus + wgs - 1) / wgs;
         // ... but no split shorter than kMinTokensPerSplit tokens
         int64_t cap = ((int64_t)max_tokens + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
         if (cap < 1)
@@ -457,6 +460,7 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.tokens_per_split = plan->tokens_per_split;
     a.total_rows = (int32_t)total_rows;
     a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    a.split_by_length = 1;
     a.ws_acc = ws->acc;
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;

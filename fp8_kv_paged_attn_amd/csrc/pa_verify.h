@@ -39,7 +39,18 @@ struct VerifyArgs {
     int32_t total_rows;         // rows of the workspace = B * q_rows * H
     float logit_scale;          // sm_scale * k_scale * log2(e)
     float *ws_acc, *ws_max, *ws_sum;
+    int32_t split_by_length;    // 1: a unit's splits share its longest row length
+                                // (split_span), 0: split s covers s*T .. s*T + T - 1
 };
+
+// Positions per split of a KV unit whose longest (clamped) row length is lmax,
+// when splits follow the length: ceil(lmax / S) rounded up to the 64-token
+// tile, so never more than the plan's T (S * T covers every length).
+__host__ __device__ inline int split_span(int lmax, int num_splits)
+{
+    const int t = (lmax + num_splits - 1) / num_splits;
+    return t > 0 ? (t + 63) / 64 * 64 : 64;
+}
 
 // Launchers return hipSuccess or the launch error.  Grid = (num_splits, units,
 // row chunks of 48).

@@ -341,8 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         lmine = a.row_lens[(int64_t)b * a.q_rows + lane];
         lmine = lmine < 0 ? 0 : (lmine > a.len_cap ? a.len_cap : lmine);
     }
-    const int lo = split * a.tokens_per_split;
-    const int hi_list = min(lo + a.tokens_per_split, a.list_len);
+    // positions per split: fixed, or (split_by_length) from this unit's
+    // longest row, which costs one more round trip before the table reads
+    int tps = a.tokens_per_split;
+    if (a.split_by_length)
+        tps = split_span(max16_broadcast(lmine), a.num_splits);
+    const int lo = split * tps;
+    const int hi_list = min(lo + tps, a.list_len);
     const int32_t *table = a.block_table + (int64_t)b * a.table_stride;
     int slot0 = 0, nslots = 0;
     if (hi_list > lo) {

@@ -115,8 +115,9 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
     for (int i = 0; i < a.q_rows; ++i)
         lmax = max(lmax, len_s[i]);
 
-    const int lo = split * a.tokens_per_split;
-    int hi = min(lo + a.tokens_per_split, a.list_len);
+    const int tps = a.split_by_length ? split_span(lmax, a.num_splits) : a.tokens_per_split;
+    const int lo = split * tps;
+    int hi = min(lo + tps, a.list_len);
     if (MODE == kModeDense)
         hi = min(hi, lmax);
 

@@ -137,7 +137,9 @@ typedef struct pa_workspace {
  * num_kv_units units of rows_per_kv_unit rows.  num_cus = compute units to
  * fill (<= 0: 256, the MI355X count).  requested_splits > 0 forces the split
  * count (clamped to what the token count allows); 0 picks one: one workgroup
- * per compute unit over all units, but no split shorter than 128 tokens, so
+ * per compute unit over all units (a unit of more than 48 rows counts once per
+ * 48-row chunk, each chunk being a workgroup), but no split shorter than 128
+ * tokens, so
  * that the FP32 partial each split writes stays small against its K/V bytes
  * (the pages tune split counts per device and region, [QSA] sm_120 retune
  * commit).  Returns PA_EINVAL for non-positive sizes. */
@@ -187,6 +189,11 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
  *   plan         (host) from paged_attn_plan(max_blocks_per_req*page_size,
  *                q_rows*num_heads/num_kv_heads, batch*num_kv_heads, head_dim, ...)
  *   rows of the workspace and of the combined output: (b, i, h).
+ * Splits follow each request's own length: with L_b its longest row length
+ * (after the clamp) and S = plan->num_splits, split s of request b covers
+ * tokens [s*T_b, (s+1)*T_b), T_b = ceil(L_b / S) rounded up to a multiple of
+ * 64 (never more than plan->tokens_per_split), so a short request's work is
+ * spread over all S splits instead of leaving most of them empty.
  * Other arguments, masking and errors as for paged_attn_verify_e4m3. */
 int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                      const int32_t *block_table, int32_t max_blocks_per_req,

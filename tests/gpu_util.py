@@ -73,7 +73,7 @@ def run_dense(w, kernel="auto", splits: Optional[int] = None, d: Optional[DenseD
     return res
 
 
-def run_batch(w, kernel="auto", splits: Optional[int] = None):
+def run_batch(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     """A DenseBatchWorkload through paged_attn_verify_batch_e4m3 + combine."""
     q = fp16_tensor(w.q_bits).to(DEV)
     k = torch.from_numpy(w.k_pool).to(DEV)
@@ -84,9 +84,12 @@ def run_batch(w, kernel="auto", splits: Optional[int] = None):
     s = w.num_splits if splits is None else splits
     p = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, splits=s,
                 kernel=kernel)
+    ws = pa.make_workspace(p, w.batch * w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
-                          v_scale=w.v_scale, p=p)
+                          v_scale=w.v_scale, p=p, ws=ws)
     torch.cuda.synchronize()
+    if return_ws:
+        return out.cpu().numpy(), p, tuple(t.cpu().numpy() for t in ws)
     return out.cpu().numpy()
 
 

@@ -52,6 +52,7 @@ def test_abi_and_status(L):
     (131072, 48, 1, 256, 0, 0), (262144, 48, 1, 256, 0, 0), (2048, 48, 32, 128, 0, 0),
     (1, 6, 1, 256, 0, 0), (0, 6, 1, 256, 0, 0), (300, 4, 2, 128, 0, 7), (64, 48, 1, 256, 0, 9),
     (100000, 48, 3, 256, 80, 0), (262144, 48, 1, 256, 0, 100000),
+    (32960, 96, 8, 256, 0, 0), (32960, 49, 8, 256, 0, 0),
 ])
 def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
     p = pa.plan(max_tokens, rows, units, D, num_cus=cus, splits=req)
@@ -65,12 +66,19 @@ def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
         assert S <= min(req, tiles)
     else:
         c = cus if cus > 0 else 256
-        assert S <= max(1, -(-c // units))
+        assert S <= max(1, -(-c // (units * -(-rows // 48))))
         assert S <= max(1, -(-max_tokens // 128))
     assert (p.max_tokens, p.rows_per_kv_unit, p.num_kv_units, p.head_dim) == (max_tokens, rows, units, D)
     assert p.ws_acc_bytes == S * rows * units * D * 4
     assert p.ws_stat_bytes == S * rows * units * 4
     assert p.kernel == 0
+
+
+def test_plan_counts_row_chunks(L):
+    # 8 units of 96 rows = 16 workgroups per split: 16 splits fill 256 CUs
+    assert pa.plan(32960, 96, 8, 256).num_splits == 16
+    # 8 units of 48 rows: 32 splits wanted; 1,088 tokens each cover 32,960 in 31
+    assert pa.plan(32960, 48, 8, 256).num_splits == 31
 
 
 def test_plan_rejects(L):

@@ -722,17 +722,38 @@ def test_batch_small(orc, case, kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_batch_matches_single_requests(kernel):
-    """With equal split boundaries (256 tokens), each request of the batch entry
-    is bit-identical to the single-request entry on that request alone."""
+    """The batch entry splits each request by its own longest row: split s of
+    request b covers [s*T_b, (s+1)*T_b), T_b = ceil(L_b / S) rounded up to 64.
+    Its partials for request b are bit-identical to the single-request
+    entry's with those boundaries (whose further splits are empty)."""
     w = wl.make_dense_batch("bsingle", 0xB51, ctxs=[1000, 300, 770], q_rows=8, num_heads=6,
                             num_kv_heads=1, head_dim=256, page_size=96, sigma=1.0,
                             k_scale=0.5, v_scale=1.5, max_blocks=12)
+    lens = w.row_lens.copy()
+    lens[2] = [770, 700, 0, 3, 770, 500, 769, 1]
+    w = dataclasses.replace(w, row_lens=lens)
+    S = 4
     announce("batch vs single", kernel)
-    got = gu.run_batch(w, kernel, splits=w.cap // 256)
+    _, _, (bacc, bmx, bsm) = gu.run_batch(w, kernel, splits=S, return_ws=True)
+    R = w.q_rows * w.num_heads
     for b in range(w.batch):
+        L = int(np.clip(w.row_lens[b], 0, w.cap).max())
+        T = -(-L // S)
+        T = -(-T // 64) * 64 if T > 0 else 64
         r = dataclasses.replace(w.request(b), max_tokens=w.cap)
-        single = gu.run_dense(r, kernel, splits=w.cap // 256)
-        assert np.array_equal(got[b], single), b
+        d = gu.dense_to_dev(r)
+        p = pa.plan(w.cap, R // w.num_kv_heads, w.num_kv_heads, w.head_dim, kernel=kernel)
+        p.tokens_per_split = T
+        p.num_splits = -(-w.cap // T)
+        ws = pa.make_workspace(p, R, w.head_dim, gu.DEV)
+        pa.paged_attn_verify_e4m3(d.q, d.k, d.v, d.table, d.lens, w.cap, w.sm_scale,
+                                  w.k_scale, p, ws)
+        torch.cuda.synchronize()
+        acc, mx, sm = (t.cpu().numpy() for t in ws)
+        rows = slice(b * R, (b + 1) * R)
+        assert np.array_equal(bacc[:, rows], acc[:S]), b
+        assert np.array_equal(bmx[:, rows], mx[:S]) and np.array_equal(bsm[:, rows], sm[:S]), b
+        assert np.all(mx[S:] == -np.inf) and not sm[S:].any() and not acc[S:].any(), b
 
 
 def test_batch_config(orc):
