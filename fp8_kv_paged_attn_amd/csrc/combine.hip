@@ -19,9 +19,12 @@
 // A thread owns one float4 of columns of one row and a group of its splits
 // (splits g, g + GROUPS, ...).  A workgroup of 256 threads covers 64 columns of
 // 16 / GROUPS rows.  All loads of a batch are issued before any is used (one
-// memory round trip per batch of BATCH splits), and the thread merges its
-// splits online against its own running max.  The GROUPS states of a row's
-// float4 are then merged through LDS in group order.  GROUPS is chosen on the
+// memory round trip per batch of BATCH splits).  The thread takes the batch's
+// largest max first and then weights every split against it, so the
+// exponentials of a batch are independent of each other instead of forming
+// one chain of pairwise merges.  The GROUPS states of a row's float4 are
+// combined the same way through LDS: the row max over the groups, each group
+// rescaled to it, and the rescaled sums added in group order.  GROUPS is chosen on the
 // host so that the grid has about 128 K threads: many splits over few rows
 // (one request, long context) get 16 groups; many rows over few splits (a
 // batch of sparse requests) get 1 or 2.  All arithmetic is FP32.
@@ -42,18 +45,6 @@ constexpr int kLanes = 16;                 // float4 column lanes: 64 columns
 constexpr int kTargetThreads = 131072;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// (m, l, num) <- merge with the state (mo, lo, no); max -inf is the empty state.
-__device__ __forceinline__ void merge_state(float &m, float &l, f32x4 &num, float mo, float lo,
-                                            f32x4 no)
-{
-    const float mn = fmaxf(m, mo);
-    const float a = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
-    const float b = (mo == -INFINITY) ? 0.0f : exp2f(mo - mn);
-    l = l * a + lo * b;
-    num = num * a + no * b;
-    m = mn;
-}
 
 template <int GROUPS, int BATCH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ acc,
@@ -98,25 +89,51 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                     vs[k] = *(const f32x4 *)(acc + i * D + d0);
                 }
             }
+            // the batch's largest max among non-empty splits (empty: l = 0; a
+            // NaN sum is kept), then every split weighted against it at once
+            // (an empty split's numerator is never multiplied, whatever it holds)
+            float bm = m;
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k)
+                bm = ls[k] != 0.0f ? fmaxf(bm, ms[k]) : bm;
+            const float a = (m == -INFINITY) ? 0.0f : exp2f(m - bm);
+            l *= a;
+            num *= a;
 #pragma unroll
             for (int k = 0; k < BATCH; ++k) {
-                if (ls[k] != 0.0f)              // empty: l = 0; a NaN sum is kept
-                    merge_state(m, l, num, ms[k], ls[k], vs[k]);
+                const float wk = (ms[k] == -INFINITY) ? 0.0f : exp2f(ms[k] - bm);
+                if (ls[k] != 0.0f) {
+                    l += wk * ls[k];
+                    num += wk * vs[k];
+                }
             }
+            m = bm;
         }
     }
     if (GROUPS > 1) {
+        // the row's max over the groups, each group rescaled to it, and the
+        // rescaled sums added in group order
+        const int base = rsub * kLanes * GROUPS + lane;
         gm[tid] = m;
-        gl[tid] = l;
-        gn[tid] = num;
+        __syncthreads();
+        float M = gm[base];
+#pragma unroll
+        for (int k = 1; k < GROUPS; ++k)
+            M = fmaxf(M, gm[base + k * kLanes]);
+        const float f = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+        gl[tid] = l * f;
+        gn[tid] = num * f;
         __syncthreads();
         if (grp != 0)
             return;
-        const int base = rsub * kLanes * GROUPS + lane;
+        m = M;
+        l = gl[base];
+        num = gn[base];
 #pragma unroll
-        for (int k = 1; k < GROUPS; ++k)
-            merge_state(m, l, num, gm[base + k * kLanes], gl[base + k * kLanes],
-                        gn[base + k * kLanes]);
+        for (int k = 1; k < GROUPS; ++k) {
+            l += gl[base + k * kLanes];
+            num += gn[base + k * kLanes];
+        }
     }
     if (ok) {
         f32x4 o;
