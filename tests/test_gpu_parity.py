@@ -277,6 +277,85 @@ def test_combine_empty_and_single_split():
     assert np.array_equal(o, exp)
 
 
+def _random_partials(S, R, D, seed):
+    """FP32 split partials with maxima spread over many binades and about a
+    third of the (split, row) pairs empty (m = -inf, l = 0, acc = 0); row 3 is
+    empty in every split."""
+    rng = np.random.default_rng(seed)
+    mx = rng.normal(0.0, 8.0, (S, R)).astype(np.float32)
+    sm = rng.uniform(0.5, 40.0, (S, R)).astype(np.float32)
+    acc = (rng.normal(0.0, 1.0, (S, R, D)) * sm[..., None]).astype(np.float32)
+    empty = rng.random((S, R)) < 0.3
+    empty[:, 3] = True
+    mx[empty] = -np.inf
+    sm[empty] = 0.0
+    acc[empty] = 0.0
+    return acc, mx, sm, empty
+
+
+def _combine(acc, mx, sm, v_scale, lse=False):
+    S, R, D = acc.shape
+    dev = [torch.from_numpy(np.ascontiguousarray(x)).to(gu.DEV) for x in (acc, mx, sm)]
+    out = torch.empty((R, D), dtype=torch.float16, device=gu.DEV)
+    if not lse:
+        pa.paged_attn_combine_fp32(tuple(dev), S, R, D, v_scale, out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+    o32 = torch.empty(R * D, dtype=torch.float32, device=gu.DEV)
+    l32 = torch.empty(R, dtype=torch.float32, device=gu.DEV)
+    pa.paged_attn_combine_fp32_lse(tuple(dev), S, R, D, v_scale, out=out, out32=o32, lse=l32)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), o32.cpu().numpy().reshape(R, D), l32.cpu().numpy()
+
+
+@pytest.mark.parametrize("S", [37, 300, 700])
+def test_combine_many_splits(orc, S):
+    """More splits than one batch per thread (12 rows get 16 split groups, so
+    300 and 700 splits take 2 and 3 batches of 16, 37 one partial batch): the
+    running state is rescaled from batch to batch.  The FP16 output is within
+    1 fp16 ulp of the oracle's FP64 merge of the same FP32 partials, the FP32
+    output and LSE within FP32 rounding, and a row with every split empty gives
+    zeros and LSE -inf.  Garbage (NaN, inf) in the accumulators of empty splits
+    changes no output bit: an empty split's numerator is never used."""
+    R, D, v_scale = 12, 256, 1.7
+    announce("combine many splits", S)
+    acc, mx, sm, empty = _random_partials(S, R, D, 0xC0B1 + S)
+    ref, ref_lse = orc.combine(acc, mx, sm, v_scale, with_lse=True)
+    got16, got32, gl = _combine(acc, mx, sm, v_scale, lse=True)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got16.astype(np.float64) - ref) <= ulp), "combine off by > 1 fp16 ulp"
+    assert np.abs(got32 - ref).max() <= 2e-6 * np.abs(ref).max()
+    live = np.isfinite(ref_lse)
+    assert not live[3] and gl[3] == -np.inf and not got16[3].any() and not got32[3].any()
+    assert np.all(np.abs(gl[live] - ref_lse[live]) <= 2e-6 * np.maximum(1.0, np.abs(ref_lse[live])))
+    dirty = acc.copy()
+    dirty[empty] = np.nan
+    dirty[empty & (np.arange(S)[:, None] % 2 == 0)] = np.inf
+    assert np.array_equal(_combine(dirty, mx, sm, v_scale).view(np.uint16),
+                          got16.view(np.uint16)), "empty-split accumulators leaked"
+
+
+def test_combine_nan_sum_reaches_row():
+    """A split whose sum is NaN is not empty: its row becomes NaN, also when
+    its max is -inf (every score it saw was NaN) and when it is the row's only
+    non-empty split; the other rows are unaffected."""
+    S, R, D = 300, 12, 256
+    announce("combine NaN sums")
+    acc, mx, sm, empty = _random_partials(S, R, D, 0xC0B2)
+    clean = _combine(acc, mx, sm, 1.0)
+    sm2, mx2 = sm.copy(), mx.copy()
+    sm2[7, 5] = np.nan                       # row 5: NaN sum, finite max
+    sm2[:, 6] = 0.0                          # row 6: only split 250, NaN sum, max -inf
+    mx2[:, 6] = -np.inf
+    sm2[250, 6] = np.nan
+    sm2[40, 8], mx2[40, 8] = np.nan, -np.inf  # row 8: NaN sum, max -inf, among live splits
+    got = _combine(acc, mx2, sm2, 1.0)
+    for r in (5, 6, 8):
+        assert np.isnan(got[r].astype(np.float32)).all(), f"row {r} must be NaN"
+    keep = [r for r in range(R) if r not in (5, 6, 8)]
+    assert np.array_equal(got[keep].view(np.uint16), clean[keep].view(np.uint16))
+
+
 # ---------------------------------------------------------------------------
 # index handling: bit-exact
 # ---------------------------------------------------------------------------
