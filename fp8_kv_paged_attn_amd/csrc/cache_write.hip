@@ -8,8 +8,9 @@
 // goes to page slot / page_size, row slot % page_size of both planes.
 //
 // One thread per 16 elements of a token: two 16-byte FP16 loads and one
-// 16-byte store per plane.  The encoder is exact: the quotient is scaled by a power of two so
-// that the code's step is 1, then rounded half to even (v_rndne).
+// 16-byte store per plane.  The quotient is a correctly rounded FP32 division;
+// the hardware FP8 conversion rounds it to nearest even after a clamp to the
+// largest finite code.
 #include "pa_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -21,45 +22,52 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 256 * 8;
 
-// FP32 -> E4M3FN code: nearest, ties to even, saturating; NaN -> 0x7F.
-__device__ __forceinline__ uint32_t e4m3_code(float x)
+// Two FP32 values -> two E4M3FN codes, written into bytes 0-1 (HI false) or 2-3
+// (HI true) of `old`: nearest, ties to even, saturating at +-448.  The values
+// are clamped to [-448, 448] first (so infinities and values past the largest
+// code saturate, as the rounding of a clamped value does) and the hardware
+// conversion rounds to nearest even.  A NaN passes through unclamped and comes
+// out as a NaN code (0xFF); nan_to_7f turns it into 0x7F.
+template <bool HI>
+__device__ __forceinline__ int e4m3_pair(float a, float b, int old)
 {
-    const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
-    const float a = fabsf(x);
-    if (!(a == a))
-        return 0x7Fu;
-    if (a >= 448.0f)                       // also +-inf
-        return sign | 0x7Eu;
-    uint32_t code;
-    if (a < 0.015625f) {
-        // below 2^-6 the codes are m * 2^-9, m = 0..7 (m = 8 is the first normal)
-        code = (uint32_t)rintf(a * 512.0f);
-    } else {
-        // 2^e <= a < 2^(e+1), e = -6..8: a * 2^(3-e) in [8, 16), the code's
-        // mantissa step is 1; rounding up to 16 carries into the exponent
-        const int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu) - 127;
-        const uint32_t m8 = (uint32_t)rintf(ldexpf(a, 3 - e));
-        code = ((uint32_t)(e + 7) << 3) + m8 - 8u;
-    }
-    return sign | code;
+    a = (a == a) ? __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f) : a;
+    b = (b == b) ? __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f) : b;
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-// 16 FP16 values (32 bytes) -> 16 E4M3 codes (16 bytes), each divided by scale.
+// Bytes 0xFF of w become 0x7F.  0xFF is a NaN code and no finite value
+// encodes to it (the most negative finite code is 0xFE), so this only gives
+// every NaN the single code 0x7F.
+__device__ __forceinline__ uint32_t nan_to_7f(uint32_t w)
+{
+    const uint32_t t = ~w;                                        // 0xFF bytes -> 0x00
+    // high bit of each byte of t that is nonzero; the byte sums cannot carry
+    const uint32_t nz = ((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t;
+    return w ^ (~nz & 0x80808080u);
+}
+
+// 16 FP16 values (32 bytes) -> 16 E4M3 codes (16 bytes), each divided by scale
+// with a correctly rounded FP32 division.
 __device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale)
 {
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    float q[16];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint16_t bits = (uint16_t)(w[j] >> (16 * h));
-            const float x = (float)__builtin_bit_cast(_Float16, bits);
-            const uint32_t c = e4m3_code(__fdiv_rn(x, scale));
-            out[j >> 1] |= c << (8 * (2 * (j & 1) + h));
+            q[2 * j + h] = __fdiv_rn((float)__builtin_bit_cast(_Float16, bits), scale);
         }
     }
-    return make_uint4(out[0], out[1], out[2], out[3]);
+    int out[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        out[i] = e4m3_pair<true>(q[4 * i + 2], q[4 * i + 3],
+                                 e4m3_pair<false>(q[4 * i], q[4 * i + 1], 0));
+    return make_uint4(nan_to_7f((uint32_t)out[0]), nan_to_7f((uint32_t)out[1]),
+                      nan_to_7f((uint32_t)out[2]), nan_to_7f((uint32_t)out[3]));
 }
 
 // Thread layout: a token's chunks (num_kv_heads x head_dim/16 of them) are
