@@ -27,7 +27,8 @@ constexpr int kMaxBlocks = 256 * 8;
 // are clamped to [-448, 448] first (so infinities and values past the largest
 // code saturate, as the rounding of a clamped value does) and the hardware
 // conversion rounds to nearest even.  A NaN passes through unclamped and comes
-// out as a NaN code (0xFF); nan_to_7f turns it into 0x7F.
+// out as a NaN code (0xFF on gfx950, whatever its sign); nan_to_7f makes every
+// NaN code 0x7F.
 template <bool HI>
 __device__ __forceinline__ int e4m3_pair(float a, float b, int old)
 {
