@@ -860,7 +860,7 @@ def _write_and_compare(orc, k_bits, v_bits, slots, k0, v0, ks, vs, view=None):
     return kd.cpu().numpy(), vd.cpu().numpy()
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.37, 2.25])
+@pytest.mark.parametrize("scale", [1.0, 0.37, 2.25, 2.0 ** -7, 0.0625, 3.0, 61.0, 1000.0])
 def test_cache_write_every_fp16_value(orc, scale):
     """Every FP16 bit pattern, written with k_scale = scale (and v_scale =
     1/scale), gives the oracle encoder's byte for the FP32 quotient, bit for bit."""
