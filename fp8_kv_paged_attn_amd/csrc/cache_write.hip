@@ -8,8 +8,9 @@
 // goes to page slot / page_size, row slot % page_size of both planes.
 //
 // One thread per 16 elements of a token: two 16-byte FP16 loads and one
-// 16-byte store per plane.  The quotient is a correctly rounded FP32 division;
-// the hardware FP8 conversion rounds it to nearest even after a clamp to the
+// 16-byte store per plane.  The quotient is the correctly rounded FP32
+// division, formed from the scale's reciprocal with one FMA correction; the
+// hardware FP8 conversion rounds it to nearest even after a clamp to the
 // largest finite code.
 #include "pa_internal.h"
 
@@ -48,9 +49,26 @@ __device__ __forceinline__ uint32_t nan_to_7f(uint32_t w)
     return w ^ (~nz & 0x80808080u);
 }
 
-// 16 FP16 values (32 bytes) -> 16 E4M3 codes (16 bytes), each divided by scale
-// with a correctly rounded FP32 division.
-__device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale)
+// The correctly rounded FP32 quotient a / b from y = RN(1/b) (Markstein's
+// correction): q = RN(a y) lies within an ulp of a / b, r = a - q b is exact
+// with an FMA, and RN(q + r y) = RN(a / b) when nothing under- or overflows.
+// Used for FP16 a and b in [2^-110, 2^126], where a y cannot overflow; a
+// quotient small enough to underflow lies far below the smallest E4M3 code,
+// and the copysign keeps its sign (and that of a zero).  Infinite and NaN a
+// take q = a y.
+__device__ __forceinline__ float div_by(float a, float b, float y)
+{
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, b, a);
+    const float c = __builtin_copysignf(__builtin_fmaf(r, y, q), a);
+    return __builtin_isfinite(a) ? c : q;
+}
+
+// 16 FP16 values (32 bytes) -> 16 E4M3 codes (16 bytes), each divided by scale:
+// with div_by (FAST, y = RN(1 / scale)) or the library's correctly rounded
+// division.
+template <bool FAST>
+__device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale, float y)
 {
     const uint32_t w[8] = {in0.x, in0.y, in0.z, in0.w, in1.x, in1.y, in1.z, in1.w};
     float q[16];
@@ -59,7 +77,8 @@ __device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint16_t bits = (uint16_t)(w[j] >> (16 * h));
-            q[2 * j + h] = __fdiv_rn((float)__builtin_bit_cast(_Float16, bits), scale);
+            const float x = (float)__builtin_bit_cast(_Float16, bits);
+            q[2 * j + h] = FAST ? div_by(x, scale, y) : __fdiv_rn(x, scale);
         }
     }
     int out[4];
@@ -74,6 +93,7 @@ __device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale)
 // Thread layout: a token's chunks (num_kv_heads x head_dim/16 of them) are
 // consecutive threads; a workgroup covers 256 / chunks tokens per iteration
 // (chunks <= 256), and loops over chunks itself when a token has more.
+template <bool FAST>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, int64_t num_tokens,
     int num_kv_heads, int head_dim, const int64_t *__restrict__ slots, uint8_t *__restrict__ kp,
@@ -88,6 +108,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     const int cstep = chunks <= kThreads ? chunks : kThreads;
     if (tt >= tpw)
         return;
+    const float ky = FAST ? __fdiv_rn(1.0f, k_scale) : 0.0f;
+    const float vy = FAST ? __fdiv_rn(1.0f, v_scale) : 0.0f;
     for (int64_t t = (int64_t)blockIdx.x * tpw + tt; t < num_tokens; t += (int64_t)gridDim.x * tpw) {
         const int64_t slot = slots[t];
         if (slot < 0 || slot >= num_slots)
@@ -101,8 +123,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
             const uint4 *vs = (const uint4 *)(v + src);
             const uint4 k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
             const int64_t dst = base + g * head_stride + e;
-            *(uint4 *)(kp + dst) = encode16(k0, k1, k_scale);
-            *(uint4 *)(vp + dst) = encode16(v0, v1, v_scale);
+            *(uint4 *)(kp + dst) = encode16<FAST>(k0, k1, k_scale, ky);
+            *(uint4 *)(vp + dst) = encode16<FAST>(v0, v1, v_scale, vy);
         }
     }
 }
@@ -122,9 +144,18 @@ hipError_t launch_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_
     int64_t blocks = (num_tokens + tpw - 1) / tpw;
     if (blocks > kMaxBlocks)
         blocks = kMaxBlocks;
-    hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, k, v,
-                       num_tokens, num_kv_heads, head_dim, slots, kp, vp, page_stride,
-                       token_stride, head_stride, page_size, num_slots, k_scale, v_scale);
+    // the reciprocal-based division where both scales keep it exact
+    const auto in_range = [](float s) { return s >= 0x1p-110f && s <= 0x1p126f; };
+    if (in_range(k_scale) && in_range(v_scale))
+        hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, k, v, num_tokens, num_kv_heads, head_dim, slots, kp, vp,
+                           page_stride, token_stride, head_stride, page_size, num_slots, k_scale,
+                           v_scale);
+    else
+        hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                           stream, k, v, num_tokens, num_kv_heads, head_dim, slots, kp, vp,
+                           page_stride, token_stride, head_stride, page_size, num_slots, k_scale,
+                           v_scale);
     return hipGetLastError();
 }
 

@@ -860,10 +860,13 @@ def _write_and_compare(orc, k_bits, v_bits, slots, k0, v0, ks, vs, view=None):
     return kd.cpu().numpy(), vd.cpu().numpy()
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.37, 2.25, 2.0 ** -7, 0.0625, 3.0, 61.0, 1000.0])
+@pytest.mark.parametrize("scale", [1.0, 0.37, 2.25, 2.0 ** -7, 0.0625, 3.0, 61.0, 1000.0,
+                                   2.0 ** -120, 2.0 ** 125])
 def test_cache_write_every_fp16_value(orc, scale):
     """Every FP16 bit pattern, written with k_scale = scale (and v_scale =
-    1/scale), gives the oracle encoder's byte for the FP32 quotient, bit for bit."""
+    1/scale), gives the oracle encoder's byte for the FP32 quotient, bit for bit.
+    The last two scales put one of the pair outside [2^-110, 2^126], where the
+    writer divides without the reciprocal."""
     announce("cache write all fp16", scale)
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(4096, 1, 16)
     T, P, ps = 4096, 256, 16                 # 16-byte token rows: the pool's stride rule
