@@ -24,10 +24,10 @@
 // exponentials of a batch are independent of each other instead of forming
 // one chain of pairwise merges.  The GROUPS states of a row's float4 are
 // combined the same way through LDS: the row max over the groups, each group
-// rescaled to it, and the rescaled sums added in group order.  GROUPS is chosen on the
-// host so that the grid has about 128 K threads: many splits over few rows
-// (one request, long context) get 16 groups; many rows over few splits (a
-// batch of sparse requests) get 1 or 2.  All arithmetic is FP32.
+// rescaled to it, and the rescaled sums added in group order.  GROUPS is
+// chosen on the host so that the grid has about 128 K threads: many splits
+// over few rows (one request, long context) get 16 groups; many rows over few
+// splits (a batch of sparse requests) get 1 or 2.  All arithmetic is FP32.
 //
 // The same kernel can also write the unrounded FP32 output and the base-2 LSE
 // of each row, M + log2(sum_s w_s l_s), for a merge across ranks (1Cat-vLLM PR
