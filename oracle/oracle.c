@@ -667,7 +667,7 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
         double M = -INFINITY, den = 0.0;
         for (int s = 0; s < S; ++s) {
             int64_t k = (int64_t)s * R + r;
-            double l = sm64 ? sm64[k] : (double)sm32[k];
+            double l = sm64 ? sm64[k] : (double)(ORC_MUTANT == 17 ? mx32[k] : sm32[k]);
             double m = mx64 ? mx64[k] : (double)mx32[k];
             if (l != 0.0 && m > M)
                 M = m;
@@ -676,7 +676,7 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
             out[(int64_t)r * D + d] = 0.0;
         for (int s = 0; s < S; ++s) {
             int64_t k = (int64_t)s * R + r;
-            double l = sm64 ? sm64[k] : (double)sm32[k];
+            double l = sm64 ? sm64[k] : (double)(ORC_MUTANT == 17 ? mx32[k] : sm32[k]);
             double m = mx64 ? mx64[k] : (double)mx32[k];
             double w;
             if (l == 0.0)              /* empty split; a NaN sum is not empty */
@@ -685,7 +685,8 @@ static int combine_any(const double *acc64, const float *acc32, const double *mx
             den += w * l;
             for (int d = 0; d < D; ++d) {
                 int64_t a = k * D + d;
-                out[(int64_t)r * D + d] += w * (acc64 ? acc64[a] : (double)acc32[a]);
+                int64_t a32 = (ORC_MUTANT == 18) ? (int64_t)r * D + d : a;
+                out[(int64_t)r * D + d] += w * (acc64 ? acc64[a] : (double)acc32[a32]);
             }
         }
         for (int d = 0; d < D; ++d)

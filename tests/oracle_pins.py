@@ -564,6 +564,63 @@ def pin_combine_lse(o):
         assert_close_rel(ml[live], lse[live], 1e-12, f"merged lse, cut {cut}")
 
 
+def _f32_partials_with_specials(seed: int, S: int, R: int, D: int):
+    """FP32 split partials as a verify kernel writes them, plus the cases a
+    combine must handle: empty splits (sum 0) whose max and numerator hold
+    garbage (-inf, NaN, inf), a NaN sum with a -inf max, a NaN in a numerator
+    of a non-empty split, and rows whose every split is empty."""
+    rng = np.random.default_rng(seed)
+    mx = rng.normal(0.0, 6.0, (S, R)).astype(np.float32)
+    sm = rng.uniform(0.5, 40.0, (S, R)).astype(np.float32)
+    acc = (rng.normal(0.0, 3.0, (S, R, D)) * sm[:, :, None]).astype(np.float32)
+    empty = rng.random((S, R)) < 0.2
+    sm[empty] = 0.0
+    mx[empty] = rng.choice(np.array([-np.inf, np.nan, np.inf, 7.0], np.float32), empty.sum())
+    acc[empty] = np.nan
+    sm[:, 0] = 0.0                                   # row 0: every split empty
+    mx[:, 0] = -np.inf
+    sm[1, 1], mx[1, 1] = np.nan, -np.inf             # NaN sum reaches row 1
+    sm[2, 2] = 3.0
+    acc[2, 2, 3] = np.nan                            # NaN numerator, column 3 of row 2
+    return acc, mx, sm
+
+
+def pin_combine_f32(o):
+    """The combine of FP32 partials (the form a GPU workspace holds, used to
+    check the combine kernel) equals, bit for bit, the combine of the same
+    values converted to FP64, which the other pins tie to the one-pass
+    definition and to logsumexp: with and without the LSE, on real split
+    partials rounded to FP32 and on random partials with empty splits full of
+    garbage, NaN sums and NaN numerators.  Real partials rounded to FP32 also
+    combine to the one-pass FP64 output within FP32 rounding."""
+    w = _dense_case(1)                               # lengths 0, 23, 50
+    one = o.dense_workload(w)
+    acc, mx, sm = o.verify_dense_split(w.q_bits, w.k_pool, w.v_pool, w.block_table,
+                                       w.row_lens, w.max_tokens, w.num_kv_heads,
+                                       w.sm_scale, w.k_scale, 7, 8)
+    cases = [tuple(x.astype(np.float32) for x in (acc, mx, sm)),
+             _f32_partials_with_specials(0xC0B32, 37, 12, 16)]
+    for n, (a32, m32, s32) in enumerate(cases):
+        a64, m64, s64 = (x.astype(np.float64) for x in (a32, m32, s32))
+        for vs in (1.0, 2.25):
+            got = o.combine(a32, m32, s32, vs)
+            ref = o.combine(a64, m64, s64, vs)
+            assert np.array_equal(got, ref, equal_nan=True), f"fp32 combine, case {n}"
+            go, gl = o.combine(a32, m32, s32, vs, with_lse=True)
+            ro, rl = o.combine(a64, m64, s64, vs, with_lse=True)
+            assert np.array_equal(go, ref, equal_nan=True), f"fp32 lse combine out, case {n}"
+            assert np.array_equal(gl, rl, equal_nan=True), f"fp32 lse, case {n}"
+    a32, m32, s32 = cases[0]
+    got = o.combine(a32, m32, s32, w.v_scale).reshape(one.shape)
+    assert_close_rel(got, one, 4e-7, "fp32 partials against the one-pass output")
+    a32, m32, s32 = cases[1]
+    got = o.combine(a32, m32, s32, 1.0)
+    assert not got[0].any(), "row with every split empty"
+    assert np.isnan(got[1]).all(), "NaN sum reaches its row"
+    assert np.isnan(got[2, 3]) and np.isfinite(np.delete(got[2], 3)).all(), "NaN numerator"
+    assert np.isfinite(got[3:]).all(), "garbage in empty splits leaked"
+
+
 def pin_cache_write(o):
     """The cache write puts E4M3(fp32(x) / fp32(scale)) at each slot's bytes and
     touches nothing else: PyTorch's float8_e4m3fn cast of the same FP32 quotient
@@ -684,6 +741,6 @@ ALL_PINS = [
     pin_e4m3_golden, pin_e4m3_structure, pin_e4m3_vs_torch, pin_encoder_roundtrip,
     pin_encoder_vs_torch, pin_one_hot_probe, pin_closed_forms, pin_relocation,
     pin_nan_poison, pin_dense_vs_sdpa, pin_qsa_vs_sdpa, pin_split_combine, pin_visible_nan,
-    pin_combine_lse, pin_cache_write, pin_qsa_tokens,
+    pin_combine_lse, pin_combine_f32, pin_cache_write, pin_qsa_tokens,
     pin_selection_order, pin_fp16_decode, pin_bf16_decode,
 ]

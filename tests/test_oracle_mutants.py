@@ -4,7 +4,9 @@ dropped k_scale or v_scale, an off-by-one visibility bound, a sign error in
 the softmax exponent, a transposed query index, the block table ignored, a
 shifted split boundary, a missing combine weight, wrong subnormal or exponent
 bias in the E4M3 decode, ties rounded to odd, the selection ignored, and the
-sparse visibility bound taken on list positions instead of tokens.  Each
+sparse visibility bound taken on list positions instead of tokens, and in
+the combine of FP32 partials the max read as the sum or the split index
+dropped from the numerator.  Each
 build runs in its own process, so a crash also counts as caught."""
 
 import os
@@ -16,7 +18,7 @@ import pytest
 from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-MUTANTS = list(range(1, 17))
+MUTANTS = list(range(1, 19))
 
 _RUNNER = r"""
 import sys, traceback
