@@ -82,8 +82,8 @@ class DenseBench:
         self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
         G = w.num_heads // w.num_kv_heads
         s = splits if splits else w.num_splits
-        self.plan = pa.plan(w.max_tokens, w.q_rows * G, w.num_kv_heads, w.head_dim, splits=s,
-                            kernel=kernel)
+        self.plan = pa.plan(w.max_tokens, w.q_rows * G, w.num_kv_heads, w.head_dim, w.page_size,
+                            splits=s, kernel=kernel)
         self.rows = w.q_rows * w.num_heads
         self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
         self.out = torch.empty((w.q_rows, w.num_heads, w.head_dim), dtype=torch.float16,
@@ -230,9 +230,9 @@ class QsaBench(DenseBench):
     """The sparse (QSA) batch resident on the device, with n_copies of its pool."""
 
     def __init__(self, w, n_copies: int, kernel: str):
-        self._setup(w, n_copies, w.sel_blocks, w.topk * w.page_size, kernel)
+        self._setup(w, n_copies, w.sel_blocks, w.topk * w.page_size, "blocks", kernel)
 
-    def _setup(self, w, n_copies: int, sel, list_len: int, kernel: str):
+    def _setup(self, w, n_copies: int, sel, list_len: int, selection: str, kernel: str):
         import numpy as np
         import torch
 
@@ -250,7 +250,7 @@ class QsaBench(DenseBench):
         self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
         G = w.num_heads // w.num_kv_heads
         self.plan = pa.plan(list_len, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
-                            splits=w.num_splits, kernel=kernel)
+                            w.page_size, selection, splits=w.num_splits, kernel=kernel)
         self.rows = w.num_rows
         self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
         self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),
@@ -268,7 +268,7 @@ class QsaTokensBench(QsaBench):
     """The sparse batch over selected token ids, resident on the device."""
 
     def __init__(self, w, n_copies: int, kernel: str):
-        self._setup(w, n_copies, w.sel_tokens, w.num_sel, kernel)
+        self._setup(w, n_copies, w.sel_tokens, w.num_sel, "tokens", kernel)
 
     def verify(self, i: int):
         k, v = self.pools[i % len(self.pools)]
@@ -322,7 +322,7 @@ class BatchBench(DenseBench):
         self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
         G = w.num_heads // w.num_kv_heads
         self.plan = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
-                            splits=w.num_splits, kernel=kernel)
+                            w.page_size, splits=w.num_splits, kernel=kernel)
         self.rows = w.num_rows
         self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
         self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),

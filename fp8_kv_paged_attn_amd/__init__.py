@@ -25,10 +25,10 @@ from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpaged_attn_e4m3.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 PA_KERNEL = {"auto": 0, "simple": 1, "mfma": 2}
-LOG2E = 1.4426950408889634
+PA_SELECTION = {"dense": 0, "blocks": 1, "tokens": 2}
 
 
 class PaKvPool(ctypes.Structure):
@@ -42,7 +42,8 @@ class PaPlan(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("tokens_per_split", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("rows_per_kv_unit", ctypes.c_int32), ("num_kv_units", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("ws_acc_bytes", ctypes.c_int64),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("selection", ctypes.c_int32), ("ws_acc_bytes", ctypes.c_int64),
                 ("ws_stat_bytes", ctypes.c_int64)]
 
     def __repr__(self):
@@ -56,7 +57,8 @@ class PaWorkspace(ctypes.Structure):
                 ("acc_bytes", ctypes.c_int64), ("stat_bytes", ctypes.c_int64)]
 
 
-EXPORTS = ("paged_attn_abi_version", "paged_attn_status_string", "paged_attn_plan",
+EXPORTS = ("paged_attn_abi_version", "paged_attn_build_id", "paged_attn_status_string",
+           "paged_attn_plan",
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
            "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
@@ -66,7 +68,8 @@ _LIB = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it was not built or has another ABI revision."""
+    """The loaded library; raises if it was not built, has another ABI revision,
+    or was built from sources other than the ones beside this module."""
     global _LIB
     if _LIB is not None:
         return _LIB
@@ -77,9 +80,11 @@ def lib() -> ctypes.CDLL:
     i32, i64, p, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     L.paged_attn_abi_version.argtypes = []
     L.paged_attn_abi_version.restype = i32
+    L.paged_attn_build_id.argtypes = []
+    L.paged_attn_build_id.restype = ctypes.c_char_p
     L.paged_attn_status_string.argtypes = [i32]
     L.paged_attn_status_string.restype = ctypes.c_char_p
-    L.paged_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PaPlan)]
+    L.paged_attn_plan.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(PaPlan)]
     L.paged_attn_plan.restype = i32
     L.paged_attn_verify_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, i32, i32,
                                          i32, i32, f32, f32, ctypes.POINTER(PaPlan),
@@ -113,8 +118,19 @@ def lib() -> ctypes.CDLL:
     if ver != ABI_VERSION:
         raise RuntimeError(f"libpaged_attn_e4m3 ABI revision {ver}, this binding needs "
                            f"{ABI_VERSION}: rebuild the library")
+    from . import build as _build
+
+    built, here = L.paged_attn_build_id().decode(), _build.source_hash()
+    if built != here:
+        raise RuntimeError(f"libpaged_attn_e4m3 was built from other sources (build id {built}, "
+                           f"sources here {here}): rebuild the library")
     _LIB = L
     return L
+
+
+def build_id() -> str:
+    """Source hash compiled into the loaded library."""
+    return lib().paged_attn_build_id().decode()
 
 
 TIMER_MAX_LAUNCHES = 1024
@@ -155,11 +171,14 @@ def _check(rc: int, what: str) -> None:
 
 
 def plan(max_tokens: int, rows_per_kv_unit: int, num_kv_units: int, head_dim: int,
-         num_cus: int = 0, splits: int = 0, kernel: str = "auto") -> PaPlan:
-    """Split plan (pure host integer arithmetic in the library)."""
+         page_size: int, selection: str = "dense", num_cus: int = 0, splits: int = 0,
+         kernel: str = "auto") -> PaPlan:
+    """Split plan (host integer arithmetic in the library; num_cus = 0 takes the
+    current device's compute-unit count)."""
     out = PaPlan()
     _check(lib().paged_attn_plan(int(max_tokens), int(rows_per_kv_unit), int(num_kv_units),
-                                 int(head_dim), int(num_cus), int(splits), ctypes.byref(out)),
+                                 int(head_dim), int(page_size), PA_SELECTION[selection],
+                                 int(num_cus), int(splits), ctypes.byref(out)),
            "paged_attn_plan")
     out.kernel = PA_KERNEL[kernel]
     return out
@@ -176,16 +195,20 @@ def _torch():
     return torch
 
 
-def _scale(x, device, name: str) -> float:
-    """Scales are host scalars.  A one-element tensor is accepted only on the
-    query's device (vLLM PR "Qwen4Exp: fp8_e4m3 main KV cache on the QSA path",
-    CodeRabbit finding) and is read once on the host."""
+def _scale(x, name: str) -> float:
+    """Scales are host scalars: k_scale is folded into the logit scale on the
+    host and v_scale passed by value (vLLM PR "Qwen4Exp: fp8_e4m3 main KV cache
+    on the QSA path", review thread on host-side KV scales), so reading a
+    device tensor would cost a synchronisation and break graph capture.  A
+    Python number or a one-element CPU tensor is accepted; a tensor on any
+    other device is refused before anything is enqueued."""
     torch = _torch()
     if isinstance(x, torch.Tensor):
+        if x.device.type != "cpu":
+            raise ValueError(f"{name} must be a host scalar (a float or a CPU tensor), "
+                             f"not a tensor on {x.device}: the library takes scales by value")
         if x.numel() != 1:
             raise ValueError(f"{name} must have one element")
-        if x.device != device:
-            raise ValueError(f"{name} is on {x.device}, the query is on {device}")
         x = x.item()
     x = float(x)
     if not math.isfinite(x):
@@ -250,7 +273,7 @@ def paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens:
     rc = lib().paged_attn_verify_e4m3(
         q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
         block_table.numel(), _i32(row_lens, "row_lens", dev), int(max_tokens), qr, H,
-        k_pool.shape[2], D, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        k_pool.shape[2], D, _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"),
         ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "paged_attn_verify_e4m3")
 
@@ -274,7 +297,7 @@ def paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_sc
     rc = lib().paged_attn_verify_batch_e4m3(
         q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
         block_table.shape[1], _i32(row_lens, "row_lens", dev), B, qr, H, Hkv, D,
-        _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"), ctypes.byref(p),
+        _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"), ctypes.byref(p),
         ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "paged_attn_verify_batch_e4m3")
 
@@ -299,8 +322,8 @@ def paged_attn_cache_write_e4m3(k, v, slot_mapping, k_pool, v_pool, k_scale, v_s
     pool = _pool(k_pool, v_pool, dev)
     rc = lib().paged_attn_cache_write_e4m3(k.data_ptr(), v.data_ptr(), T, Hkv, D,
                                            slot_mapping.data_ptr(), ctypes.byref(pool),
-                                           _scale(k_scale, dev, "k_scale"),
-                                           _scale(v_scale, dev, "v_scale"), _stream(dev))
+                                           _scale(k_scale, "k_scale"),
+                                           _scale(v_scale, "v_scale"), _stream(dev))
     _check(rc, "paged_attn_cache_write_e4m3")
 
 
@@ -318,7 +341,7 @@ def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, o
         raise ValueError("workspace smaller than num_splits x num_rows")
     rc = lib().paged_attn_combine_fp32(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
                                        int(num_splits), int(num_rows), int(head_dim),
-                                       _scale(out_scale, out.device, "out_scale"),
+                                       _scale(out_scale, "out_scale"),
                                        out.data_ptr(), _stream(out.device))
     _check(rc, "paged_attn_combine_fp32")
 
@@ -346,7 +369,7 @@ def paged_attn_combine_fp32_lse(ws, num_splits: int, num_rows: int, head_dim: in
     ptr = lambda t: None if t is None else t.data_ptr()
     rc = lib().paged_attn_combine_fp32_lse(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
                                            int(num_splits), int(num_rows), int(head_dim),
-                                           _scale(out_scale, dev, "out_scale"), ptr(out),
+                                           _scale(out_scale, "out_scale"), ptr(out),
                                            ptr(out32), ptr(lse), _stream(dev))
     _check(rc, "paged_attn_combine_fp32_lse")
 
@@ -378,7 +401,7 @@ def qsa_sparse_verify_e4m3(q, k_pool, v_pool, block_table, sel_blocks, row_lens,
     args, dev = _sparse_args(q, k_pool, v_pool, block_table, sel_blocks, row_lens,
                              "sel_blocks")
     rc = lib().qsa_sparse_verify_e4m3(
-        *args, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        *args, _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"),
         ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "qsa_sparse_verify_e4m3")
 
@@ -390,7 +413,7 @@ def qsa_sparse_verify_tokens_e4m3(q, k_pool, v_pool, block_table, sel_tokens, ro
     args, dev = _sparse_args(q, k_pool, v_pool, block_table, sel_tokens, row_lens,
                              "sel_tokens")
     rc = lib().qsa_sparse_verify_tokens_e4m3(
-        *args, _scale(sm_scale, dev, "sm_scale"), _scale(k_scale, dev, "k_scale"),
+        *args, _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"),
         ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "qsa_sparse_verify_tokens_e4m3")
 
@@ -408,7 +431,8 @@ def verify(q, k_pool, v_pool, block_table, row_lens, max_tokens: int, *, sm_scal
     qr, H, D = q.shape
     Hkv = k_pool.shape[2]
     if p is None:
-        p = plan(max_tokens, qr * (H // Hkv), Hkv, D, splits=splits, kernel=kernel)
+        p = plan(max_tokens, qr * (H // Hkv), Hkv, D, k_pool.shape[1], splits=splits,
+                 kernel=kernel)
     if ws is None:
         ws = make_workspace(p, qr * H, D, q.device)
     if out is None:
@@ -428,7 +452,8 @@ def verify_batch(q, k_pool, v_pool, block_table, row_lens, *, sm_scale, k_scale,
     Hkv = k_pool.shape[2]
     cap = block_table.shape[1] * k_pool.shape[1]
     if p is None:
-        p = plan(cap, qr * (H // Hkv), B * Hkv, D, splits=splits, kernel=kernel)
+        p = plan(cap, qr * (H // Hkv), B * Hkv, D, k_pool.shape[1], splits=splits,
+                 kernel=kernel)
     if ws is None:
         ws = make_workspace(p, B * qr * H, D, q.device)
     if out is None:
@@ -448,8 +473,8 @@ def qsa_verify(q, k_pool, v_pool, block_table, sel_blocks, row_lens, *, sm_scale
     Hkv = k_pool.shape[2]
     page = k_pool.shape[1]
     if p is None:
-        p = plan(sel_blocks.shape[2] * page, qr * (H // Hkv), B * Hkv, D, splits=splits,
-                 kernel=kernel)
+        p = plan(sel_blocks.shape[2] * page, qr * (H // Hkv), B * Hkv, D, page, "blocks",
+                 splits=splits, kernel=kernel)
     if ws is None:
         ws = make_workspace(p, B * qr * H, D, q.device)
     if out is None:
@@ -469,7 +494,8 @@ def qsa_verify_tokens(q, k_pool, v_pool, block_table, sel_tokens, row_lens, *, s
     B, qr, H, D = q.shape
     Hkv = k_pool.shape[2]
     if p is None:
-        p = plan(sel_tokens.shape[2], qr * (H // Hkv), B * Hkv, D, splits=splits, kernel=kernel)
+        p = plan(sel_tokens.shape[2], qr * (H // Hkv), B * Hkv, D, k_pool.shape[1], "tokens",
+                 splits=splits, kernel=kernel)
     if ws is None:
         ws = make_workspace(p, B * qr * H, D, q.device)
     if out is None:

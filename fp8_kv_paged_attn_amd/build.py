@@ -7,6 +7,7 @@ All HIP code is compiled with packed-FP32 instruction generation disabled
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -31,6 +32,23 @@ CODEGEN_FLAGS = [
 
 # sources whose kernels issue direct-to-LDS loads as inline asm
 ASM_DMA_SOURCES = ["verify_mfma.hip"]
+
+
+def source_files():
+    """Every file the library is compiled from, in a fixed order."""
+    return (sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+            + [os.path.join(ROOT, "include", "paged_attn_e4m3.h")])
+
+
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over the library's sources and its
+    code-generation flags; compiled into the library as its build id."""
+    h = hashlib.sha256()
+    for path in source_files():
+        with open(path, "rb") as f:
+            h.update(os.path.relpath(path, ROOT).encode() + b"\0" + f.read() + b"\0")
+    h.update(" ".join(CODEGEN_FLAGS).encode())
+    return h.hexdigest()[:16]
 
 
 def check_hazards(extra_flags=()) -> None:
@@ -62,7 +80,7 @@ def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = out + ".tmp"
     cmd = [hipcc(), *CODEGEN_FLAGS, "-fPIC", "-shared",
-           "-Wall", "-Werror", "-Wno-unused-function",
+           "-Wall", "-Werror", "-Wno-unused-function", f'-DPA_BUILD_ID="{source_hash()}"',
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra_flags, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

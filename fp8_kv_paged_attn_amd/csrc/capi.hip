@@ -11,9 +11,14 @@
 #include "pa_internal.h"
 
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <mutex>
+
+#ifndef PA_BUILD_ID
+#error "PA_BUILD_ID (the source hash) is defined by the build"
+#endif
 
 namespace {
 
@@ -28,13 +33,35 @@ constexpr int kDefaultCUs = 256;
 // Fewest tokens a split should read, so that the FP32 partial it writes
 // (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.
 constexpr int kMinTokensPerSplit = 128;
-constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned16(int64_t v) { return (v & 15) == 0; }
 
 // Per-device record: 0 unknown, 1 gfx950, -1 something else.
 std::atomic<int> g_device_ok[64];
+// Per-device compute-unit count: 0 unknown.
+std::atomic<int> g_device_cus[64];
+
+// Compute units of the current device, queried once per device; kDefaultCUs
+// when no device can be queried (a host without a GPU).
+int device_cus()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return kDefaultCUs;
+    if (dev < 64) {
+        const int known = g_device_cus[dev].load(std::memory_order_relaxed);
+        if (known > 0)
+            return known;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        return kDefaultCUs;
+    if (dev < 64)
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 int32_t check_device()
 {
@@ -98,20 +125,33 @@ int32_t check_scales(float sm_scale, float k_scale)
     return PA_OK;
 }
 
+// A plan fits a call when it was made for the call's sizes, page size and
+// selection, its splits cover the list without a split wholly past it and
+// without 32-bit overflow of a split's bounds, and -- for the MFMA kernel --
+// every split's page slots fit that kernel's LDS slot cache.
 int32_t check_plan(const pa_plan *plan, int32_t list_len, int32_t rows_per_unit,
-                   int32_t units, int32_t head_dim)
+                   int32_t units, int32_t head_dim, int32_t page_size, int32_t selection)
 {
     if (!plan)
         return PA_EINVAL;
     if (plan->max_tokens != list_len || plan->rows_per_kv_unit != rows_per_unit ||
-        plan->num_kv_units != units || plan->head_dim != head_dim)
+        plan->num_kv_units != units || plan->head_dim != head_dim ||
+        plan->page_size != page_size || plan->selection != selection)
         return PA_EPLAN;
     if (plan->num_splits < 1 || plan->tokens_per_split < kTileTokens ||
         plan->tokens_per_split % kTileTokens != 0 || plan->num_splits > 65535)
         return PA_EPLAN;
-    if ((int64_t)plan->num_splits * plan->tokens_per_split < (int64_t)list_len)
+    const int64_t span = (int64_t)plan->num_splits * plan->tokens_per_split;
+    if (span < (int64_t)list_len || span > INT32_MAX)
+        return PA_EPLAN;
+    if ((int64_t)(plan->num_splits - 1) * plan->tokens_per_split >=
+        (int64_t)(list_len > 1 ? list_len : 1))
         return PA_EPLAN;
     if (plan->kernel < PA_KERNEL_AUTO || plan->kernel > PA_KERNEL_MFMA)
+        return PA_EPLAN;
+    if (plan->kernel != PA_KERNEL_SIMPLE &&
+        pa::mfma_slots_needed(plan->tokens_per_split, page_size, selection == PA_SEL_TOKENS) >
+            pa::mfma_max_slots(head_dim))
         return PA_EPLAN;
     return PA_OK;
 }
@@ -184,20 +224,14 @@ int32_t dispatch(const pa::VerifyArgs &a, const pa_plan *plan, int head_dim,
         return rc;
     const hipEvent_t *ev = timer_take();
     hipError_t err;
-    switch (plan->kernel) {
-    case PA_KERNEL_SIMPLE:
+    if (plan->kernel == PA_KERNEL_SIMPLE) {
         err = pa::launch_verify_simple(a, head_dim, mode, stream, ev);
-        break;
-    case PA_KERNEL_MFMA:
+    } else {
+        // AUTO is the MFMA kernel; check_plan has made sure it takes the plan,
+        // and nothing falls back to the plain kernel
         err = pa::launch_verify_mfma(a, head_dim, mode, stream, ev);
         if (err == hipErrorNotSupported)
-            return PA_EUNSUPPORTED;
-        break;
-    default:
-        err = pa::launch_verify_mfma(a, head_dim, mode, stream, ev);
-        if (err == hipErrorNotSupported)
-            err = pa::launch_verify_simple(a, head_dim, mode, stream, ev);
-        break;
+            return PA_EPLAN;
     }
     return err == hipSuccess ? PA_OK : PA_EHIP;
 }
@@ -232,7 +266,8 @@ int32_t sparse_verify(pa::VerifyMode mode, const void *q_bf16, const pa_kv_pool 
     if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
         return rc;
     if ((rc = check_plan(plan, (int32_t)list_len, rows_per_unit, batch * num_kv_heads,
-                         head_dim)) != PA_OK)
+                         head_dim, kv->page_size,
+                         mode == pa::kModeTokens ? PA_SEL_TOKENS : PA_SEL_BLOCKS)) != PA_OK)
         return rc;
     const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
     if (total_rows > 0x7FFFFFFF)
@@ -278,6 +313,8 @@ extern "C" {
 
 int32_t paged_attn_abi_version(void) { return PA_ABI_VERSION; }
 
+const char *paged_attn_build_id(void) { return PA_BUILD_ID; }
+
 const char *paged_attn_status_string(int32_t status)
 {
     switch (status) {
@@ -294,13 +331,14 @@ const char *paged_attn_status_string(int32_t status)
 }
 
 int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
-                        int32_t head_dim, int32_t num_cus, int32_t requested_splits,
-                        pa_plan *out)
+                        int32_t head_dim, int32_t page_size, int32_t selection,
+                        int32_t num_cus, int32_t requested_splits, pa_plan *out)
 {
     if (!out || max_tokens < 0 || rows_per_kv_unit < 1 || num_kv_units < 1 || head_dim < 1 ||
-        requested_splits < 0)
+        requested_splits < 0 || page_size < 1 || selection < PA_SEL_DENSE ||
+        selection > PA_SEL_TOKENS)
         return PA_EINVAL;
-    const int64_t cus = num_cus > 0 ? num_cus : kDefaultCUs;
+    const int64_t cus = num_cus > 0 ? num_cus : device_cus();
     const int64_t tiles = max_tokens > 0 ? (max_tokens + kTileTokens - 1) / kTileTokens : 1;
     int64_t splits;
     if (requested_splits > 0) {
@@ -323,8 +361,17 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     if (splits > 65535)
         splits = 65535;
     const int64_t tiles_per_split = (tiles + splits - 1) / splits;
-    const int64_t tps = tiles_per_split * kTileTokens;
+    int64_t tps = tiles_per_split * kTileTokens;
+    // longest split whose page slots (token ids: entries) fit the MFMA
+    // kernel's cache: (T - 1) / page + 2 <= slots, i.e. T <= (slots - 1) * page
+    const int64_t slots = pa::mfma_max_slots(head_dim);
+    int64_t tcap = selection == PA_SEL_TOKENS ? slots : (slots - 1) * (int64_t)page_size;
+    tcap = tcap / kTileTokens * kTileTokens;
+    if (tps > tcap)
+        tps = tcap;
     splits = max_tokens > 0 ? ((int64_t)max_tokens + tps - 1) / tps : 1;
+    if (splits > 65535 || splits * tps > INT32_MAX)
+        return PA_EUNSUPPORTED;
     const int64_t rows = (int64_t)rows_per_kv_unit * num_kv_units;
     std::memset(out, 0, sizeof *out);
     out->num_splits = (int32_t)splits;
@@ -334,6 +381,8 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     out->rows_per_kv_unit = rows_per_kv_unit;
     out->num_kv_units = num_kv_units;
     out->head_dim = head_dim;
+    out->page_size = page_size;
+    out->selection = selection;
     out->ws_acc_bytes = splits * rows * head_dim * 4;
     out->ws_stat_bytes = splits * rows * 4;
     return PA_OK;
@@ -360,7 +409,8 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
         return PA_EINVAL;
     if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
         return rc;
-    if ((rc = check_plan(plan, max_tokens, rows_per_unit, num_kv_heads, head_dim)) != PA_OK)
+    if ((rc = check_plan(plan, max_tokens, rows_per_unit, num_kv_heads, head_dim, kv->page_size,
+                         PA_SEL_DENSE)) != PA_OK)
         return rc;
     const int64_t total_rows = (int64_t)q_rows * num_heads;
     if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
@@ -395,7 +445,6 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.ws_acc = ws->acc;
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
-    (void)kLog2e;
     return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
 }
 
@@ -425,8 +474,8 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
         return PA_EUNSUPPORTED;
     if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
         return rc;
-    if ((rc = check_plan(plan, (int32_t)cap, rows_per_unit, batch * num_kv_heads, head_dim)) !=
-        PA_OK)
+    if ((rc = check_plan(plan, (int32_t)cap, rows_per_unit, batch * num_kv_heads, head_dim,
+                         kv->page_size, PA_SEL_DENSE)) != PA_OK)
         return rc;
     const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
     if (total_rows > 0x7FFFFFFF)

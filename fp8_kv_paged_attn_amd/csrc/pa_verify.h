@@ -52,6 +52,21 @@ __host__ __device__ inline int split_span(int lmax, int num_splits)
     return t > 0 ? (t + 63) / 64 * 64 : 64;
 }
 
+// Page slots (token ids: list entries) the MFMA kernel keeps per workgroup in
+// LDS.  A split of T positions in pages of P tokens needs (T - 1) / P + 2 of
+// them; a split of T token ids needs T.
+__host__ __device__ constexpr int mfma_max_slots(int head_dim)
+{
+    return head_dim == 256 ? 1024 : 2048;
+}
+
+__host__ __device__ inline long long mfma_slots_needed(int tokens_per_split, int page_size,
+                                                       bool token_ids)
+{
+    return token_ids ? (long long)tokens_per_split
+                     : (long long)(tokens_per_split - 1) / page_size + 2;
+}
+
 // Launchers return hipSuccess or the launch error.  Grid = (num_splits, units,
 // row chunks of 48).
 // `ev`, when not null, is a (begin, end) pair of HIP events bound to the

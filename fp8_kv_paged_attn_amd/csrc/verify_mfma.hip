@@ -266,13 +266,10 @@ struct Cfg {
     static constexpr int SHARED = STAGES > MERGE ? STAGES : MERGE;
 };
 
-constexpr int kMaxSlotsD256 = 1024;
-constexpr int kMaxSlotsD128 = 2048;
-
 template <int D>
 constexpr int max_slots()
 {
-    return D == 256 ? kMaxSlotsD256 : kMaxSlotsD128;
+    return mfma_max_slots(D);
 }
 
 template <int D, int MODE>
@@ -978,9 +975,7 @@ template <int D, int MODE>
 hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
 {
     // every split's page slots (token ids: positions) must fit the LDS slot cache
-    const int64_t slots = MODE == kModeTokens ? (int64_t)a.tokens_per_split
-                                              : (int64_t)(a.tokens_per_split - 1) / a.page_size + 2;
-    if (slots > max_slots<D>())
+    if (mfma_slots_needed(a.tokens_per_split, a.page_size, MODE == kModeTokens) > max_slots<D>())
         return hipErrorNotSupported;
     // grid z: chunks of 48 rows of a KV unit (one chunk up to 48 rows)
     dim3 grid(a.num_splits, a.batch * a.num_kv_heads,

@@ -57,8 +57,9 @@ extern "C" {
 /* Revision of this interface.  A caller built against another revision must
  * refuse the library rather than run it ([DN] revision gate: the wrapper
  * requires the revision it was written for, so new workspace layouts never
- * reach an older binary). */
-#define PA_ABI_VERSION 1
+ * reach an older binary).  Revision 2: the planner takes the page size and
+ * the selection kind, and plans carry them. */
+#define PA_ABI_VERSION 2
 
 enum pa_status {
     PA_OK = 0,
@@ -73,6 +74,13 @@ enum pa_status {
 
 /* PA_ABI_VERSION of the built library. */
 int32_t paged_attn_abi_version(void);
+
+/* Static, never-NULL identifier of the sources the library was built from: the
+ * first 16 hex digits of a SHA-256 over its HIP sources, its headers and its
+ * code-generation flags, computed by the build and compiled in.  A harness
+ * compares it with the same hash of the sources it holds to know that the
+ * binary it loaded is the one those sources describe. */
+const char *paged_attn_build_id(void);
 
 /* Static, never-NULL description of a status code. */
 const char *paged_attn_status_string(int32_t status);
@@ -94,17 +102,28 @@ typedef struct pa_kv_pool {
 } pa_kv_pool;
 
 /* Kernel choice carried by a plan (an A/B switch; both compute the same
- * function, with different FP32 rounding). */
+ * function, with different FP32 rounding).  Neither falls back to the other:
+ * a plan the chosen kernel cannot run is refused with PA_EPLAN. */
 enum pa_kernel {
-    PA_KERNEL_AUTO = 0,            /* MFMA kernel where it applies, else simple */
-    PA_KERNEL_SIMPLE = 1,          /* plain FP32 kernel (A/B baseline) */
-    PA_KERNEL_MFMA = 2             /* MFMA kernel; PA_EUNSUPPORTED where it does not apply */
+    PA_KERNEL_AUTO = 0,            /* the MFMA kernel */
+    PA_KERNEL_SIMPLE = 1,          /* plain FP32 kernel (A/B baseline, any plan) */
+    PA_KERNEL_MFMA = 2             /* the MFMA kernel */
+};
+
+/* What a list position of a KV unit names (the entry point a plan is for). */
+enum pa_selection {
+    PA_SEL_DENSE = 0,              /* paged_attn_verify_e4m3, paged_attn_verify_batch_e4m3 */
+    PA_SEL_BLOCKS = 1,             /* qsa_sparse_verify_e4m3 */
+    PA_SEL_TOKENS = 2              /* qsa_sparse_verify_tokens_e4m3 */
 };
 
 /* (host) Split plan: the token axis of each KV unit (one KV head of one
  * request) is cut into num_splits ranges of tokens_per_split tokens; range s
  * is one workgroup.  Filled by paged_attn_plan; the other fields record what
- * the plan was made for and are checked by the compute entry points. */
+ * the plan was made for and are checked by the compute entry points
+ * (PA_EPLAN when they differ from the call).  The fields past num_splits and
+ * tokens_per_split, and the workspace struct below, add to the pages' bare
+ * "split count + FP32 workspace" what the library checks before a launch. */
 typedef struct pa_plan {
     int32_t num_splits;
     int32_t tokens_per_split;      /* multiple of 64 */
@@ -113,6 +132,8 @@ typedef struct pa_plan {
     int32_t rows_per_kv_unit;      /* query rows x heads sharing one KV head */
     int32_t num_kv_units;          /* KV heads x requests */
     int32_t head_dim;
+    int32_t page_size;             /* tokens per page (per selected block) */
+    int32_t selection;             /* enum pa_selection */
     int64_t ws_acc_bytes;          /* FP32 [num_splits][rows][head_dim] */
     int64_t ws_stat_bytes;         /* FP32 [num_splits][rows], each of max and sum */
 } pa_plan;
@@ -133,19 +154,26 @@ typedef struct pa_workspace {
     int64_t stat_bytes;            /* capacity of each of max and sum */
 } pa_workspace;
 
-/* (host, pure integer) Choose the split of max_tokens tokens for
- * num_kv_units units of rows_per_kv_unit rows.  num_cus = compute units to
- * fill (<= 0: 256, the MI355X count).  requested_splits > 0 forces the split
- * count (clamped to what the token count allows); 0 picks one: one workgroup
- * per compute unit over all units (a unit of more than 48 rows counts once per
- * 48-row chunk, each chunk being a workgroup), but no split shorter than 128
- * tokens, so
- * that the FP32 partial each split writes stays small against its K/V bytes
- * (the pages tune split counts per device and region, [QSA] sm_120 retune
- * commit).  Returns PA_EINVAL for non-positive sizes. */
+/* (host, integer) Choose the split of max_tokens list positions (tokens for
+ * the dense entries, topk*page_size for selected blocks, the list length for
+ * token ids) for num_kv_units units of rows_per_kv_unit rows, read in pages of
+ * page_size tokens with the given selection (enum pa_selection).
+ * num_cus = compute units to fill; <= 0 takes the current device's count
+ * (queried once per device and kept), or 256 (the MI355X count) when no
+ * device can be queried.  requested_splits > 0 asks for that split count; 0
+ * picks one: one workgroup per compute unit over all units (a unit of more
+ * than 48 rows counts once per 48-row chunk, each chunk being a workgroup),
+ * but no split shorter than 128 tokens, so that the FP32 partial each split
+ * writes stays small against its K/V bytes (the pages tune split counts per
+ * device and region, [QSA] sm_120 retune commit).  Either count is then
+ * clamped to what the token count allows and raised where a split would
+ * otherwise cover more pages (token ids: entries) than the MFMA kernel keeps
+ * per workgroup, 1,024 at head_dim 256 and 2,048 at 128, so that every plan
+ * it returns runs on that kernel.  Returns PA_EINVAL for non-positive sizes or
+ * an unknown selection, PA_EUNSUPPORTED when the count would pass 65,535. */
 int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
-                        int32_t head_dim, int32_t num_cus, int32_t requested_splits,
-                        pa_plan *out);
+                        int32_t head_dim, int32_t page_size, int32_t selection,
+                        int32_t num_cus, int32_t requested_splits, pa_plan *out);
 
 /* Dense verify of one request ([DN] first section), writing split partials.
  *   q_fp16       [q_rows][num_heads][head_dim] FP16, contiguous, 16-byte aligned
@@ -161,7 +189,13 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
  *                sm_scale*k_scale*log2(e) is folded on the host ([QSA]) and must
  *                be a positive normal FP32 number (PA_EINVAL otherwise)
  *   plan         (host) from paged_attn_plan(max_tokens, q_rows*num_heads/num_kv_heads,
- *                num_kv_heads, head_dim, ...)
+ *                num_kv_heads, head_dim, kv->page_size, PA_SEL_DENSE, ...); besides
+ *                the checks of its fields (PA_EPLAN), its splits must satisfy
+ *                (int64)num_splits*tokens_per_split <= INT32_MAX and leave no
+ *                split wholly past max_tokens ((num_splits-1)*tokens_per_split
+ *                < max(max_tokens, 1)), and the MFMA kernel (PA_KERNEL_AUTO or
+ *                _MFMA) needs (tokens_per_split-1)/page_size + 2 pages per split
+ *                to fit its 1,024 (head_dim 256) or 2,048 (128) page slots
  *   ws           (host) workspace of at least plan->ws_*_bytes
  * Tokens a row does not see never reach P.V: their scores are replaced by
  * -inf and their V rows by zero with selects, so NaN bytes in padding pages
@@ -187,7 +221,8 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
  *   <= 96 rows per KV head (more than 48 run as two row chunks, each reading
  *   the unit's K/V); batch*num_kv_heads <= 65535; head_dim 128 or 256
  *   plan         (host) from paged_attn_plan(max_blocks_per_req*page_size,
- *                q_rows*num_heads/num_kv_heads, batch*num_kv_heads, head_dim, ...)
+ *                q_rows*num_heads/num_kv_heads, batch*num_kv_heads, head_dim,
+ *                page_size, PA_SEL_DENSE, ...)
  *   rows of the workspace and of the combined output: (b, i, h).
  * Splits follow each request's own length: with L_b its longest row length
  * (after the clamp) and S = plan->num_splits, split s of request b covers
@@ -247,7 +282,8 @@ int32_t paged_attn_combine_fp32_lse(const float *ws_acc, const float *ws_max,
  *                t < clamp(len, 0, max_blocks_per_req*page_size), which masks
  *                the newest block causally
  *   plan         (host) from paged_attn_plan(topk*page_size, q_rows*num_heads/num_kv_heads,
- *                batch*num_kv_heads, head_dim, ...); split s covers selection
+ *                batch*num_kv_heads, head_dim, page_size, PA_SEL_BLOCKS, ...);
+ *                split s covers selection
  *                list positions [s*T, (s+1)*T), position p naming slot
  *                p / page_size and in-block token p % page_size
  *   rows of the workspace and of the combined output: (b, i, h).
@@ -273,11 +309,11 @@ int32_t qsa_sparse_verify_e4m3(const void *q_bf16, const pa_kv_pool *kv,
  *                t < clamp(len, 0, max_blocks_per_req*page_size), so each row
  *                has its own mask at any position of the list
  *   plan         (host) from paged_attn_plan(num_sel, q_rows*num_heads/num_kv_heads,
- *                batch*num_kv_heads, head_dim, ...); split s covers list entries
- *                [s*T, (s+1)*T).  The MFMA kernel takes T <= 1024 (head_dim 256)
- *                or <= 2048 (head_dim 128); with PA_KERNEL_AUTO a longer split
- *                runs on the plain kernel, with PA_KERNEL_MFMA it is
- *                PA_EUNSUPPORTED.
+ *                batch*num_kv_heads, head_dim, page_size, PA_SEL_TOKENS, ...);
+ *                split s covers list entries [s*T, (s+1)*T).  The MFMA kernel
+ *                takes T <= 1024 (head_dim 256) or <= 2048 (head_dim 128), which
+ *                the planner keeps; a hand-made plan with a longer split runs
+ *                only on PA_KERNEL_SIMPLE (PA_EPLAN otherwise).
  * Other arguments, the workspace rows and the errors as for
  * qsa_sparse_verify_e4m3.  A block selection written out as its token ids
  * (block s -> ids s*page_size .. s*page_size + page_size - 1, an empty slot

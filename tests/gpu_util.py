@@ -54,8 +54,8 @@ def dense_to_dev(w) -> DenseDev:
 def dense_plan(w, kernel="auto", splits: Optional[int] = None):
     G = w.num_heads // w.num_kv_heads
     s = w.num_splits if splits is None else splits
-    return pa.plan(w.max_tokens, w.q_rows * G, w.num_kv_heads, w.head_dim, splits=s,
-                   kernel=kernel)
+    return pa.plan(w.max_tokens, w.q_rows * G, w.num_kv_heads, w.head_dim, w.page_size,
+                   splits=s, kernel=kernel)
 
 
 def run_dense(w, kernel="auto", splits: Optional[int] = None, d: Optional[DenseDev] = None,
@@ -82,8 +82,8 @@ def run_batch(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(DEV)
     G = w.num_heads // w.num_kv_heads
     s = w.num_splits if splits is None else splits
-    p = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, splits=s,
-                kernel=kernel)
+    p = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, w.page_size,
+                splits=s, kernel=kernel)
     ws = pa.make_workspace(p, w.batch * w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                           v_scale=w.v_scale, p=p, ws=ws)
@@ -110,7 +110,7 @@ def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     G = w.num_heads // w.num_kv_heads
     s = w.num_splits if splits is None else splits
     p = pa.plan(w.topk * w.page_size, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
-                splits=s, kernel=kernel)
+                w.page_size, "blocks", splits=s, kernel=kernel)
     ws = pa.make_workspace(p, w.batch * w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.qsa_verify(q, k, v, bt, sel, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                         v_scale=w.v_scale, p=p, ws=ws)
@@ -131,8 +131,8 @@ def run_qsa_tokens(w, kernel="auto", splits: Optional[int] = None, k_pool=None, 
     lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(DEV)
     G = w.num_heads // w.num_kv_heads
     s = w.num_splits if splits is None else splits
-    p = pa.plan(w.num_sel, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, splits=s,
-                kernel=kernel)
+    p = pa.plan(w.num_sel, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, w.page_size,
+                "tokens", splits=s, kernel=kernel)
     out = pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                                v_scale=w.v_scale, p=p)
     torch.cuda.synchronize()

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import fp8_kv_paged_attn_amd as pa
@@ -40,35 +41,62 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_and_status(L):
-    assert L.paged_attn_abi_version() == pa.ABI_VERSION == 1
+    assert L.paged_attn_abi_version() == pa.ABI_VERSION == 2
     for rc in (PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP,
                PA_EPLAN, 12345):
         s = L.paged_attn_status_string(rc)
         assert s and len(s) > 1
 
 
-@pytest.mark.parametrize("max_tokens,rows,units,D,cus,req", [
-    (2048, 12, 1, 256, 256, 4), (8192, 48, 1, 256, 0, 0), (65536, 48, 1, 256, 0, 0),
-    (131072, 48, 1, 256, 0, 0), (262144, 48, 1, 256, 0, 0), (2048, 48, 32, 128, 0, 0),
-    (1, 6, 1, 256, 0, 0), (0, 6, 1, 256, 0, 0), (300, 4, 2, 128, 0, 7), (64, 48, 1, 256, 0, 9),
-    (100000, 48, 3, 256, 80, 0), (262144, 48, 1, 256, 0, 100000),
-    (32960, 96, 8, 256, 0, 0), (32960, 49, 8, 256, 0, 0),
+def mfma_slots_fit(p) -> bool:
+    """The MFMA kernel's rule: a split of T positions in pages of P tokens
+    needs (T - 1) // P + 2 page slots (token ids: T), within 1,024 slots at
+    head_dim 256 and 2,048 at 128."""
+    T = p.tokens_per_split
+    need = T if p.selection == pa.PA_SELECTION["tokens"] else (T - 1) // p.page_size + 2
+    return need <= (1024 if p.head_dim == 256 else 2048)
+
+
+@pytest.mark.parametrize("max_tokens,rows,units,D,page,sel,cus,req", [
+    (2048, 12, 1, 256, 800, "dense", 256, 4), (8192, 48, 1, 256, 3296, "dense", 0, 0),
+    (65536, 48, 1, 256, 3296, "dense", 0, 0), (131072, 48, 1, 256, 3296, "dense", 0, 0),
+    (262144, 48, 1, 256, 3456, "dense", 0, 0), (2048, 48, 32, 128, 64, "blocks", 0, 0),
+    (1, 6, 1, 256, 16, "dense", 0, 0), (0, 6, 1, 256, 16, "dense", 0, 0),
+    (300, 4, 2, 128, 7, "dense", 0, 7), (64, 48, 1, 256, 1, "dense", 0, 9),
+    (100000, 48, 3, 256, 1616, "dense", 80, 0), (262144, 48, 1, 256, 3456, "dense", 0, 100000),
+    (32960, 96, 8, 256, 1600, "dense", 0, 0), (32960, 49, 8, 256, 1600, "dense", 0, 0),
+    (2048, 48, 32, 128, 64, "tokens", 0, 0), (4096, 48, 256, 256, 64, "tokens", 0, 0),
+    (262144, 48, 1, 256, 1, "dense", 0, 0), (262144, 48, 1, 256, 1, "dense", 0, 1),
+    (20000, 48, 1, 128, 1, "blocks", 0, 1), (70000, 12, 1, 256, 2, "dense", 0, 0),
 ])
-def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
-    p = pa.plan(max_tokens, rows, units, D, num_cus=cus, splits=req)
+def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
+    p = pa.plan(max_tokens, rows, units, D, page, sel, num_cus=cus, splits=req)
     S, T = p.num_splits, p.tokens_per_split
     tiles = max(1, -(-max_tokens // 64))
     assert T % 64 == 0 and T >= 64 and 1 <= S <= 65535
     assert S * T >= max_tokens
     if max_tokens > 0:
         assert (S - 1) * T < max_tokens, "no split may lie wholly past max_tokens"
+    assert mfma_slots_fit(p), "every plan runs on the MFMA kernel"
+    # the slot cap only ever raises the count: the uncapped rule's count is a lower bound
     if req:
-        assert S <= min(req, tiles)
+        want = min(req, tiles)
     else:
         c = cus if cus > 0 else 256
-        assert S <= max(1, -(-c // (units * -(-rows // 48))))
-        assert S <= max(1, -(-max_tokens // 128))
-    assert (p.max_tokens, p.rows_per_kv_unit, p.num_kv_units, p.head_dim) == (max_tokens, rows, units, D)
+        want = min(max(1, -(-c // (units * -(-rows // 48)))), max(1, -(-max_tokens // 128)))
+    T0 = -(-tiles // want) * 64
+    S0 = max(1, -(-max_tokens // T0))
+    assert S >= S0
+    if S > S0:
+        # raised only because the uncapped split overflowed the slot cache, and
+        # then to the fewest splits of the longest split that fits
+        slots = 1024 if D == 256 else 2048
+        cap = slots if sel == "tokens" else (slots - 1) * page
+        assert T0 > cap and T == cap // 64 * 64
+    else:
+        assert T == T0
+    assert (p.max_tokens, p.rows_per_kv_unit, p.num_kv_units, p.head_dim, p.page_size,
+            p.selection) == (max_tokens, rows, units, D, page, pa.PA_SELECTION[sel])
     assert p.ws_acc_bytes == S * rows * units * D * 4
     assert p.ws_stat_bytes == S * rows * units * 4
     assert p.kernel == 0
@@ -76,18 +104,66 @@ def test_plan_rules(L, max_tokens, rows, units, D, cus, req):
 
 def test_plan_counts_row_chunks(L):
     # 8 units of 96 rows = 16 workgroups per split: 16 splits fill 256 CUs
-    assert pa.plan(32960, 96, 8, 256).num_splits == 16
+    assert pa.plan(32960, 96, 8, 256, 1600, num_cus=256).num_splits == 16
     # 8 units of 48 rows: 32 splits wanted; 1,088 tokens each cover 32,960 in 31
-    assert pa.plan(32960, 48, 8, 256).num_splits == 31
+    assert pa.plan(32960, 48, 8, 256, 1600, num_cus=256).num_splits == 31
+
+
+def test_plan_raises_splits_to_fit_the_slot_cache(L):
+    # one page per token: a 1,024-token split would need 1,025 slots; 960 fit
+    p = pa.plan(262144, 48, 1, 256, 1, num_cus=256)
+    assert (p.tokens_per_split, p.num_splits) == (960, 274)
+    # 4,096 token ids over 256 units want one split each, but 1,024 ids fit a split
+    p = pa.plan(4096, 48, 256, 256, 64, "tokens", num_cus=256)
+    assert (p.tokens_per_split, p.num_splits) == (1024, 4)
+    # head_dim 128 keeps twice the slots
+    p = pa.plan(4096, 48, 256, 128, 64, "tokens", num_cus=256)
+    assert (p.tokens_per_split, p.num_splits) == (2048, 2)
 
 
 def test_plan_rejects(L):
     out = pa.PaPlan()
-    assert L.paged_attn_plan(-1, 48, 1, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
-    assert L.paged_attn_plan(10, 0, 1, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
-    assert L.paged_attn_plan(10, 4, 0, 256, 0, 0, ctypes.byref(out)) == PA_EINVAL
-    assert L.paged_attn_plan(10, 4, 1, 256, 0, -2, ctypes.byref(out)) == PA_EINVAL
-    assert L.paged_attn_plan(10, 4, 1, 256, 0, 0, None) == PA_EINVAL
+    f = L.paged_attn_plan
+    assert f(-1, 48, 1, 256, 16, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert f(10, 0, 1, 256, 16, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert f(10, 4, 0, 256, 16, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL
+    assert f(10, 4, 1, 256, 16, 0, 0, -2, ctypes.byref(out)) == PA_EINVAL
+    assert f(10, 4, 1, 256, 0, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL      # page size
+    assert f(10, 4, 1, 256, 16, 3, 0, 0, ctypes.byref(out)) == PA_EINVAL     # selection
+    assert f(10, 4, 1, 256, 16, 0, 0, 0, None) == PA_EINVAL
+    # a count past 65,535 splits: two billion tokens in one-token pages
+    assert f(2 ** 31 - 1, 4, 1, 256, 1, 0, 0, 0, ctypes.byref(out)) == PA_EUNSUPPORTED
+
+
+def test_build_id_matches_sources(L):
+    from fp8_kv_paged_attn_amd import build
+
+    assert pa.build_id() == build.source_hash()
+    assert len(pa.build_id()) == 16
+
+
+def test_binding_refuses_a_library_built_from_other_sources(L, monkeypatch):
+    from fp8_kv_paged_attn_amd import build
+
+    monkeypatch.setattr(pa, "_LIB", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 16)
+    with pytest.raises(RuntimeError, match="other sources"):
+        pa.lib()
+
+
+def test_scales_are_host_values():
+    """Scales are folded on the host: a tensor on a device is refused before any
+    call, so nothing reads it back (no synchronisation, capturable calls)."""
+    import torch
+
+    assert pa._scale(torch.tensor(0.5), "k_scale") == 0.5
+    assert pa._scale(np.float32(2.25), "v_scale") == 2.25
+    with pytest.raises(ValueError, match="host scalar"):
+        pa._scale(torch.tensor(0.5, device="meta"), "k_scale")
+    with pytest.raises(ValueError, match="one element"):
+        pa._scale(torch.ones(2), "k_scale")
+    with pytest.raises(ValueError, match="finite"):
+        pa._scale(float("nan"), "k_scale")
 
 
 # Fake, 16-byte-aligned addresses: every call below is rejected by a host check
@@ -107,7 +183,7 @@ class Call:
         self.lens, self.max_tokens = A * 5, 8192
         self.q_rows, self.H, self.Hkv, self.D = 8, 6, 1, 256
         self.sm, self.ks = 0.0625, 0.37
-        self.plan = pa.plan(8192, 48, 1, 256)
+        self.plan = pa.plan(8192, 48, 1, 256, 3296)
         S = self.plan.num_splits
         self.ws = pa.PaWorkspace(A * 6, A * 7, A * 8, S * 48 * 256 * 4, S * 48 * 4)
 
@@ -152,6 +228,10 @@ def test_verify_rejects_bad_arguments(L):
     _spoil(L, "tokens_per_split", 100, PA_EPLAN, sub="plan")
     _spoil(L, "num_splits", 1, PA_EPLAN, sub="plan")
     _spoil(L, "kernel", 7, PA_EPLAN, sub="plan")
+    _spoil(L, "page_size", 3200, PA_EPLAN, sub="plan")             # made for other pages
+    _spoil(L, "selection", 1, PA_EPLAN, sub="plan")                # made for blocks
+    _spoil(L, "tokens_per_split", 1 << 30, PA_EPLAN, sub="plan")   # S*T past INT32_MAX
+    _spoil(L, "num_splits", 200, PA_EPLAN, sub="plan")              # splits wholly past the end
     _spoil(L, "acc_bytes", 1024, PA_EWORKSPACE, sub="ws")
     _spoil(L, "stat_bytes", 4, PA_EWORKSPACE, sub="ws")
     _spoil(L, "sum", None, PA_EINVAL, sub="ws")
@@ -160,7 +240,7 @@ def test_verify_rejects_bad_arguments(L):
 @no_device
 def test_qsa_and_combine_reject_bad_arguments(L):
     pool = pa.PaKvPool(A * 2, A * 3, 64 * 256, 256, 128, 8192, 64)
-    p = pa.plan(32 * 64, 48, 32, 128)
+    p = pa.plan(32 * 64, 48, 32, 128, 64, "blocks")
     ws = pa.PaWorkspace(A * 6, A * 7, A * 8, p.ws_acc_bytes, p.ws_stat_bytes)
 
     def qsa(**kw):
@@ -190,7 +270,7 @@ def test_qsa_tokens_rejects_bad_arguments(L):
     """The token-id entry: the plan is made for num_sel list positions (not
     num_sel * page_size), and a device-free valid call reaches PA_EDEVICE."""
     pool = pa.PaKvPool(A * 2, A * 3, 64 * 256, 256, 128, 8192, 64)
-    p = pa.plan(2048, 48, 32, 128)
+    p = pa.plan(2048, 48, 32, 128, 64, "tokens")
     ws = pa.PaWorkspace(A * 6, A * 7, A * 8, p.ws_acc_bytes, p.ws_stat_bytes)
 
     def tok(**kw):
@@ -207,7 +287,18 @@ def test_qsa_tokens_rejects_bad_arguments(L):
     assert tok(sel=None) == PA_EINVAL
     assert tok(n=0) == PA_EINVAL
     assert tok(n=32) == PA_EPLAN                        # the block entry's list length
-    assert tok(plan=pa.plan(4096, 48, 32, 128)) == PA_EPLAN
+    assert tok(plan=pa.plan(4096, 48, 32, 128, 64, "tokens")) == PA_EPLAN
+    assert tok(plan=pa.plan(2048, 48, 32, 128, 64, "blocks")) == PA_EPLAN
+    # a hand-made split longer than the MFMA kernel's slot cache runs only on
+    # the plain kernel, when asked for
+    long = pa.plan(2048, 48, 32, 128, 64, "tokens", splits=1)
+    long.num_splits, long.tokens_per_split = 1, 2112
+    long.ws_acc_bytes, long.ws_stat_bytes = p.ws_acc_bytes, p.ws_stat_bytes
+    assert tok(plan=long) == PA_EPLAN
+    long.kernel = pa.PA_KERNEL["mfma"]
+    assert tok(plan=long) == PA_EPLAN
+    long.kernel = pa.PA_KERNEL["simple"]
+    assert tok(plan=long) == PA_EDEVICE
     assert tok(B=8) == PA_EPLAN
     assert tok(q=A + 8) == PA_EALIGN
     assert tok(ks=float("inf")) == PA_EINVAL
@@ -223,7 +314,7 @@ def test_verify_batch_rejects_bad_arguments(L):
     pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
                        head_stride=256, num_pages=64, page_size=64)
     p = pa.PaPlan()
-    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 0, 0, ctypes.byref(p)) == PA_OK
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 0, 0, 0, ctypes.byref(p)) == PA_OK
     ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
                         stat_bytes=1 << 40)
     A = ctypes.c_void_p(0x60000)
@@ -255,7 +346,7 @@ def test_verify_batch_without_device_reports_edevice(L):
     pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
                        head_stride=256, num_pages=64, page_size=64)
     p = pa.PaPlan()
-    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 0, 0, ctypes.byref(p)) == PA_OK
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 0, 0, 0, ctypes.byref(p)) == PA_OK
     ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
                         stat_bytes=1 << 40)
     A = ctypes.c_void_p(0x60000)

@@ -217,15 +217,37 @@ def test_qsa_tokens_unseen_bytes_never_read(kernel):
 
 
 def test_qsa_tokens_long_split_kernel_choice(orc):
-    """A split longer than the MFMA kernel's slot cache: auto runs the plain
-    kernel, a forced MFMA kernel is refused."""
+    """A list longer than the MFMA kernel's slot cache asked for in one split:
+    the planner raises the split count so that the MFMA kernel takes it (auto
+    and mfma match the oracle); a hand-made one-split plan is refused by the
+    MFMA kernel and runs only on the plain kernel, when asked for."""
     w = wl.make_qsa_tokens("tok_long", 0x70F0, batch=1, q_rows=2, num_heads=6, num_kv_heads=1,
                            head_dim=256, ctx=3000, page_size=64, num_sel=1100, num_empty=4,
                            k_scale=0.5, v_scale=2.0, num_splits=1)
     announce("tokens_long_split")
-    gu.assert_parity(gu.run_qsa_tokens(w, "auto"), orc.qsa_tokens_workload(w), "tok_long")
-    with pytest.raises(RuntimeError, match="-2|unsupported"):
-        gu.run_qsa_tokens(w, "mfma")
+    ref = orc.qsa_tokens_workload(w)
+    for kernel in ("auto", "mfma"):
+        gu.assert_parity(gu.run_qsa_tokens(w, kernel), ref, f"tok_long {kernel}")
+    q = gu.bf16_tensor(w.q_bits).to(gu.DEV)
+    k = torch.from_numpy(w.k_pool).to(gu.DEV)
+    v = torch.from_numpy(w.v_pool).to(gu.DEV)
+    bt = torch.from_numpy(w.block_table.astype(np.int32)).to(gu.DEV)
+    sel = torch.from_numpy(w.sel_tokens.astype(np.int32)).to(gu.DEV)
+    lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(gu.DEV)
+    p = pa.plan(w.num_sel, w.q_rows * w.num_heads, 1, w.head_dim, w.page_size, "tokens")
+    assert p.num_splits == 2
+    p.num_splits, p.tokens_per_split = 1, 1152
+    p.ws_acc_bytes, p.ws_stat_bytes = p.ws_acc_bytes // 2, p.ws_stat_bytes // 2
+    run = lambda: pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale,
+                                       k_scale=w.k_scale, v_scale=w.v_scale, p=p)
+    for kernel in ("auto", "mfma"):
+        p.kernel = pa.PA_KERNEL[kernel]
+        with pytest.raises(RuntimeError, match="-7|plan"):
+            run()
+    p.kernel = pa.PA_KERNEL["simple"]
+    got = run()
+    torch.cuda.synchronize()
+    gu.assert_parity(got.cpu().numpy(), ref, "tok_long simple, one split")
 
 
 # ---------------------------------------------------------------------------
@@ -593,17 +615,19 @@ def test_graph_replay_sparse_and_batch_entries():
         G = H // w.num_kv_heads
         if kind == "blocks":
             sel = torch.from_numpy(w.sel_blocks.astype(np.int32)).to(dev)
-            p = pa.plan(w.topk * w.page_size, qr * G, B * w.num_kv_heads, D, splits=3)
+            p = pa.plan(w.topk * w.page_size, qr * G, B * w.num_kv_heads, D, w.page_size,
+                        "blocks", splits=3)
             fn = lambda: pa.qsa_verify(q, k, v, bt, sel, lens, sm_scale=w.sm_scale,
                                        k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws, out=out)
         elif kind == "tokens":
             sel = torch.from_numpy(w.sel_tokens.astype(np.int32)).to(dev)
-            p = pa.plan(w.num_sel, qr * G, B * w.num_kv_heads, D, splits=3)
+            p = pa.plan(w.num_sel, qr * G, B * w.num_kv_heads, D, w.page_size, "tokens",
+                        splits=3)
             fn = lambda: pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale,
                                               k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
                                               out=out)
         else:
-            p = pa.plan(w.cap, qr * G, B * w.num_kv_heads, D, splits=4)
+            p = pa.plan(w.cap, qr * G, B * w.num_kv_heads, D, w.page_size, splits=4)
             fn = lambda: pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale,
                                          k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
                                          out=out)
@@ -821,7 +845,8 @@ def test_batch_matches_single_requests(kernel):
         T = -(-T // 64) * 64 if T > 0 else 64
         r = dataclasses.replace(w.request(b), max_tokens=w.cap)
         d = gu.dense_to_dev(r)
-        p = pa.plan(w.cap, R // w.num_kv_heads, w.num_kv_heads, w.head_dim, kernel=kernel)
+        p = pa.plan(w.cap, R // w.num_kv_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                    kernel=kernel)
         p.tokens_per_split = T
         p.num_splits = -(-w.cap // T)
         ws = pa.make_workspace(p, R, w.head_dim, gu.DEV)
