@@ -36,9 +36,13 @@
 //  * The running reference max of a row moves only when a block exceeds it by
 //    more than 2^8, so P <= 2^14 in FP16 and accumulator rescales are rare;
 //    the partial written out uses the exact row max.
-//  * Tokens a row must not see get score -inf by select, and V bytes of
-//    positions no row sees are zeroed by select before P.V, so NaN bytes in
-//    padding pages cannot leak (null-block fix of 1Cat-vLLM PR #702).
+//  * Tokens a row must not see get score -inf by select.  In a block that
+//    some live row does not see whole, the V bytes are sanitised in registers
+//    before P.V (NaN codes become 0, so p = 0 times a NaN byte cannot reach a
+//    row that does not see it), and the (row, column) pairs whose row sees a
+//    NaN V byte in that column are recorded and set to NaN before the split's
+//    merge: every row gets what the unsplit definition gives it, and NaN bytes
+//    in padding pages cannot leak (null-block fix of 1Cat-vLLM PR #702).
 #include "pa_verify.h"
 
 #include <math.h>
@@ -227,6 +231,27 @@ __device__ __forceinline__ float sum_over_groups(float v)
     swap32(v, a, b);
     swap16(a + b, a, b);
     return a + b;
+}
+
+__device__ __forceinline__ uint32_t or_over_groups(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    const auto t = __builtin_amdgcn_permlane16_swap(r0 | r1, r0 | r1, false, false);
+    const uint32_t t0 = t[0], t1 = t[1];
+    return t0 | t1;
+}
+
+// E4M3 NaN codes (S.1111.111) of the four bytes of x become 0x00; returns a
+// 4-bit mask of the bytes that were NaN.  (x & 0x7F) + 1 carries into bit 7
+// of a byte exactly when its low seven bits are all ones, and never into the
+// next byte.
+__device__ __forceinline__ uint32_t drop_nan_bytes(int &x)
+{
+    const uint32_t u = (uint32_t)x;
+    const uint32_t hit = ((u & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    x = (int)(u & ~((hit >> 7) * 0xFFu));
+    return ((hit >> 7) & 1u) | ((hit >> 14) & 2u) | ((hit >> 21) & 4u) | ((hit >> 28) & 8u);
 }
 
 // x *= f, one accumulator fragment at a time: the volatile asm keeps the
@@ -600,11 +625,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         for (int d = 0; d < C::DB; ++d)
             acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_true[kRowBlocks], m_ref[kRowBlocks], l_part[kRowBlocks];
+    // per row block, (d-block, k) pairs of this lane whose row saw a NaN V byte
+    uint64_t nan_hit[kRowBlocks];
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         m_true[rb] = -INFINITY;
         m_ref[rb] = -INFINITY;
         l_part[rb] = 0.0f;
+        nan_hit[rb] = 0;
     }
     const float c = a.logit_scale;
 
@@ -622,19 +650,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     const int vrow = 8 * g + (n >> 1);
     const uint32_t voff = vrow * D + (swz<D>(vrow) << 4) + ((n & 1) << 3);
-
-    // Zero V rows [from, 32) of this wave's stage: V bytes of positions that no
-    // query sees must not reach P.V (they may be NaN).  Rare: the last block of
-    // a split, or a sparse block cut by the lengths.
-    const uint32_t rowbit = 1u << (lane / C::LANES_PER_ROW);   // row of this lane in a 1 KB load
-    auto zero_v_rows = [&](uint8_t *vst, uint32_t keep) __attribute__((always_inline)) {
-        uint8_t *blk = vst + w * C::BLOCK;
-#pragma unroll
-        for (int i = 0; i < C::DMA; ++i) {
-            if (!((keep >> (i * C::ROWS_PER_DMA)) & rowbit))
-                *(int4v *)(blk + i * 1024 + lane * 16) = int4v{0, 0, 0, 0};
-        }
-    };
 
     // One block of this wave (step j) with NRB live row blocks.  Block j uses K
     // stage j%2 and V stage j%2.  Issue order: K0 V0 (prologue), then in step
@@ -710,12 +725,12 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 
         // ---- visibility, online softmax, P = hi + lo -------------------------
         half8 ph[NRB], pl[NRB];
-        uint32_t keep = 0xFFFFFFFFu;                 // V rows some query sees
+        // every live row block sees every token of this block (wave-uniform)
+        bool all_full = true;
         if (any) {
             // row blocks that see every token of this block (wave-uniform)
             const int tmax = SPARSE ? blk_tmax[w][st] : 0;
             bool full[NRB];
-            bool all_full = true;
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 full[rb] = SPARSE ? (tmax < minl[rb]) : (pos0 + kSub <= minl[rb]);
@@ -729,17 +744,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 const int4v t1 = *(const int4v *)&tok[8 * g + 4];
                 tk[0] = t0.x; tk[1] = t0.y; tk[2] = t0.z; tk[3] = t0.w;
                 tk[4] = t1.x; tk[5] = t1.y; tk[6] = t1.z; tk[7] = t1.w;
-                uint32_t mine = 0;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    mine |= (tk[jj] != INT32_MAX) ? (1u << jj) : 0u;
-                // gather the 32 row flags: lane group g holds rows 8g .. 8g+7
-                keep = 0;
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg)
-                    keep |= (uint32_t)__builtin_amdgcn_readlane((int)mine, 16 * gg) << (8 * gg);
-            } else if (!SPARSE && pos0 + kSub > hi) {
-                keep = (1u << (hi - pos0)) - 1u;
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
@@ -808,8 +812,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 
         // ---- O^T += V^T P^T over the wave's 32 tokens, all D columns ---------
         if (any) {
-            if (keep != 0xFFFFFFFFu)
-                zero_v_rows(vst, keep);
             const uint32_t vaddr = lds_addr(vst + w * C::BLOCK) + voff;
             // all V^T reads of the block first, so that their latencies overlap
             int2v vraw[C::DB];
@@ -818,6 +820,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 vraw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (__attribute__((address_space(3))) int2v *)(uintptr_t)(vaddr ^ (uint32_t)(db << 4)));
             __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their uses
+            // Lane (n, g) holds V[token 8g + j][column 16 db + n] in byte j of
+            // vraw[db].  A block that some live row does not see whole has its
+            // NaN bytes replaced by 0, and their positions recorded as one
+            // 32-bit token mask per column ([D] words, byte g from lane group
+            // g) in this wave's K stage, which holds nothing until K(j+2).
+            uint8_t *const nanw = kst + w * C::BLOCK;
+            if (!all_full) {
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    int x = vraw[db].x, y = vraw[db].y;
+                    const uint32_t lo4 = drop_nan_bytes(x);
+                    const uint32_t hi4 = drop_nan_bytes(y);
+                    vraw[db] = int2v{x, y};
+                    nanw[(16 * db + n) * 4 + g] = (uint8_t)(lo4 | (hi4 << 4));
+                }
+            }
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
                 const half8 vf = dec_f16(vraw[db]);
@@ -827,6 +845,43 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb)
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][db], 0, 0, 0);
+            }
+            if (!all_full) {
+                // acc[rb][db] lane (n, g) holds row 16 rb + n, columns
+                // 16 db + 4 g + k; bit 4 db + k of nan_hit[rb] records that the
+                // row sees a NaN byte of that column.  Row visibility over the
+                // block's 32 tokens: dense, the prefix below the row's length;
+                // sparse, the tokens below it (INT32_MAX: no row sees it).
+                uint32_t vis32[NRB];
+                int tk8[8];
+                if (SPARSE) {
+                    const int4v t0 = *(const int4v *)&tok[8 * g];
+                    const int4v t1 = *(const int4v *)&tok[8 * g + 4];
+                    tk8[0] = t0.x; tk8[1] = t0.y; tk8[2] = t0.z; tk8[3] = t0.w;
+                    tk8[4] = t1.x; tk8[5] = t1.y; tk8[6] = t1.z; tk8[7] = t1.w;
+                }
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) {
+                    if (SPARSE) {
+                        uint32_t v8 = 0;
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj)
+                            v8 |= (tk8[jj] < lrow[rb]) ? (1u << jj) : 0u;
+                        vis32[rb] = or_over_groups(v8 << (8 * g));
+                    } else {
+                        const int nv = min(max(min(lrow[rb], hi) - pos0, 0), kSub);
+                        vis32[rb] = nv >= kSub ? 0xFFFFFFFFu : (1u << nv) - 1u;
+                    }
+                }
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    const int4v nm = *(const int4v *)(nanw + (16 * db + 4 * g) * 4);
+#pragma unroll
+                    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            nan_hit[rb] |= ((uint32_t)nm[k] & vis32[rb]) ? (1ull << (4 * db + k)) : 0ull;
+                }
             }
         }
         if (j + 1 < nms)
@@ -866,6 +921,23 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             m_ref[rb] = -INFINITY;
             l_part[rb] = 0.0f;
         }
+    }
+    // NaN V bytes seen by a row (rare; only blocks not seen whole record them)
+    bool any_nan = false;
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb)
+        any_nan = any_nan || nan_hit[rb] != 0;
+    if (__any(any_nan)) {
+#pragma unroll
+        for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+            for (int d = 0; d < C::DB; ++d) {
+                f32x4 x = acc[rb][d];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    x[k] = ((nan_hit[rb] >> (4 * d + k)) & 1ull) ? __builtin_nanf("") : x[k];
+                acc[rb][d] = x;
+            }
     }
     float lw[kRowBlocks];
 #pragma unroll
@@ -947,6 +1019,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     for (int vi = 0; vi < kWaves - 1; ++vi)
                         o += xs[vi][d] * fv[vi < q ? vi : vi + 1];
                 }
+                // a row that sees nothing of the split writes zeros, whatever
+                // its accumulators took up unmasked (the weights are 0, but
+                // 0 x NaN is not)
+                if (L == 0.0f)
+                    o = f32x4{0.f, 0.f, 0.f, 0.f};
                 // lane (n, g) of d-block db holds d = 16 db + 4 g + k
                 if (r < R)
                     *(f32x4 *)(dst + 16 * (q * C::DQ + d) + 4 * g) = o;

@@ -4,7 +4,9 @@
 // One workgroup per (split, KV unit).  Each 64-position tile of the split is
 // gathered into LDS as raw E4M3 bytes, scores are FP32 dot products, the
 // online softmax keeps a per-row FP32 max and sum, and P.V accumulates in FP32
-// registers, one output column per thread.  It is the plain form of the
+// registers, one output column per thread.  A position a row does not see
+// adds nothing to that row's P.V (selected out, not multiplied by 0), so a
+// NaN byte reaches exactly the rows that see it.  It is the plain form of the
 // computation (design note "DFlash2 E4M3 attention with FP32 state", first
 // section: FP32 unnormalised partition numerators, separate FP32 max/sum),
 // kept as the A/B baseline of the MFMA kernel and for shapes it does not take.
@@ -163,12 +165,13 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
             for (int j = 0; j < kTile; ++j)
                 mx = fmaxf(mx, p_s[tid][j]);
             float alpha = (mx == -INFINITY) ? 1.0f : exp2f(m_s[tid] - mx);
+            // a position the row does not see (score -inf) is marked p = -1
             float sum = 0.0f;
             for (int j = 0; j < kTile; ++j) {
                 float s = p_s[tid][j];
-                float p = (s == -INFINITY) ? 0.0f : exp2f(s - mx);
+                float p = (s == -INFINITY) ? -1.0f : exp2f(s - mx);
                 p_s[tid][j] = p;
-                sum += p;
+                sum += (p < 0.0f) ? 0.0f : p;
             }
             l_s[tid] = l_s[tid] * alpha + sum;
             m_s[tid] = mx;
@@ -180,8 +183,10 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
             for (int r = 0; r < kMaxRows; ++r) {
                 if (r < R) {
                     float s = acc[r] * alpha_s[r];
-                    for (int j = 0; j < kTile; ++j)
-                        s += p_s[r][j] * e4m3_to_float(v_s[j][tid]);
+                    for (int j = 0; j < kTile; ++j) {
+                        const float p = p_s[r][j];
+                        s += (p < 0.0f) ? 0.0f : p * e4m3_to_float(v_s[j][tid]);
+                    }
                     acc[r] = s;
                 }
             }

@@ -197,9 +197,13 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
  *                _MFMA) needs (tokens_per_split-1)/page_size + 2 pages per split
  *                to fit its 1,024 (head_dim 256) or 2,048 (128) page slots
  *   ws           (host) workspace of at least plan->ws_*_bytes
- * Tokens a row does not see never reach P.V: their scores are replaced by
- * -inf and their V rows by zero with selects, so NaN bytes in padding pages
- * or page tails have no effect ([NB] null-block fix). */
+ * Tokens a row does not see never reach that row's P.V: their scores are
+ * replaced by -inf with selects, and in a block that some row does not see
+ * whole the V bytes are cleared of NaN codes before P.V, so NaN bytes in
+ * padding pages or page tails have no effect ([NB] null-block fix).  NaN bytes
+ * at positions a row sees (not specified by the pages) give what the
+ * definition gives: a NaN K byte makes every row that sees its token NaN, a
+ * NaN V byte makes its column NaN in exactly the rows that see its token. */
 int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                const int32_t *block_table, int32_t num_table_entries,
                                const int32_t *row_lens, int32_t max_tokens, int32_t q_rows,

@@ -234,7 +234,8 @@ def test_qsa_tokens_long_split_kernel_choice(orc):
     bt = torch.from_numpy(w.block_table.astype(np.int32)).to(gu.DEV)
     sel = torch.from_numpy(w.sel_tokens.astype(np.int32)).to(gu.DEV)
     lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(gu.DEV)
-    p = pa.plan(w.num_sel, w.q_rows * w.num_heads, 1, w.head_dim, w.page_size, "tokens")
+    p = pa.plan(w.num_sel, w.q_rows * w.num_heads, 1, w.head_dim, w.page_size, "tokens",
+                splits=1)
     assert p.num_splits == 2
     p.num_splits, p.tokens_per_split = 1, 1152
     p.ws_acc_bytes, p.ws_stat_bytes = p.ws_acc_bytes // 2, p.ws_stat_bytes // 2
