@@ -62,7 +62,8 @@ EXPORTS = ("paged_attn_abi_version", "paged_attn_build_id", "paged_attn_status_s
            "paged_attn_verify_e4m3", "paged_attn_combine_fp32", "qsa_sparse_verify_e4m3",
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
            "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
-           "paged_attn_cache_write_e4m3", "qsa_sparse_verify_tokens_e4m3")
+           "paged_attn_cache_write_e4m3", "qsa_sparse_verify_tokens_e4m3",
+           "paged_attn_verify_noalloc_e4m3")
 
 _LIB = None
 
@@ -92,6 +93,10 @@ def lib() -> ctypes.CDLL:
     L.paged_attn_verify_e4m3.restype = i32
     L.paged_attn_combine_fp32.argtypes = [p, p, p, i32, i32, i32, f32, p, p]
     L.paged_attn_combine_fp32.restype = i32
+    L.paged_attn_verify_noalloc_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32,
+                                                 i32, i32, i32, i32, f32, f32, f32,
+                                                 ctypes.POINTER(PaPlan), p, p]
+    L.paged_attn_verify_noalloc_e4m3.restype = i32
     L.paged_attn_verify_batch_e4m3.argtypes = [p, ctypes.POINTER(PaKvPool), p, i32, p, i32, i32,
                                                i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                                ctypes.POINTER(PaWorkspace), p]
@@ -276,6 +281,34 @@ def paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens:
         k_pool.shape[2], D, _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"),
         ctypes.byref(p), ctypes.byref(_ws(*ws)), _stream(dev))
     _check(rc, "paged_attn_verify_e4m3")
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+
+
+def paged_attn_verify_noalloc_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens: int,
+                                   sm_scale, k_scale, v_scale, p: PaPlan, out) -> None:
+    """Dense verify + combine of one request into out (float16, contiguous
+    [q_rows][heads][head_dim]) with the split partials in the library's fixed
+    per-device scratch: no workspace, nothing allocated."""
+    torch = _torch()
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous float16 tensor [q_rows][heads][head_dim]")
+    dev = q.device
+    pool = _pool(k_pool, v_pool, dev)
+    qr, H, D = q.shape
+    if k_pool.shape[3] != D:
+        raise ValueError("head_dim of q and the pool differ")
+    if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() < qr * H * D \
+            or out.device != dev:
+        raise ValueError("out must be a contiguous float16 tensor of q_rows*heads*head_dim "
+                         "elements on the query's device")
+    rc = lib().paged_attn_verify_noalloc_e4m3(
+        q.data_ptr(), ctypes.byref(pool), _i32(block_table, "block_table", dev),
+        block_table.numel(), _i32(row_lens, "row_lens", dev), int(max_tokens), qr, H,
+        k_pool.shape[2], D, _scale(sm_scale, "sm_scale"), _scale(k_scale, "k_scale"),
+        _scale(v_scale, "v_scale"), ctypes.byref(p), out.data_ptr(), _stream(dev))
+    _check(rc, "paged_attn_verify_noalloc_e4m3")
 
 
 def paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_scale, k_scale,

@@ -307,6 +307,91 @@ int32_t sparse_verify(pa::VerifyMode mode, const void *q_bf16, const pa_kv_pool 
     return dispatch(a, plan, head_dim, mode, static_cast<hipStream_t>(stream));
 }
 
+// Checks and kernel arguments of one dense request (everything but the
+// workspace), shared by the dense entry points.
+int32_t dense_args(const void *q_fp16, const pa_kv_pool *kv, const int32_t *block_table,
+                   int32_t num_table_entries, const int32_t *row_lens, int32_t max_tokens,
+                   int32_t q_rows, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   float sm_scale, float k_scale, const pa_plan *plan, pa::VerifyArgs *out)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!q_fp16 || !block_table || !row_lens)
+        return PA_EINVAL;
+    if ((rc = check_pool(kv)) != PA_OK)
+        return rc;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
+        return rc;
+    if (!aligned16(q_fp16))
+        return PA_EALIGN;
+    if (num_table_entries < 0 || max_tokens < 0 ||
+        (int64_t)max_tokens > (int64_t)num_table_entries * kv->page_size)
+        return PA_EINVAL;
+    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
+        return rc;
+    if ((int64_t)q_rows * num_heads > INT32_MAX)
+        return PA_EINVAL;
+    if (num_kv_heads > 65535)
+        return PA_EUNSUPPORTED;
+    if ((rc = check_plan(plan, max_tokens, rows_per_unit, num_kv_heads, head_dim, kv->page_size,
+                         PA_SEL_DENSE)) != PA_OK)
+        return rc;
+    pa::VerifyArgs &a = *out;
+    std::memset(&a, 0, sizeof a);
+    a.q = static_cast<const uint16_t *>(q_fp16);
+    a.k_pool = kv->k_pool;
+    a.v_pool = kv->v_pool;
+    a.page_stride = kv->page_stride;
+    a.token_stride = kv->token_stride;
+    a.head_stride = kv->head_stride;
+    a.page_size = kv->page_size;
+    a.block_table = block_table;
+    a.table_stride = 0;
+    a.sel = nullptr;
+    a.topk = 0;
+    a.row_lens = row_lens;
+    a.len_cap = max_tokens;
+    a.list_len = max_tokens;
+    a.batch = 1;
+    a.q_rows = q_rows;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_heads / num_kv_heads;
+    a.rows = rows_per_unit;
+    a.num_splits = plan->num_splits;
+    a.tokens_per_split = plan->tokens_per_split;
+    a.total_rows = q_rows * num_heads;
+    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    return PA_OK;
+}
+
+int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// Scratch of the allocation-free entry point: the FP32 split partials of one
+// call, in a fixed array of every device the library runs on (held until the
+// process ends).  Host code never uses the array's name as an address: its
+// device address is looked up once per device, with that device current, and
+// kept.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_base[64] = {};
+
+int32_t scratch_base(uint8_t **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return PA_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_base[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return PA_EHIP;
+        g_scratch_base[dev] = static_cast<uint8_t *>(p);
+    }
+    *out = g_scratch_base[dev];
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -326,6 +411,8 @@ const char *paged_attn_status_string(int32_t status)
     case PA_EDEVICE: return "no usable gfx950 device";
     case PA_EHIP: return "HIP launch failed";
     case PA_EPLAN: return "plan does not match this call";
+    case PA_ESCRATCH:
+        return "plan needs more partials than the allocation-free entry's fixed scratch holds";
     default: return "unknown status";
     }
 }
@@ -395,57 +482,65 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                float sm_scale, float k_scale, const pa_plan *plan,
                                const pa_workspace *ws, void *stream)
 {
-    int32_t rc, rows_per_unit = 0;
-    if (!q_fp16 || !block_table || !row_lens)
-        return PA_EINVAL;
-    if ((rc = check_pool(kv)) != PA_OK)
-        return rc;
-    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit)) != PA_OK)
-        return rc;
-    if (!aligned16(q_fp16))
-        return PA_EALIGN;
-    if (num_table_entries < 0 || max_tokens < 0 ||
-        (int64_t)max_tokens > (int64_t)num_table_entries * kv->page_size)
-        return PA_EINVAL;
-    if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
-        return rc;
-    if ((rc = check_plan(plan, max_tokens, rows_per_unit, num_kv_heads, head_dim, kv->page_size,
-                         PA_SEL_DENSE)) != PA_OK)
-        return rc;
-    const int64_t total_rows = (int64_t)q_rows * num_heads;
-    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
-        return rc;
-
     pa::VerifyArgs a;
-    std::memset(&a, 0, sizeof a);
-    a.q = static_cast<const uint16_t *>(q_fp16);
-    a.k_pool = kv->k_pool;
-    a.v_pool = kv->v_pool;
-    a.page_stride = kv->page_stride;
-    a.token_stride = kv->token_stride;
-    a.head_stride = kv->head_stride;
-    a.page_size = kv->page_size;
-    a.block_table = block_table;
-    a.table_stride = 0;
-    a.sel = nullptr;
-    a.topk = 0;
-    a.row_lens = row_lens;
-    a.len_cap = max_tokens;
-    a.list_len = max_tokens;
-    a.batch = 1;
-    a.q_rows = q_rows;
-    a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = num_heads / num_kv_heads;
-    a.rows = rows_per_unit;
-    a.num_splits = plan->num_splits;
-    a.tokens_per_split = plan->tokens_per_split;
-    a.total_rows = (int32_t)total_rows;
-    a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
+    int32_t rc = dense_args(q_fp16, kv, block_table, num_table_entries, row_lens, max_tokens,
+                            q_rows, num_heads, num_kv_heads, head_dim, sm_scale, k_scale, plan,
+                            &a);
+    if (rc != PA_OK)
+        return rc;
+    if ((rc = check_ws(ws, plan, a.total_rows, head_dim)) != PA_OK)
+        return rc;
     a.ws_acc = ws->acc;
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_verify_noalloc_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                                       const int32_t *block_table, int32_t num_table_entries,
+                                       const int32_t *row_lens, int32_t max_tokens,
+                                       int32_t q_rows, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, float sm_scale, float k_scale,
+                                       float v_scale, const pa_plan *plan, void *out_fp16,
+                                       void *stream)
+{
+    pa::VerifyArgs a;
+    int32_t rc = dense_args(q_fp16, kv, block_table, num_table_entries, row_lens, max_tokens,
+                            q_rows, num_heads, num_kv_heads, head_dim, sm_scale, k_scale, plan,
+                            &a);
+    if (rc != PA_OK)
+        return rc;
+    if (!out_fp16)
+        return PA_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0)
+        return PA_EALIGN;
+    if (!std::isfinite(v_scale))
+        return PA_EINVAL;
+    // the partials' layout in the scratch array: acc, then max, then sum,
+    // each starting on a 256-byte boundary
+    const int64_t cells = (int64_t)plan->num_splits * a.total_rows;
+    const int64_t acc_bytes = align256(cells * head_dim * 4);
+    const int64_t stat_bytes = align256(cells * 4);
+    if (acc_bytes + 2 * stat_bytes > PA_NOALLOC_SCRATCH_BYTES)
+        return PA_ESCRATCH;
+    if ((rc = check_device()) != PA_OK)
+        return rc;
+    uint8_t *base = nullptr;
+    if ((rc = scratch_base(&base)) != PA_OK)
+        return rc;
+    a.ws_acc = reinterpret_cast<float *>(base);
+    a.ws_max = reinterpret_cast<float *>(base + acc_bytes);
+    a.ws_sum = reinterpret_cast<float *>(base + acc_bytes + stat_bytes);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = dispatch(a, plan, head_dim, pa::kModeDense, st)) != PA_OK)
+        return rc;
+    // the verify kernel has written every (split, row) of the partials it
+    // combines, so nothing in the array needs clearing between calls
+    const hipError_t err = pa::launch_combine(a.ws_acc, a.ws_max, a.ws_sum, plan->num_splits,
+                                              a.total_rows, head_dim, v_scale,
+                                              static_cast<uint16_t *>(out_fp16), nullptr,
+                                              nullptr, st);
+    return err == hipSuccess ? PA_OK : PA_EHIP;
 }
 
 int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,

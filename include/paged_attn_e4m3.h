@@ -69,7 +69,9 @@ enum pa_status {
     PA_EALIGN = -4,        /* pointer or stride not 16-byte aligned */
     PA_EDEVICE = -5,       /* no HIP device, or not gfx950 */
     PA_EHIP = -6,          /* a HIP call or kernel launch failed */
-    PA_EPLAN = -7          /* plan does not cover this call */
+    PA_EPLAN = -7,         /* plan does not cover this call */
+    PA_ESCRATCH = -8       /* plan needs more than the fixed scratch of
+                              paged_attn_verify_noalloc_e4m3 */
 };
 
 /* PA_ABI_VERSION of the built library. */
@@ -240,6 +242,36 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                      float sm_scale, float k_scale, const pa_plan *plan,
                                      const pa_workspace *ws, void *stream);
+
+/* Allocation-free dense verify of one request: paged_attn_verify_e4m3 followed
+ * by paged_attn_combine_fp32 (the same kernels, so the same output bits), with
+ * the FP32 split partials kept in a fixed device array of the library instead
+ * of a caller workspace.  For callers that cannot allocate device memory or
+ * manage a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The entry itself allocates and frees
+ * nothing.
+ *   Arguments as for paged_attn_verify_e4m3, plus
+ *   v_scale      (host) finite; the combine's output scale
+ *   out_fp16     [q_rows][num_heads][head_dim] FP16, 8-byte aligned
+ * Limit: the partials, num_splits*rows*(head_dim + 2)*4 bytes with rows =
+ * q_rows*num_heads (each of the three parts rounded up to 256 bytes), must fit
+ * PA_NOALLOC_SCRATCH_BYTES (16 MiB; 256 splits of 48 rows at head_dim 256
+ * take 12.7 MB); a larger plan returns PA_ESCRATCH before anything is
+ * enqueued.  The array is a file-scope __device__ variable: every device the
+ * library runs on holds its own copy until the process ends.  Its device
+ * address is looked up on the first call on each device (PA_EHIP if that
+ * fails).  Every call overwrites all the partials it reads, so nothing needs
+ * clearing between calls; but all calls on one device share the one array,
+ * so calls that may overlap on one device (other streams, other threads)
+ * race and must be ordered by the caller. */
+#define PA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int32_t paged_attn_verify_noalloc_e4m3(const void *q_fp16, const pa_kv_pool *kv,
+                                       const int32_t *block_table, int32_t num_table_entries,
+                                       const int32_t *row_lens, int32_t max_tokens,
+                                       int32_t q_rows, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, float sm_scale, float k_scale,
+                                       float v_scale, const pa_plan *plan, void *out_fp16,
+                                       void *stream);
 
 /* FP32 combination of split partials into FP16 rows ([DN] first section):
  *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),

@@ -16,6 +16,7 @@ HEADER = os.path.join(ROOT, "include", "paged_attn_e4m3.h")
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP, PA_EPLAN = (
     0, -1, -2, -3, -4, -5, -6, -7)
+PA_ESCRATCH = -8
 
 
 @pytest.fixture(scope="module")
@@ -43,7 +44,7 @@ def test_exports_every_declared_function(L):
 def test_abi_and_status(L):
     assert L.paged_attn_abi_version() == pa.ABI_VERSION == 2
     for rc in (PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP,
-               PA_EPLAN, 12345):
+               PA_EPLAN, PA_ESCRATCH, 12345):
         s = L.paged_attn_status_string(rc)
         assert s and len(s) > 1
 
@@ -308,6 +309,36 @@ def test_qsa_tokens_rejects_bad_arguments(L):
 @no_device
 def test_valid_call_without_device_reports_edevice(L):
     assert Call()(L) == PA_EDEVICE
+
+
+@no_device
+def test_noalloc_entry_checks_before_any_device_call(L):
+    """The allocation-free entry checks its arguments like the workspace entry,
+    refuses a plan whose partials exceed the fixed scratch (PA_ESCRATCH), and
+    only then looks for a device."""
+    c = Call()
+    out = A * 9
+
+    def call(plan=None, out=out, vs=1.9, max_tokens=8192):
+        p = plan or c.plan
+        return L.paged_attn_verify_noalloc_e4m3(c.q, ctypes.byref(c.pool), c.table, c.entries,
+                                                c.lens, max_tokens, c.q_rows, c.H, c.Hkv, c.D,
+                                                c.sm, c.ks, vs, ctypes.byref(p), out, None)
+
+    assert call() == PA_EDEVICE
+    assert call(out=None) == PA_EINVAL
+    assert call(out=A * 9 + 4) == PA_EALIGN
+    assert call(vs=float("inf")) == PA_EINVAL
+    assert call(max_tokens=8000) == PA_EPLAN
+    big = pa.plan(8192, 48, 1, 256, 3296, splits=128)
+    assert big.num_splits * 48 * 258 * 4 <= pa.NOALLOC_SCRATCH_BYTES
+    assert call(plan=big) == PA_EDEVICE
+    pool = pa.PaKvPool(A * 2, A * 3, 4096 * 256, 256, 256, 64, 4096)
+    huge = pa.plan(1 << 15, 48, 1, 256, 4096, splits=512)
+    assert huge.num_splits * 48 * 258 * 4 > pa.NOALLOC_SCRATCH_BYTES
+    assert L.paged_attn_verify_noalloc_e4m3(c.q, ctypes.byref(pool), c.table, 8, c.lens,
+                                            1 << 15, 8, 6, 1, 256, c.sm, c.ks, 1.0,
+                                            ctypes.byref(huge), out, None) == PA_ESCRATCH
 
 
 def test_verify_batch_rejects_bad_arguments(L):
