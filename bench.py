@@ -146,40 +146,58 @@ class DenseBench:
     def run_graph(self, steps: int, warmup: int, rotate: bool):
         """Per-call time of verify + combine replayed from a HIP graph.
 
-        GRAPH_CALLS consecutive calls (rotating over the pool copies when
-        rotate) are captured once and the graph is replayed; an event follows
-        every replay.  Returns ms per call and sets self.pcts (per-call
-        percentiles over the replays)."""
+        A graph of c = gcd(steps, GRAPH_CALLS) consecutive calls (rotating over
+        the pool copies when rotate) is captured once.  After at least `warmup`
+        untimed calls, exactly `steps` calls (steps / c replays) are timed
+        between two synchronisations; that gives ms per call.  A separate
+        sample of PCT_REPLAYS replays, an event after each, sets self.pcts (the
+        per-call percentiles), so that they rest on at least 50 samples
+        whatever `steps` is."""
         torch = self.torch
+        calls = math.gcd(max(1, steps), GRAPH_CALLS)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for i in range(GRAPH_CALLS):
+            for i in range(calls):
                 self.verify(i if rotate else 0)
                 self.combine()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(GRAPH_CALLS):
+            for i in range(calls):
                 self.verify(i if rotate else 0)
                 self.combine()
         torch.cuda.synchronize()
-        reps = max(1, steps // GRAPH_CALLS)
-        for _ in range(max(1, warmup // GRAPH_CALLS)):
+        for _ in range(max(1, -(-warmup // calls))):
             g.replay()
         torch.cuda.synchronize()
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        reps = max(1, steps // calls)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(PCT_REPLAYS + 1)]
         marks[0].record()
-        for k in range(reps):
+        for k in range(PCT_REPLAYS):
             g.replay()
             marks[k + 1].record()
         torch.cuda.synchronize()
-        total_ms = marks[0].elapsed_time(marks[reps])
-        self.pcts = percentiles([marks[k].elapsed_time(marks[k + 1]) / GRAPH_CALLS
-                                 for k in range(reps)], GRAPH_CALLS)
+        self.pcts = percentiles([marks[k].elapsed_time(marks[k + 1]) / calls
+                                 for k in range(PCT_REPLAYS)], calls)
         del g
-        return total_ms / (reps * GRAPH_CALLS)
+        return total_ms / (reps * calls)
+
+    def output(self):
+        """One verify + combine on the first pool copy, as float64 on the host."""
+        self.verify(0)
+        self.combine()
+        self.torch.cuda.synchronize()
+        return self.out.float().cpu().numpy().astype("float64").reshape(self.out.shape)
 
     def run(self, steps: int, warmup: int, rotate: bool):
         """Time `steps` eager calls; returns (ms per call, mean and median verify-kernel ms).
@@ -213,7 +231,8 @@ class DenseBench:
 
 
 SAMPLE = 10          # eager calls per timing sample
-GRAPH_CALLS = 10     # verify + combine calls captured in one graph
+GRAPH_CALLS = 10     # verify + combine calls captured in one graph (at most)
+PCT_REPLAYS = 60     # graph replays behind the per-call percentiles
 
 
 def percentiles(xs, calls_per_sample: int):
@@ -289,17 +308,53 @@ def measure(b, steps: int, warmup: int) -> dict:
     _, h_vk, _ = b.run(steps, warmup, rotate=False)
     return {"us": c_ms * 1e3, "pcts": c_pcts, "eager_us": e_ms * 1e3, "verify_us": vk * 1e3,
             "verify_med_us": vmed * 1e3, "hot_us": h_ms * 1e3, "hot_pcts": h_pcts,
-            "hot_verify_us": h_vk * 1e3}
+            "hot_verify_us": h_vk * 1e3, "out": b.output()}
 
 
 def sweep_entry(name: str, kv_bytes: int, plan, m: dict, **extra) -> dict:
     gb = lambda us: round(kv_bytes / (us * 1e-6) / 1e9, 1)
     return {"workload": name, **extra, "kv_bytes": kv_bytes, "splits": plan.num_splits,
             "us_per_call": round(m["us"], 3), "gbs": gb(m["us"]),
+            "us_per_call_pcts": m["pcts"],
             "verify_us": round(m["verify_us"], 3), "verify_gbs": gb(m["verify_us"]),
             "eager_us_per_call": round(m["eager_us"], 3),
             "hot_us_per_call": round(m["hot_us"], 3), "hot_gbs": gb(m["hot_us"]),
             "hot_verify_us": round(m["hot_verify_us"], 3)}
+
+
+def error_figures(gpu, ref) -> dict:
+    """The GPU output against the FP64 oracle output o: rel-L2 and max-abs, with
+    the FP16 output-rounding floor of o beside each (rel-L2 of fp16(o), and
+    max |fp16(o) - o|), as the design note "DFlash2 E4M3 attention with FP32
+    state" reports its errors ("Observability and reproduction")."""
+    import numpy as np
+
+    gpu = np.asarray(gpu, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    fin = np.isfinite(ref)
+    if not np.array_equal(np.isfinite(gpu), fin):
+        return {"finite_pattern_matches": False}
+    g, o = gpu[fin], ref[fin]
+    r16 = o.astype(np.float16).astype(np.float64)
+    norm = float(np.linalg.norm(o)) or 1.0
+    return {"rel_l2": float(f"{np.linalg.norm(g - o) / norm:.4e}"),
+            "floor_rel_l2": float(f"{np.linalg.norm(r16 - o) / norm:.4e}"),
+            "max_abs": float(f"{np.abs(g - o).max(initial=0.0):.4e}"),
+            "floor_abs": float(f"{np.abs(r16 - o).max(initial=0.0):.4e}")}
+
+
+def oracle_output(orc, w, threads: int):
+    """The FP64 oracle's output for any of the bench workloads."""
+    import numpy as np
+
+    if hasattr(w, "sel_tokens"):
+        return orc.qsa_tokens_workload(w, nthreads=threads)
+    if hasattr(w, "sel_blocks"):
+        return orc.qsa_workload(w, nthreads=threads)
+    if hasattr(w, "request"):
+        return np.stack([orc.dense_workload(w.request(b), nthreads=threads)
+                         for b in range(w.batch)])
+    return orc.dense_workload(w, nthreads=threads)
 
 
 class BatchBench(DenseBench):
@@ -434,28 +489,42 @@ def copies_for(pool_bytes: int) -> int:
     return max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
 
 
-def cpu_baseline(w, max_seconds: float = 20.0):
+def cpu_baseline(w, outputs: dict, max_seconds: float = 20.0):
+    """The FP64 oracle timed on the host on the headline workload, and run once
+    on every workload the bench measured, whose outputs (`outputs`: name ->
+    (workload, GPU output)) it is compared with (the accuracy figures).
+
+    Threads: the CPUs this process may use, at most 16 (the host CPUs a GPU machine
+    allots to one GPU); the host's CPU count is reported beside it."""
     import oracle
 
     orc = oracle.get()
-    threads = max(1, min(16, os.cpu_count() or 1))
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    threads = max(1, min(16, avail))
     times = []
     t_start = time.perf_counter()
+    ref = None
     while len(times) < 3 and (time.perf_counter() - t_start) < max_seconds:
         t0 = time.perf_counter()
-        orc.dense_workload(w, nthreads=threads)
+        ref = orc.dense_workload(w, nthreads=threads)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     t0 = time.perf_counter()
     orc.dense_workload(w, nthreads=1)
     t1 = time.perf_counter() - t0
+    accuracy = {}
+    for name, (wk, gpu) in outputs.items():
+        o = ref if name == w.name else oracle_output(orc, wk, threads)
+        accuracy[name] = error_figures(gpu, o)
     return {"value": round(w.kv_bytes() / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole {w.name} workload (all {w.q_rows} rows x {w.num_heads} heads), "
                       f"FP64 oracle on {threads} threads, median of {len(times)} runs, "
                       f"{t * 1e3:.1f} ms per call",
+            "host_cpus": os.cpu_count(), "cpus_available": avail,
             "value_1thread": round(w.kv_bytes() / t1 / 1e9, 4),
-            "sample_1thread": f"the same workload on 1 thread, one run, {t1 * 1e3:.1f} ms"}
+            "sample_1thread": f"the same workload on 1 thread, one run, {t1 * 1e3:.1f} ms"}, \
+        accuracy
 
 
 def traffic_from_profile(src_hash: str, workload: str):
@@ -523,6 +592,7 @@ def main():
         f"verify {m['hot_verify_us']:.2f} us")
     gbs = b.kv_bytes / (m["us"] * 1e-6) / 1e9
     achieved = b.kv_bytes / (m["verify_us"] * 1e-6) / 1e9
+    outputs = {w.name: (w, m.pop("out"))}
     combines = b.time_combines()
     log(f"[bench] combine {combines['combine_us']:.2f} us, with LSE {combines['combine_lse_us']:.2f} us")
     plan = b.plan
@@ -536,28 +606,35 @@ def main():
             log(f"[bench] sweep {name}")
             ws = wl.cached(name)
             bs = DenseBench(ws, copies_for(2 * ws.k_pool.size), args.kernel, 0)
-            sweep.append(sweep_entry(ws.name, bs.kv_bytes, bs.plan, measure(bs, steps, args.warmup),
-                                     ctx=ws.max_tokens))
+            ms = measure(bs, steps, args.warmup)
+            outputs[ws.name] = (ws, ms.pop("out"))
+            sweep.append(sweep_entry(ws.name, bs.kv_bytes, bs.plan, ms, ctx=ws.max_tokens))
             del bs
             torch.cuda.empty_cache()
         log("[bench] sweep c4 (QSA)")
         wq = wl.cached("c4")
         bq = QsaBench(wq, copies_for(2 * wq.k_pool.size), args.kernel)
-        sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, measure(bq, steps, args.warmup),
+        mq = measure(bq, steps, args.warmup)
+        outputs[wq.name] = (wq, mq.pop("out"))
+        sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, mq,
                                  units=wq.batch * wq.num_kv_heads))
         del bq
         torch.cuda.empty_cache()
         log("[bench] sweep c4tok (QSA over token ids)")
         wt = wl.cached("c4tok")
         bt = QsaTokensBench(wt, copies_for(2 * wt.k_pool.size), args.kernel)
-        sweep.append(sweep_entry(wt.name, bt.kv_bytes, bt.plan, measure(bt, steps, args.warmup),
+        mt = measure(bt, steps, args.warmup)
+        outputs[wt.name] = (wt, mt.pop("out"))
+        sweep.append(sweep_entry(wt.name, bt.kv_bytes, bt.plan, mt,
                                  units=wt.batch * wt.num_kv_heads))
         del bt
         torch.cuda.empty_cache()
         log("[bench] sweep batch (independent requests)")
         wb = wl.cached("batch")
         bb = BatchBench(wb, copies_for(2 * wb.k_pool.size), args.kernel)
-        sweep.append(sweep_entry(wb.name, bb.kv_bytes, bb.plan, measure(bb, steps, args.warmup),
+        mb = measure(bb, steps, args.warmup)
+        outputs[wb.name] = (wb, mb.pop("out"))
+        sweep.append(sweep_entry(wb.name, bb.kv_bytes, bb.plan, mb,
                                  units=wb.batch * wb.num_kv_heads))
         del bb
         torch.cuda.empty_cache()
@@ -575,10 +652,10 @@ def main():
     log(f"[bench] read probe over {w.kv_bytes()} B, cold: {same_size['us']:.2f} us, "
         f"{same_size['gbs']:.0f} GB/s")
 
-    cpu = None
+    cpu, accuracy = None, None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(w)
+        log("[bench] cpu baseline (oracle), and the oracle's outputs for the accuracy figures")
+        cpu, accuracy = cpu_baseline(w, outputs)
 
     kernel_name = {0: "auto", 1: "simple", 2: "mfma"}[plan.kernel]
     traffic = traffic_from_profile(src_hash, w.name)
@@ -618,8 +695,10 @@ def main():
         "combine": combines,
         "cache_write": cache_write,
         "cpu_baseline": cpu,
+        "accuracy": accuracy,
         "sweep": sweep,
         "source_hash": src_hash,
+        "build_id": pa.build_id(),
     }
     print(json.dumps(line), flush=True)
 

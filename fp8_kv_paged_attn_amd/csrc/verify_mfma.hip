@@ -242,14 +242,20 @@ __device__ __forceinline__ uint32_t or_over_groups(uint32_t v)
     return t0 | t1;
 }
 
-// E4M3 NaN codes (S.1111.111) of the four bytes of x become 0x00; returns a
-// 4-bit mask of the bytes that were NaN.  (x & 0x7F) + 1 carries into bit 7
-// of a byte exactly when its low seven bits are all ones, and never into the
-// next byte.
+// Bit 7 of each byte of the result is set where that byte of x is an E4M3 NaN
+// code (S.1111.111): (x & 0x7F) + 1 carries into bit 7 of a byte exactly when
+// its low seven bits are all ones, and never into the next byte.
+__device__ __forceinline__ uint32_t nan_byte_marks(uint32_t x)
+{
+    return ((x & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+}
+
+// The NaN codes of the four bytes of x become 0x00; returns a 4-bit mask of
+// the bytes that were NaN.
 __device__ __forceinline__ uint32_t drop_nan_bytes(int &x)
 {
     const uint32_t u = (uint32_t)x;
-    const uint32_t hit = ((u & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    const uint32_t hit = nan_byte_marks(u);
     x = (int)(u & ~((hit >> 7) * 0xFFu));
     return ((hit >> 7) & 1u) | ((hit >> 14) & 2u) | ((hit >> 21) & 4u) | ((hit >> 28) & 8u);
 }
@@ -265,14 +271,46 @@ __device__ __forceinline__ void scale_in_place(f32x4 &x, float f)
     x = t;
 }
 
+// Reductions over each row of 16 lanes by DPP rotations within the row
+// (row_ror 8, 4, 2, 1): every lane ends with its row's result, with no LDS
+// round trip (a shuffle through ds_bpermute costs one per step).
+template <int ROR>
+__device__ __forceinline__ int row_ror(int v)
+{
+    return __builtin_amdgcn_update_dpp(v, v, 0x120 + ROR, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int row16_max(int v)
+{
+    v = max(v, row_ror<8>(v));
+    v = max(v, row_ror<4>(v));
+    v = max(v, row_ror<2>(v));
+    return max(v, row_ror<1>(v));
+}
+
+__device__ __forceinline__ int row16_min(int v)
+{
+    v = min(v, row_ror<8>(v));
+    v = min(v, row_ror<4>(v));
+    v = min(v, row_ror<2>(v));
+    return min(v, row_ror<1>(v));
+}
+
 // Max over lanes 0..15 (the row lengths of one request), broadcast to the wave.
 __device__ __forceinline__ int max16_broadcast(int v)
 {
-    v = max(v, __shfl_xor(v, 1, 64));
-    v = max(v, __shfl_xor(v, 2, 64));
-    v = max(v, __shfl_xor(v, 4, 64));
-    v = max(v, __shfl_xor(v, 8, 64));
-    return __builtin_amdgcn_readfirstlane(v);
+    return __builtin_amdgcn_readfirstlane(row16_max(v));
+}
+
+// Max over the whole wave: each row of 16, then across the four rows.
+__device__ __forceinline__ int wave_max(int v)
+{
+    v = row16_max(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const int r0 = r[0], r1 = r[1];
+    const auto t = __builtin_amdgcn_permlane16_swap(max(r0, r1), max(r0, r1), false, false);
+    const int t0 = t[0], t1 = t[1];
+    return max(t0, t1);
 }
 
 template <int D>
@@ -338,11 +376,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     uint8_t *const k_st = smem;                               // [2][kWaves][BLOCK]
     uint8_t *const v_st = smem + 2 * kWaves * C::BLOCK;       // [2][kWaves][BLOCK]
 
+    // With pages of at least 32 tokens a 32-row block spans at most two page
+    // slots and is loaded from one page lookup (two_slot).
+    const bool two_slot = !TOK && ps >= kSub && a.token_stride < (1 << 25);
+
     // ---- one round trip: Q (to LDS), row lengths, page table ----------------
     // Q is fetched once per workgroup with direct-to-LDS loads into the K0
     // stage (free until the first K/V loads), rows of 2D bytes with their
     // 16-byte chunks XOR-swizzled by row, and read into registers from there.
     // Q row r of this KV unit is query row r / G, head kvh*G + r % G.
+    uint8_t *const q_st = k_st;
     constexpr int kQRowsPerDma = 1024 / (2 * D);
     constexpr int kQLanesPerRow = 2 * D / 16;
     {
@@ -354,20 +397,30 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 const int qi = (row0 + r) / G, h = kvh * G + (row0 + r - qi * G);
                 const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + qi) * a.num_heads + h) * D;
                 dma16((const uint8_t *)qrow + 16 * (c ^ (r & 15)),
-                      __builtin_amdgcn_readfirstlane(lds_addr(smem + i * 1024)));
+                      __builtin_amdgcn_readfirstlane(lds_addr(q_st + i * 1024)));
             }
         }
     }
-    int lmine = 0;                                  // lane i < q_rows: length of query row i
-    if (lane < a.q_rows) {
-        lmine = a.row_lens[(int64_t)b * a.q_rows + lane];
-        lmine = lmine < 0 ? 0 : (lmine > a.len_cap ? a.len_cap : lmine);
-    }
+    // lane i < q_rows: length of query row i, clamped where it is first
+    // needed, so that nothing waits for the load before the table reads are
+    // issued
+    int lraw = 0;
+    if (lane < a.q_rows)
+        lraw = a.row_lens[(int64_t)b * a.q_rows + lane];
+    auto clamp_len = [&](int l) __attribute__((always_inline)) {
+        return l < 0 ? 0 : (l > a.len_cap ? a.len_cap : l);
+    };
     // positions per split: fixed, or (split_by_length) from this unit's
     // longest row, which costs one more round trip before the table reads
+    // (the empty asm statements keep each use where it is written: the
+    // compiler would otherwise hoist one clamp above the branch, right after
+    // the load, and wait for the load there)
     int tps = a.tokens_per_split;
-    if (a.split_by_length)
-        tps = split_span(max16_broadcast(lmine), a.num_splits);
+    if (a.split_by_length) {
+        int l = lraw;
+        asm volatile("" : "+v"(l));
+        tps = split_span(max16_broadcast(clamp_len(l)), a.num_splits);
+    }
     const int lo = split * tps;
     const int hi_list = min(lo + tps, a.list_len);
     const int32_t *table = a.block_table + (int64_t)b * a.table_stride;
@@ -387,95 +440,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             ent[k] = SPARSE ? a.sel[((int64_t)b * a.num_kv_heads + kvh) * a.topk + slot0 + i]
                             : table[slot0 + i];
     }
-    const int lmax = max16_broadcast(lmine);
-    int lrow[kRowBlocks];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-        const int lr = __shfl(lmine, r < R ? (row0 + r) / G : 0, 64);
-        lrow[rb] = r < R ? lr : 0;
-    }
-    // row blocks up to the last one with a row that sees a token
-    int nrb = 1;
-#pragma unroll
-    for (int rb = 1; rb < kRowBlocks; ++rb)
-        if (__any(lrow[rb] > 0))
-            nrb = rb + 1;
-    int hi = hi_list;
-    if (!SPARSE)
-        hi = min(hi, lmax);
-    // Per row block, the smallest length among the rows that can see tokens of
-    // this split (dense: length past the split start; sparse: nonzero).  A
-    // block whose tokens all lie below it is seen whole by every such row, and
-    // is processed without masks; rows that see nothing of the split are reset
-    // to the empty state at the end.
-    // Dense blocks are never unmasked past hi, where the K bytes may be NaN.
-    int minl[kRowBlocks];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        int v = SPARSE ? INT32_MAX : hi;
-        if (rb * 16 + n < R && lrow[rb] > (SPARSE ? 0 : lo))
-            v = SPARSE ? lrow[rb] : min(lrow[rb], hi);
-        v = min(v, __shfl_xor(v, 1, 64));
-        v = min(v, __shfl_xor(v, 2, 64));
-        v = min(v, __shfl_xor(v, 4, 64));
-        v = min(v, __shfl_xor(v, 8, 64));
-        minl[rb] = __builtin_amdgcn_readfirstlane(v);
-    }
-#pragma unroll
-    for (int k = 0; k < kEnt; ++k) {
-        const int i = tid + k * kThreads;
-        if (i < nslots) {
-            int phys = -1, tb = 0;
-            if (!SPARSE) {
-                phys = ent[k];
-                tb = (slot0 + i) * ps;
-            } else if (TOK) {
-                // a token no row sees keeps phys -1; lmax <= the table's
-                // capacity, so a token below it has a table entry
-                const int t = ent[k];
-                if (t >= 0 && t < lmax) {
-                    phys = table[divp(t, dm)];
-                    tb = t;
-                }
-            } else {
-                const int blk = ent[k];
-                if (blk >= 0 && (int64_t)blk * ps < lmax) {
-                    phys = table[blk];
-                    tb = blk * ps;
-                }
-            }
-            slots[i] = int2v{phys, tb};
-        }
-    }
-    wait_vmcnt<0>();   // this wave's Q loads
-    __syncthreads();
-
-    // Q^T is the B operand of S^T = K Q^T: lane (n, g) holds row 16rb + n.
-    // The head dimension is walked in a permuted order that both operands
-    // share: MFMA k-block kb = 2t + e, lane group g covers dims
-    // 64t + 16g + 8e .. +7 (16-byte chunk 8t + 2g + e of the row), so that one
-    // 16-byte LDS chunk of K (dims 64t + 16g .. +15) feeds two consecutive
-    // k-blocks.
-    QFrag qf[kRowBlocks][C::KB];
-#pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const int r = rb * 16 + n;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            int4v v = int4v{0, 0, 0, 0};
-            if (r < R) {
-                const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
-                v = *(const int4v *)(smem + r * 2 * D + 16 * (c ^ (r & 15)));
-            }
-            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
-        }
-    }
-    barrier_lds();     // everyone has its Q before the K0 stage is refilled
-
+    // the longest row length and the split's end, known once the lengths
+    // are in (the addressing helpers below read them only after that)
+    int lmax = 0, hi = hi_list;
     const int64_t head_off = (int64_t)kvh * a.head_stride;
-    // this wave's blocks: positions lo + 32 (4j + w), j = 0 .. nms-1
-    const int nms = hi > lo ? (hi - lo + kMacro - 1) / kMacro : 0;
 
     // Position -> (byte offset of the K/V head row, token, valid).  Branch-free;
     // the slot cache is the only table read.
@@ -511,7 +479,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // receives the token of each row, INT32_MAX for rows no query sees, and
     // blk_tmax the largest of them when it is known (INT32_MAX otherwise).
     const int cp = lane % C::LANES_PER_ROW;
-    const bool two_slot = !TOK && ps >= kSub && a.token_stride < (1 << 25);
     int32_t loff[C::DMA];
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
@@ -523,31 +490,44 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // two page slots: rows [0, end_a) come from the first at base_a + row
     // offset, rows [na, end_b) from the second at base_b + row offset.
     struct BlockRef {
-        int na, ua, end_a, end_b, tb_a, tb_b;
+        int na, ua, end_a, end_b, tb_a, tb_b, phys_a, phys_b;
         int64_t base_a, base_b;
+    };
+    // The page reference of a 32-row block at position pos0 whose rows
+    // [0, na) lie in page phys_a (first token tb_a) and the rest in phys_b
+    // (first token tb_b), rows at or past end loading the dummy address.
+    auto make_ref = [&](int pos0, int end, int phys_a, int tb_a, int phys_b,
+                        int tb_b) __attribute__((always_inline)) -> BlockRef {
+        BlockRef br;
+        const int sa = divp(pos0, dm);
+        br.ua = pos0 - sa * ps;
+        br.na = min(kSub, ps - br.ua);
+        br.phys_a = phys_a;
+        br.phys_b = phys_b;
+        br.tb_a = tb_a;
+        br.tb_b = tb_b;
+        const int hip = end - pos0;
+        br.end_a = min(br.na, hip);
+        br.end_b = hip;
+        br.base_a = (int64_t)phys_a * a.page_stride + (int64_t)br.ua * a.token_stride + head_off;
+        br.base_b = (int64_t)phys_b * a.page_stride - (int64_t)br.na * a.token_stride + head_off;
+        return br;
     };
     auto lookup = [&](int j) __attribute__((always_inline)) -> BlockRef {
         BlockRef br = {};
         if (two_slot) {
             const int pos0 = lo + (j * kWaves + w) * kSub;
             const int sa = divp(pos0, dm);
-            br.ua = pos0 - sa * ps;
-            br.na = min(kSub, ps - br.ua);
             const int2v ea = slots[min(max(sa - slot0, 0), kSlots - 1)];
             const int2v eb = slots[min(max(sa + 1 - slot0, 0), kSlots - 1)];
-            const int phys_a = __builtin_amdgcn_readfirstlane(ea.x);
-            br.tb_a = __builtin_amdgcn_readfirstlane(ea.y);
-            const int phys_b = __builtin_amdgcn_readfirstlane(eb.x);
-            br.tb_b = __builtin_amdgcn_readfirstlane(eb.y);
-            const int hip = hi - pos0;
-            br.end_a = min(br.na, hip);
-            br.end_b = hip;
+            br = make_ref(pos0, hi, __builtin_amdgcn_readfirstlane(ea.x),
+                          __builtin_amdgcn_readfirstlane(ea.y),
+                          __builtin_amdgcn_readfirstlane(eb.x),
+                          __builtin_amdgcn_readfirstlane(eb.y));
             if (SPARSE) {
-                br.end_a = phys_a >= 0 ? min(br.end_a, lmax - (br.tb_a + br.ua)) : 0;
-                br.end_b = phys_b >= 0 ? min(br.end_b, br.na + lmax - br.tb_b) : 0;
+                br.end_a = br.phys_a >= 0 ? min(br.end_a, lmax - (br.tb_a + br.ua)) : 0;
+                br.end_b = br.phys_b >= 0 ? min(br.end_b, br.na + lmax - br.tb_b) : 0;
             }
-            br.base_a = (int64_t)phys_a * a.page_stride + (int64_t)br.ua * a.token_stride + head_off;
-            br.base_b = (int64_t)phys_b * a.page_stride - (int64_t)br.na * a.token_stride + head_off;
         }
         return br;
     };
@@ -606,16 +586,98 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     tokst[row] = ok ? t : INT32_MAX;
                 tm = max(tm, ok ? t : INT32_MAX);
             }
-            if (TOK && tokst != nullptr) {
-                // token ids are unordered: the block's largest comes from the wave
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1)
-                    tm = max(tm, __shfl_xor(tm, o, 64));
-            }
+            if (TOK && tokst != nullptr)
+                tm = wave_max(tm);   // token ids are unordered: the block's largest
             if (SPARSE && tokst != nullptr && lane == 0)
                 *tmaxp = TOK ? tm : INT32_MAX;
         }
     };
+
+    asm volatile("" : "+v"(lraw));
+    const int lmine = clamp_len(lraw);
+    lmax = max16_broadcast(lmine);
+    int lrow[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = rb * 16 + n;
+        const int lr = __shfl(lmine, r < R ? (row0 + r) / G : 0, 64);
+        lrow[rb] = r < R ? lr : 0;
+    }
+    // row blocks up to the last one with a row that sees a token
+    int nrb = 1;
+#pragma unroll
+    for (int rb = 1; rb < kRowBlocks; ++rb)
+        if (__any(lrow[rb] > 0))
+            nrb = rb + 1;
+    if (!SPARSE)
+        hi = min(hi, lmax);
+    // Per row block, the smallest length among the rows that can see tokens of
+    // this split (dense: length past the split start; sparse: nonzero).  A
+    // block whose tokens all lie below it is seen whole by every such row, and
+    // is processed without masks; rows that see nothing of the split are reset
+    // to the empty state at the end.
+    // Dense blocks are never unmasked past hi, where the K bytes may be NaN.
+    int minl[kRowBlocks];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        int v = SPARSE ? INT32_MAX : hi;
+        if (rb * 16 + n < R && lrow[rb] > (SPARSE ? 0 : lo))
+            v = SPARSE ? lrow[rb] : min(lrow[rb], hi);
+        minl[rb] = __builtin_amdgcn_readfirstlane(row16_min(v));   // rows of lanes share n
+    }
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < nslots) {
+            int phys = -1, tb = 0;
+            if (!SPARSE) {
+                phys = ent[k];
+                tb = (slot0 + i) * ps;
+            } else if (TOK) {
+                // a token no row sees keeps phys -1; lmax <= the table's
+                // capacity, so a token below it has a table entry
+                const int t = ent[k];
+                if (t >= 0 && t < lmax) {
+                    phys = table[divp(t, dm)];
+                    tb = t;
+                }
+            } else {
+                const int blk = ent[k];
+                if (blk >= 0 && (int64_t)blk * ps < lmax) {
+                    phys = table[blk];
+                    tb = blk * ps;
+                }
+            }
+            slots[i] = int2v{phys, tb};
+        }
+    }
+    wait_vmcnt<0>();   // this wave's Q loads
+    __syncthreads();
+
+    // Q^T is the B operand of S^T = K Q^T: lane (n, g) holds row 16rb + n.
+    // The head dimension is walked in a permuted order that both operands
+    // share: MFMA k-block kb = 2t + e, lane group g covers dims
+    // 64t + 16g + 8e .. +7 (16-byte chunk 8t + 2g + e of the row), so that one
+    // 16-byte LDS chunk of K (dims 64t + 16g .. +15) feeds two consecutive
+    // k-blocks.
+    QFrag qf[kRowBlocks][C::KB];
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const int r = rb * 16 + n;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            int4v v = int4v{0, 0, 0, 0};
+            if (r < R && rb < nrb) {          // row blocks past nrb are never used
+                const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
+                v = *(const int4v *)(q_st + r * 2 * D + 16 * (c ^ (r & 15)));
+            }
+            qf[rb][kb] = __builtin_bit_cast(QFrag, v);
+        }
+    }
+    barrier_lds();     // everyone has its Q before its stage is refilled
+
+    // this wave's blocks: positions lo + 32 (4j + w), j = 0 .. nms-1
+    const int nms = hi > lo ? (hi - lo + kMacro - 1) / kMacro : 0;
 
     // ---- per-wave state ------------------------------------------------------
     f32x4 acc[kRowBlocks][C::DB];
@@ -821,12 +883,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     (__attribute__((address_space(3))) int2v *)(uintptr_t)(vaddr ^ (uint32_t)(db << 4)));
             __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of their uses
             // Lane (n, g) holds V[token 8g + j][column 16 db + n] in byte j of
-            // vraw[db].  A block that some live row does not see whole has its
-            // NaN bytes replaced by 0, and their positions recorded as one
+            // vraw[db].  In a block that some live row does not see whole, a
+            // NaN byte would reach rows that mask its token (p = 0 times NaN):
+            // such a block is checked for NaN codes, and only if it holds any
+            // are they replaced by 0 and their positions recorded as one
             // 32-bit token mask per column ([D] words, byte g from lane group
             // g) in this wave's K stage, which holds nothing until K(j+2).
             uint8_t *const nanw = kst + w * C::BLOCK;
-            if (!all_full) {
+            bool has_nan = false;
+            if (__builtin_expect(!all_full, 0)) {
+                uint32_t hit = 0;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+                    hit |= nan_byte_marks((uint32_t)vraw[db].x) | nan_byte_marks((uint32_t)vraw[db].y);
+                has_nan = __any(hit != 0);
+            }
+            if (__builtin_expect(has_nan, 0)) {
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
                     int x = vraw[db].x, y = vraw[db].y;
@@ -846,7 +918,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 for (int rb = 0; rb < NRB; ++rb)
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[rb], acc[rb][db], 0, 0, 0);
             }
-            if (!all_full) {
+            if (__builtin_expect(has_nan, 0)) {
                 // acc[rb][db] lane (n, g) holds row 16 rb + n, columns
                 // 16 db + 4 g + k; bit 4 db + k of nan_hit[rb] records that the
                 // row sees a NaN byte of that column.  Row visibility over the
@@ -927,7 +999,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb)
         any_nan = any_nan || nan_hit[rb] != 0;
-    if (__any(any_nan)) {
+    if (__builtin_expect(__any(any_nan), 0)) {
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
 #pragma unroll
