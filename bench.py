@@ -376,8 +376,10 @@ class BatchBench(DenseBench):
         self.table = torch.from_numpy(w.block_table.astype(np.int32)).to(dev)
         self.lens = torch.from_numpy(w.row_lens.astype(np.int32)).to(dev)
         G = w.num_heads // w.num_kv_heads
+        # one ragged split plan over the whole batch: the splits are shared out
+        # over the requests in proportion to their lengths
         self.plan = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
-                            w.page_size, splits=w.num_splits, kernel=kernel)
+                            w.page_size, "batch", splits=w.num_splits, kernel=kernel)
         self.rows = w.num_rows
         self.ws = pa.make_workspace(self.plan, self.rows, w.head_dim, dev)
         self.out = torch.empty((w.batch, w.q_rows, w.num_heads, w.head_dim),
@@ -389,6 +391,11 @@ class BatchBench(DenseBench):
         w = self.w
         self.pa.paged_attn_verify_batch_e4m3(self.q, k, v, self.table, self.lens, w.sm_scale,
                                              w.k_scale, self.plan, self.ws)
+
+    def combine(self):
+        w = self.w
+        self.pa.paged_attn_combine_batch_fp32(self.ws, self.plan, w.batch, w.q_rows, w.num_heads,
+                                              w.num_kv_heads, w.head_dim, w.v_scale, self.out)
 
 
 def time_cache_write(torch, pa, tokens: int, reps: int = 20) -> dict:

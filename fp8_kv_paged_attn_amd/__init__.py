@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn_e4m3.so")
 ABI_VERSION = 2
 
 PA_KERNEL = {"auto": 0, "simple": 1, "mfma": 2}
-PA_SELECTION = {"dense": 0, "blocks": 1, "tokens": 2}
+PA_SELECTION = {"dense": 0, "blocks": 1, "tokens": 2, "batch": 3}
 
 
 class PaKvPool(ctypes.Structure):
@@ -44,7 +44,7 @@ class PaPlan(ctypes.Structure):
                 ("rows_per_kv_unit", ctypes.c_int32), ("num_kv_units", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("selection", ctypes.c_int32), ("ws_acc_bytes", ctypes.c_int64),
-                ("ws_stat_bytes", ctypes.c_int64)]
+                ("ws_stat_bytes", ctypes.c_int64), ("ws_index_bytes", ctypes.c_int64)]
 
     def __repr__(self):
         return (f"PaPlan(splits={self.num_splits}, tokens_per_split={self.tokens_per_split}, "
@@ -54,7 +54,8 @@ class PaPlan(ctypes.Structure):
 
 class PaWorkspace(ctypes.Structure):
     _fields_ = [("acc", ctypes.c_void_p), ("max", ctypes.c_void_p), ("sum", ctypes.c_void_p),
-                ("acc_bytes", ctypes.c_int64), ("stat_bytes", ctypes.c_int64)]
+                ("acc_bytes", ctypes.c_int64), ("stat_bytes", ctypes.c_int64),
+                ("index", ctypes.c_void_p), ("index_bytes", ctypes.c_int64)]
 
 
 EXPORTS = ("paged_attn_abi_version", "paged_attn_build_id", "paged_attn_status_string",
@@ -63,7 +64,7 @@ EXPORTS = ("paged_attn_abi_version", "paged_attn_build_id", "paged_attn_status_s
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
            "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
            "paged_attn_cache_write_e4m3", "qsa_sparse_verify_tokens_e4m3",
-           "paged_attn_verify_noalloc_e4m3")
+           "paged_attn_verify_noalloc_e4m3", "paged_attn_combine_batch_fp32")
 
 _LIB = None
 
@@ -101,6 +102,10 @@ def lib() -> ctypes.CDLL:
                                                i32, i32, i32, f32, f32, ctypes.POINTER(PaPlan),
                                                ctypes.POINTER(PaWorkspace), p]
     L.paged_attn_verify_batch_e4m3.restype = i32
+    L.paged_attn_combine_batch_fp32.argtypes = [ctypes.POINTER(PaWorkspace),
+                                                ctypes.POINTER(PaPlan), i32, i32, i32, i32, i32,
+                                                f32, p, p]
+    L.paged_attn_combine_batch_fp32.restype = i32
     L.paged_attn_cache_write_e4m3.argtypes = [p, p, i64, i32, i32, p, ctypes.POINTER(PaKvPool),
                                               f32, f32, p]
     L.paged_attn_cache_write_e4m3.restype = i32
@@ -248,20 +253,31 @@ def _stream(device) -> int:
 
 
 def make_workspace(p: PaPlan, total_rows: int, head_dim: int, device):
+    """(acc, max, sum) for the plan; a batch plan (ragged splits) also gets the
+    split index, and its rows are one KV unit's (total_rows is not used)."""
     torch = _torch()
+    if p.selection == PA_SELECTION["batch"]:
+        total_rows = p.rows_per_kv_unit
     acc = torch.empty((p.num_splits, total_rows, head_dim), dtype=torch.float32, device=device)
     mx = torch.empty((p.num_splits, total_rows), dtype=torch.float32, device=device)
     sm = torch.empty((p.num_splits, total_rows), dtype=torch.float32, device=device)
+    if p.selection == PA_SELECTION["batch"]:
+        idx = torch.empty(p.num_kv_units + 1, dtype=torch.int32, device=device)
+        return acc, mx, sm, idx
     return acc, mx, sm
 
 
-def _ws(acc, mx, sm) -> PaWorkspace:
+def _ws(acc, mx, sm, index=None) -> PaWorkspace:
     torch = _torch()
     for t in (acc, mx, sm):
         if t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("workspace buffers must be contiguous float32")
+    if index is not None and (index.dtype != torch.int32 or not index.is_contiguous()):
+        raise ValueError("the split index must be a contiguous int32 tensor")
     return PaWorkspace(acc.data_ptr(), mx.data_ptr(), sm.data_ptr(),
-                       acc.numel() * 4, min(mx.numel(), sm.numel()) * 4)
+                       acc.numel() * 4, min(mx.numel(), sm.numel()) * 4,
+                       None if index is None else index.data_ptr(),
+                       0 if index is None else index.numel() * 4)
 
 
 def paged_attn_verify_e4m3(q, k_pool, v_pool, block_table, row_lens, max_tokens: int,
@@ -360,11 +376,30 @@ def paged_attn_cache_write_e4m3(k, v, slot_mapping, k_pool, v_pool, k_scale, v_s
     _check(rc, "paged_attn_cache_write_e4m3")
 
 
+def paged_attn_combine_batch_fp32(ws, p: PaPlan, batch: int, q_rows: int, num_heads: int,
+                                  num_kv_heads: int, head_dim: int, out_scale, out) -> None:
+    """FP32 combine of a batch's ragged partials (ws = (acc, max, sum, index) as
+    paged_attn_verify_batch_e4m3 wrote them with plan p) into out (float16,
+    [batch][q_rows][heads][head_dim] elements)."""
+    torch = _torch()
+    if len(ws) != 4:
+        raise ValueError("a batch workspace is (acc, max, sum, index)")
+    if out.dtype != torch.float16 or not out.is_contiguous() or \
+            out.numel() < batch * q_rows * num_heads * head_dim or out.device != ws[0].device:
+        raise ValueError("out must be a contiguous float16 tensor of batch*q_rows*heads*head_dim "
+                         "elements on the workspace's device")
+    rc = lib().paged_attn_combine_batch_fp32(ctypes.byref(_ws(*ws)), ctypes.byref(p), int(batch),
+                                             int(q_rows), int(num_heads), int(num_kv_heads),
+                                             int(head_dim), _scale(out_scale, "out_scale"),
+                                             out.data_ptr(), _stream(out.device))
+    _check(rc, "paged_attn_combine_batch_fp32")
+
+
 def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,
                             out) -> None:
     """FP32 combine of split partials into out (float16, [num_rows][head_dim] elements)."""
     torch = _torch()
-    acc, mx, sm = ws
+    acc, mx, sm = ws[:3]
     if out.dtype != torch.float16 or not out.is_contiguous() or out.numel() < num_rows * head_dim:
         raise ValueError("out must be a contiguous float16 tensor of num_rows*head_dim elements")
     for t in (acc, mx, sm):
@@ -385,7 +420,7 @@ def paged_attn_combine_fp32_lse(ws, num_splits: int, num_rows: int, head_dim: in
     [num_rows][head_dim] elements, and lse (float32, num_rows): the base-2 LSE of
     each row, for a merge across ranks."""
     torch = _torch()
-    acc, mx, sm = ws
+    acc, mx, sm = ws[:3]
     if out is None and out32 is None and lse is None:
         raise ValueError("give at least one of out, out32, lse")
     dev = acc.device
@@ -485,7 +520,7 @@ def verify_batch(q, k_pool, v_pool, block_table, row_lens, *, sm_scale, k_scale,
     Hkv = k_pool.shape[2]
     cap = block_table.shape[1] * k_pool.shape[1]
     if p is None:
-        p = plan(cap, qr * (H // Hkv), B * Hkv, D, k_pool.shape[1], splits=splits,
+        p = plan(cap, qr * (H // Hkv), B * Hkv, D, k_pool.shape[1], "batch", splits=splits,
                  kernel=kernel)
     if ws is None:
         ws = make_workspace(p, B * qr * H, D, q.device)
@@ -493,7 +528,7 @@ def verify_batch(q, k_pool, v_pool, block_table, row_lens, *, sm_scale, k_scale,
         out = torch.empty((B, qr, H, D), dtype=torch.float16, device=q.device)
     paged_attn_verify_batch_e4m3(q, k_pool, v_pool, block_table, row_lens, sm_scale, k_scale,
                                  p, ws)
-    paged_attn_combine_fp32(ws, p.num_splits, B * qr * H, D, v_scale, out)
+    paged_attn_combine_batch_fp32(ws, p, B, qr, H, Hkv, D, v_scale, out)
     return out
 
 

@@ -141,23 +141,37 @@ int32_t check_plan(const pa_plan *plan, int32_t list_len, int32_t rows_per_unit,
     if (plan->num_splits < 1 || plan->tokens_per_split < kTileTokens ||
         plan->tokens_per_split % kTileTokens != 0 || plan->num_splits > 65535)
         return PA_EPLAN;
-    const int64_t span = (int64_t)plan->num_splits * plan->tokens_per_split;
-    if (span < (int64_t)list_len || span > INT32_MAX)
-        return PA_EPLAN;
-    if ((int64_t)(plan->num_splits - 1) * plan->tokens_per_split >=
-        (int64_t)(list_len > 1 ? list_len : 1))
-        return PA_EPLAN;
     if (plan->kernel < PA_KERNEL_AUTO || plan->kernel > PA_KERNEL_MFMA)
         return PA_EPLAN;
     if (plan->kernel != PA_KERNEL_SIMPLE &&
         pa::mfma_slots_needed(plan->tokens_per_split, page_size, selection == PA_SEL_TOKENS) >
             pa::mfma_max_slots(head_dim))
         return PA_EPLAN;
+    if (selection == PA_SEL_BATCH) {
+        // a ragged batch: its splits are shared by all units, and there must be
+        // enough of them for every unit at full length at the plan's span (so
+        // the span the kernels derive from the lengths always fits them all)
+        const int64_t T = plan->tokens_per_split;
+        if ((int64_t)list_len + T > INT32_MAX)
+            return PA_EPLAN;
+        if ((int64_t)plan->num_splits < (int64_t)units * ((list_len + T - 1) / T))
+            return PA_EPLAN;
+        return PA_OK;
+    }
+    const int64_t span = (int64_t)plan->num_splits * plan->tokens_per_split;
+    if (span < (int64_t)list_len || span > INT32_MAX)
+        return PA_EPLAN;
+    if ((int64_t)(plan->num_splits - 1) * plan->tokens_per_split >=
+        (int64_t)(list_len > 1 ? list_len : 1))
+        return PA_EPLAN;
     return PA_OK;
 }
 
+// total_rows: rows of one split's partials (all output rows, or for a ragged
+// batch the rows of one unit); index_entries: split-index entries a ragged
+// batch writes (0: none)
 int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows,
-                 int32_t head_dim)
+                 int32_t head_dim, int64_t index_entries = 0)
 {
     if (!ws || !ws->acc || !ws->max || !ws->sum)
         return PA_EINVAL;
@@ -165,6 +179,12 @@ int32_t check_ws(const pa_workspace *ws, const pa_plan *plan, int64_t total_rows
     int64_t need_stat = (int64_t)plan->num_splits * total_rows * 4;
     if (ws->acc_bytes < need_acc || ws->stat_bytes < need_stat)
         return PA_EWORKSPACE;
+    if (index_entries > 0) {
+        if (!ws->index)
+            return PA_EINVAL;
+        if (ws->index_bytes < index_entries * 4)
+            return PA_EWORKSPACE;
+    }
     return PA_OK;
 }
 
@@ -423,10 +443,43 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
 {
     if (!out || max_tokens < 0 || rows_per_kv_unit < 1 || num_kv_units < 1 || head_dim < 1 ||
         requested_splits < 0 || page_size < 1 || selection < PA_SEL_DENSE ||
-        selection > PA_SEL_TOKENS)
+        selection > PA_SEL_BATCH)
         return PA_EINVAL;
     const int64_t cus = num_cus > 0 ? num_cus : device_cus();
     const int64_t tiles = max_tokens > 0 ? (max_tokens + kTileTokens - 1) / kTileTokens : 1;
+    const int64_t slots = pa::mfma_max_slots(head_dim);
+    if (selection == PA_SEL_BATCH) {
+        // a ragged batch: num_splits counts the splits of all units together,
+        // one workgroup per compute unit and 48-row chunk (or as requested),
+        // but at least enough for every unit at full length at the longest
+        // span the MFMA kernel takes
+        const int64_t chunks = ((int64_t)rows_per_kv_unit + 47) / 48;
+        int64_t T = (slots - 1) * (int64_t)page_size / kTileTokens * kTileTokens;
+        if (T > tiles * kTileTokens)
+            T = tiles * kTileTokens;
+        int64_t splits = requested_splits > 0 ? requested_splits : (cus + chunks - 1) / chunks;
+        const int64_t need = (int64_t)num_kv_units * (((int64_t)max_tokens + T - 1) / T);
+        if (splits < need)
+            splits = need;
+        if (splits < 1)
+            splits = 1;
+        if (splits > 65535 || (int64_t)max_tokens + T > INT32_MAX)
+            return PA_EUNSUPPORTED;
+        std::memset(out, 0, sizeof *out);
+        out->num_splits = (int32_t)splits;
+        out->tokens_per_split = (int32_t)T;
+        out->kernel = PA_KERNEL_AUTO;
+        out->max_tokens = max_tokens;
+        out->rows_per_kv_unit = rows_per_kv_unit;
+        out->num_kv_units = num_kv_units;
+        out->head_dim = head_dim;
+        out->page_size = page_size;
+        out->selection = selection;
+        out->ws_acc_bytes = splits * rows_per_kv_unit * head_dim * 4;
+        out->ws_stat_bytes = splits * rows_per_kv_unit * 4;
+        out->ws_index_bytes = ((int64_t)num_kv_units + 1) * 4;
+        return PA_OK;
+    }
     int64_t splits;
     if (requested_splits > 0) {
         splits = requested_splits;
@@ -451,7 +504,6 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     int64_t tps = tiles_per_split * kTileTokens;
     // longest split whose page slots (token ids: entries) fit the MFMA
     // kernel's cache: (T - 1) / page + 2 <= slots, i.e. T <= (slots - 1) * page
-    const int64_t slots = pa::mfma_max_slots(head_dim);
     int64_t tcap = selection == PA_SEL_TOKENS ? slots : (slots - 1) * (int64_t)page_size;
     tcap = tcap / kTileTokens * kTileTokens;
     if (tps > tcap)
@@ -570,12 +622,13 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     if ((rc = check_scales(sm_scale, k_scale)) != PA_OK)
         return rc;
     if ((rc = check_plan(plan, (int32_t)cap, rows_per_unit, batch * num_kv_heads, head_dim,
-                         kv->page_size, PA_SEL_DENSE)) != PA_OK)
+                         kv->page_size, PA_SEL_BATCH)) != PA_OK)
         return rc;
     const int64_t total_rows = (int64_t)batch * q_rows * num_heads;
     if (total_rows > 0x7FFFFFFF)
         return PA_EINVAL;
-    if ((rc = check_ws(ws, plan, total_rows, head_dim)) != PA_OK)
+    if ((rc = check_ws(ws, plan, rows_per_unit, head_dim,
+                       (int64_t)batch * num_kv_heads + 1)) != PA_OK)
         return rc;
 
     pa::VerifyArgs a;
@@ -604,11 +657,45 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.tokens_per_split = plan->tokens_per_split;
     a.total_rows = (int32_t)total_rows;
     a.logit_scale = (float)((double)sm_scale * (double)k_scale * 1.4426950408889634);
-    a.split_by_length = 1;
+    a.ragged = 1;
+    a.split_index = ws->index;
     a.ws_acc = ws->acc;
     a.ws_max = ws->max;
     a.ws_sum = ws->sum;
     return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
+}
+
+int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *plan,
+                                      int32_t batch, int32_t q_rows, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, float out_scale,
+                                      void *out_fp16, void *stream)
+{
+    int32_t rc, rows_per_unit = 0;
+    if (!plan || !out_fp16)
+        return PA_EINVAL;
+    if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit,
+                          kMaxQRowsBatch, kMaxRowsPerUnitBatch)) != PA_OK)
+        return rc;
+    if (batch < 1 || !std::isfinite(out_scale))
+        return PA_EINVAL;
+    if ((int64_t)batch * num_kv_heads > 65535)
+        return PA_EUNSUPPORTED;
+    if (plan->selection != PA_SEL_BATCH || plan->num_kv_units != batch * num_kv_heads ||
+        plan->rows_per_kv_unit != rows_per_unit || plan->head_dim != head_dim ||
+        plan->num_splits < 1)
+        return PA_EPLAN;
+    if ((rc = check_ws(ws, plan, rows_per_unit, head_dim,
+                       (int64_t)batch * num_kv_heads + 1)) != PA_OK)
+        return rc;
+    if (!aligned16(ws->acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0)
+        return PA_EALIGN;
+    if ((rc = check_device()) != PA_OK)
+        return rc;
+    const hipError_t err = pa::launch_combine_ragged(
+        ws->acc, ws->max, ws->sum, ws->index, plan->num_splits, batch, q_rows, num_heads,
+        num_kv_heads, head_dim, out_scale, static_cast<uint16_t *>(out_fp16),
+        static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_EHIP;
 }
 
 int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,

@@ -33,6 +33,12 @@
 // of each row, M + log2(sum_s w_s l_s), for a merge across ranks (1Cat-vLLM PR
 // "Qualify calibrated E4M3 and disk PLE with QSA DCP2": base-2 LSE and FP32
 // partial output exported for cross-rank merging).
+//
+// Partials come in one of two layouts.  Uniform: split s of output row r is
+// element s * R + r.  Ragged (a batch whose splits follow the lengths):
+// output row r = (b, i, h) belongs to KV unit u = b * Hkv + h / G as unit row
+// ru = i * G + h % G; its splits are index[u] .. index[u + 1] - 1, and split
+// s is element s * (q_rows * G) + ru.
 #include "pa_internal.h"
 
 #include <math.h>
@@ -46,6 +52,11 @@ constexpr int kTargetThreads = 131072;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+struct RaggedRows {
+    const int32_t *index;   // null: uniform layout
+    int q_rows, heads, group, hkv;
+};
+
 template <int GROUPS, int BATCH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ acc,
                                                            const float *__restrict__ mx,
@@ -54,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                                                            float out_scale,
                                                            uint16_t *__restrict__ out,
                                                            float *__restrict__ out32,
-                                                           float *__restrict__ lse)
+                                                           float *__restrict__ lse,
+                                                           RaggedRows rg)
 {
     constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
     __shared__ float gm[GROUPS > 1 ? kThreads : 1];
@@ -69,11 +81,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
     const int d0 = blockIdx.y * (4 * kLanes) + 4 * lane;
     const bool ok = r < R && d0 < D;          // D is a multiple of 4
 
+    // this row's splits: first, count, and the element stride and offset
+    int first = 0, count = S, stride = R, rrow = r;
+    if (rg.index && ok) {
+        const int per_req = rg.q_rows * rg.heads;
+        const int rb = r / per_req, rem = r - rb * per_req;
+        const int i = rem / rg.heads, h = rem - i * rg.heads;
+        const int u = rb * rg.hkv + h / rg.group;
+        first = rg.index[u];
+        count = rg.index[u + 1] - first;
+        stride = rg.q_rows * rg.group;
+        rrow = i * rg.group + h % rg.group;
+    }
+
     // running state of this thread's splits: max m, sum l, numerator num
     float m = -INFINITY, l = 0.0f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     if (ok) {
-        for (int s0 = grp; s0 < S; s0 += GROUPS * BATCH) {
+        for (int s0 = grp; s0 < count; s0 += GROUPS * BATCH) {
             float ms[BATCH], ls[BATCH];
             f32x4 vs[BATCH];
 #pragma unroll
@@ -82,8 +107,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
                 ms[k] = -INFINITY;
                 ls[k] = 0.0f;
                 vs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (s < S) {
-                    const int64_t i = (int64_t)s * R + r;
+                if (s < count) {
+                    const int64_t i = (int64_t)(first + s) * stride + rrow;
                     ms[k] = mx[i];
                     ls[k] = sm[i];
                     vs[k] = *(const f32x4 *)(acc + i * D + d0);
@@ -157,20 +182,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
 template <int GROUPS, int BATCH>
 hipError_t launch_g(const float *acc, const float *mx, const float *sm, int num_splits,
                     int num_rows, int head_dim, float out_scale, uint16_t *out, float *out32,
-                    float *lse, hipStream_t stream)
+                    float *lse, RaggedRows rg, hipStream_t stream)
 {
     constexpr int kRowsPerWG = kThreads / (kLanes * GROUPS);
     dim3 grid((num_rows + kRowsPerWG - 1) / kRowsPerWG, (head_dim + 4 * kLanes - 1) / (4 * kLanes));
     hipLaunchKernelGGL((combine_kernel<GROUPS, BATCH>), grid, dim3(kThreads), 0, stream, acc, mx,
-                       sm, num_splits, num_rows, head_dim, out_scale, out, out32, lse);
+                       sm, num_splits, num_rows, head_dim, out_scale, out, out32, lse, rg);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
-                          int num_rows, int head_dim, float out_scale, uint16_t *out,
-                          float *out32, float *lse, hipStream_t stream)
+// splits_per_row: the splits one row combines (ragged: an estimate, the
+// total over the units' count), which sizes the split groups
+hipError_t launch_any(const float *acc, const float *mx, const float *sm, int num_splits,
+                      int splits_per_row, int num_rows, int head_dim, float out_scale,
+                      uint16_t *out, float *out32, float *lse, RaggedRows rg, hipStream_t stream)
 {
     if (num_rows == 0)
         return hipSuccess;
@@ -180,14 +205,14 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
     // target thread count and every group has a split
     const int64_t base = (int64_t)num_rows * ((head_dim + 63) / 64) * kLanes;
     int groups = 1;
-    while (groups < 16 && groups < num_splits && base * groups * 2 <= kTargetThreads)
+    while (groups < 16 && groups < splits_per_row && base * groups * 2 <= kTargetThreads)
         groups *= 2;
-    const bool big = (num_splits + groups - 1) / groups > 8;   // splits per thread
+    const bool big = (splits_per_row + groups - 1) / groups > 8;   // splits per thread
 #define PA_COMBINE(G)                                                                          \
     return big ? launch_g<G, 16>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,  \
-                                 out32, lse, stream)                                           \
+                                 out32, lse, rg, stream)                                       \
                : launch_g<G, 8>(acc, mx, sm, num_splits, num_rows, head_dim, out_scale, out,   \
-                                out32, lse, stream)
+                                out32, lse, rg, stream)
     switch (groups) {
     case 1: PA_COMBINE(1);
     case 2: PA_COMBINE(2);
@@ -196,6 +221,30 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
     default: PA_COMBINE(16);
     }
 #undef PA_COMBINE
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
+                          int num_rows, int head_dim, float out_scale, uint16_t *out,
+                          float *out32, float *lse, hipStream_t stream)
+{
+    return launch_any(acc, mx, sm, num_splits, num_splits, num_rows, head_dim, out_scale, out,
+                      out32, lse, RaggedRows{nullptr, 0, 0, 0, 0}, stream);
+}
+
+hipError_t launch_combine_ragged(const float *acc, const float *mx, const float *sm,
+                                 const int32_t *index, int num_splits, int batch, int q_rows,
+                                 int num_heads, int num_kv_heads, int head_dim, float out_scale,
+                                 uint16_t *out, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)batch * q_rows * num_heads;
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int per_row = (int)((num_splits + units - 1) / units);
+    return launch_any(acc, mx, sm, num_splits, per_row < 1 ? 1 : per_row, (int)rows, head_dim,
+                      out_scale, out, nullptr, nullptr,
+                      RaggedRows{index, q_rows, num_heads, num_heads / num_kv_heads, num_kv_heads},
+                      stream);
 }
 
 }  // namespace pa

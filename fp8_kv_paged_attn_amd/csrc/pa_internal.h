@@ -19,5 +19,11 @@ hipError_t launch_cache_write(const uint16_t *k, const uint16_t *v, int64_t num_
 hipError_t launch_combine(const float *acc, const float *mx, const float *sm, int num_splits,
                           int num_rows, int head_dim, float out_scale, uint16_t *out,
                           float *out32, float *lse, hipStream_t stream);
+// The combine of a ragged batch's partials (VerifyArgs::ragged) into FP16
+// rows (b, i, h); index[u] .. index[u + 1] - 1 are unit u's splits.
+hipError_t launch_combine_ragged(const float *acc, const float *mx, const float *sm,
+                                 const int32_t *index, int num_splits, int batch, int q_rows,
+                                 int num_heads, int num_kv_heads, int head_dim, float out_scale,
+                                 uint16_t *out, hipStream_t stream);
 
 }  // namespace pa

@@ -39,17 +39,90 @@ struct VerifyArgs {
     int32_t total_rows;         // rows of the workspace = B * q_rows * H
     float logit_scale;          // sm_scale * k_scale * log2(e)
     float *ws_acc, *ws_max, *ws_sum;
-    int32_t split_by_length;    // 1: a unit's splits share its longest row length
-                                // (split_span), 0: split s covers s*T .. s*T + T - 1
+    // 0: the grid is (num_splits, units, row chunks), split s of every unit
+    // covers positions [s*T, s*T + T) and writes workspace rows (b, i, h).
+    // 1 (a batch of requests): the grid is (num_splits, 1, row chunks), and
+    // ragged_locate() gives each workgroup its unit, its split of that unit
+    // and the span from all row lengths; it writes workspace rows
+    // [s][row of its unit], and split_index[u] is the first split of unit u
+    // (split_index[units] the number of splits used).
+    int32_t ragged;
+    int32_t *split_index;
 };
 
-// Positions per split of a KV unit whose longest (clamped) row length is lmax,
-// when splits follow the length: ceil(lmax / S) rounded up to the 64-token
-// tile, so never more than the plan's T (S * T covers every length).
-__host__ __device__ inline int split_span(int lmax, int num_splits)
+// Longest clamped row length of request b (all its KV heads see the same).
+__device__ inline int request_len(const VerifyArgs &a, int b)
 {
-    const int t = (lmax + num_splits - 1) / num_splits;
-    return t > 0 ? (t + 63) / 64 * 64 : 64;
+    int L = 0;
+    for (int i = 0; i < a.q_rows; ++i) {
+        int l = a.row_lens[(int64_t)b * a.q_rows + i];
+        l = l < 0 ? 0 : (l > a.len_cap ? a.len_cap : l);
+        L = l > L ? l : L;
+    }
+    return L;
+}
+
+struct RaggedPos {
+    int unit;    // -1: no split of the batch falls on this workgroup
+    int local;   // split index within the unit
+    int span;    // positions per split, the same for the whole batch
+};
+
+// Where workgroup s of a ragged batch works.  Called by every lane of a wave
+// (lane = 0..63); the result is the same in all lanes.  With U = batch *
+// num_kv_heads units, L_u the longest row length of unit u, and S the
+// number of splits, the span is T = ceil(sum_u L_u / (S - U)) on the 64-token
+// tile (at most the plan's tokens_per_split, which also serves when S <= U),
+// so that unit u takes S_u = ceil(L_u / T) splits and sum_u S_u <= S: splits
+// follow the lengths, a long request gets more of them than a short one, and
+// every workgroup that works reads about T tokens.  Units take consecutive
+// splits in order; with write_index the workgroup writes split_index.
+__device__ inline RaggedPos ragged_locate(const VerifyArgs &a, int s, int lane, bool write_index)
+{
+    const int B = a.batch, Hkv = a.num_kv_heads, S = a.num_splits;
+    const int64_t U = (int64_t)B * Hkv;
+    int64_t total = 0;
+    for (int b0 = 0; b0 < B; b0 += 64)
+        total += (b0 + lane < B) ? request_len(a, b0 + lane) : 0;
+    for (int o = 32; o >= 1; o >>= 1)
+        total += __shfl_xor(total, o, 64);
+    total *= Hkv;
+    int64_t T = a.tokens_per_split;
+    if (S > U) {
+        int64_t t = (total + (S - U) - 1) / (S - U);
+        t = (t + 63) / 64 * 64;
+        T = t < 64 ? 64 : (t < T ? t : T);
+    }
+    RaggedPos pos = {-1, 0, (int)T};
+    int base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int b = b0 + lane;
+        const int L = b < B ? request_len(a, b) : 0;
+        const int sb = (int)((L + T - 1) / T);
+        const int cnt = Hkv * sb;
+        int incl = cnt;                               // inclusive scan over lanes
+        for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(incl, o, 64);
+            incl += lane >= o ? up : 0;
+        }
+        const int excl = incl - cnt;
+        if (write_index && b < B)
+            for (int g = 0; g < Hkv; ++g)
+                a.split_index[(int64_t)b * Hkv + g] = base + excl + g * sb;
+        const bool hit = b < B && s >= base + excl && s < base + incl;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+            const int j = __builtin_ctzll(m);
+            const int sj = __shfl(sb, j, 64), ej = __shfl(excl, j, 64);
+            const int d = s - base - ej;
+            pos.unit = (b0 + j) * Hkv + d / sj;
+            pos.local = d % sj;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    if (write_index && lane == 0)
+        a.split_index[U] = base;
+    return pos;
 }
 
 // Page slots (token ids: list entries) the MFMA kernel keeps per workgroup in

@@ -363,8 +363,19 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int lane = tid & 63;
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int split = blockIdx.x;
-    const int unit = blockIdx.y;
+    // the split of a KV unit this workgroup reads and its span; a ragged batch
+    // derives them from every row length of the batch (the same in every
+    // wave), and a workgroup no split falls on has nothing to do
+    int split = blockIdx.x, unit = blockIdx.y, tps = a.tokens_per_split;
+    if (a.ragged) {
+        const RaggedPos rp =
+            ragged_locate(a, blockIdx.x, lane, blockIdx.x == 0 && blockIdx.z == 0 && w == 0);
+        if (rp.unit < 0)
+            return;
+        split = __builtin_amdgcn_readfirstlane(rp.local);
+        unit = __builtin_amdgcn_readfirstlane(rp.unit);
+        tps = __builtin_amdgcn_readfirstlane(rp.span);
+    }
     const int b = unit / a.num_kv_heads;
     const int kvh = unit - b * a.num_kv_heads;
     // rows of a KV unit beyond 48 go to further workgroups (grid z): this one
@@ -402,25 +413,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         }
     }
     // lane i < q_rows: length of query row i, clamped where it is first
-    // needed, so that nothing waits for the load before the table reads are
-    // issued
+    // needed (after the table reads are issued; the empty asm statement keeps
+    // the clamp there instead of right after the load, where the compiler
+    // would wait for it)
     int lraw = 0;
     if (lane < a.q_rows)
         lraw = a.row_lens[(int64_t)b * a.q_rows + lane];
     auto clamp_len = [&](int l) __attribute__((always_inline)) {
         return l < 0 ? 0 : (l > a.len_cap ? a.len_cap : l);
     };
-    // positions per split: fixed, or (split_by_length) from this unit's
-    // longest row, which costs one more round trip before the table reads
-    // (the empty asm statements keep each use where it is written: the
-    // compiler would otherwise hoist one clamp above the branch, right after
-    // the load, and wait for the load there)
-    int tps = a.tokens_per_split;
-    if (a.split_by_length) {
-        int l = lraw;
-        asm volatile("" : "+v"(l));
-        tps = split_span(max16_broadcast(clamp_len(l)), a.num_splits);
-    }
     const int lo = split * tps;
     const int hi_list = min(lo + tps, a.list_len);
     const int32_t *table = a.block_table + (int64_t)b * a.table_stride;
@@ -1040,7 +1041,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __syncthreads();
     // Every wave derives all four weights 2^(m_ref_v - M) itself, so that one
     // barrier separates the exchange from its use.
-    const int64_t ws_base = (int64_t)split * a.total_rows;
+    // workspace rows: (b, i, h) of the output, or [split][row of the unit]
+    const int64_t ws_base =
+        a.ragged ? (int64_t)blockIdx.x * a.rows : (int64_t)split * a.total_rows;
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
         if (q != w)
@@ -1080,7 +1083,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 fv[v] = f * kPUnscale;
             }
             const int i = (row0 + r) / G, h = kvh * G + (row0 + r - i * G);
-            const int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
+            const int64_t orow =
+                a.ragged ? (int64_t)(row0 + r) : ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             float *dst = a.ws_acc + (ws_base + orow) * D;
 #pragma unroll
             for (int d = 0; d < C::DQ; ++d) {
@@ -1127,7 +1131,8 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
     if (mfma_slots_needed(a.tokens_per_split, a.page_size, MODE == kModeTokens) > max_slots<D>())
         return hipErrorNotSupported;
     // grid z: chunks of 48 rows of a KV unit (one chunk up to 48 rows)
-    dim3 grid(a.num_splits, a.batch * a.num_kv_heads,
+    // (a ragged batch's splits are shared by its units: grid y is 1)
+    dim3 grid(a.num_splits, a.ragged ? 1 : a.batch * a.num_kv_heads,
               (a.rows + 16 * kRowBlocks - 1) / (16 * kRowBlocks));
     hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,

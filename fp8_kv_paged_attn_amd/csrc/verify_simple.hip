@@ -92,7 +92,18 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
     __shared__ int32_t len_s[16];
 
     const int tid = threadIdx.x;
-    const int split = blockIdx.x, unit = blockIdx.y;
+    // the split of a KV unit this workgroup reads and its span (a ragged batch
+    // derives them from every row length, the same in every wave)
+    int split = blockIdx.x, unit = blockIdx.y, tps = a.tokens_per_split;
+    if (a.ragged) {
+        const RaggedPos rp = ragged_locate(a, blockIdx.x, tid & 63,
+                                           blockIdx.x == 0 && blockIdx.z == 0 && tid < 64);
+        if (rp.unit < 0)
+            return;
+        split = rp.local;
+        unit = rp.unit;
+        tps = rp.span;
+    }
     const int b = unit / a.num_kv_heads, g = unit - b * a.num_kv_heads;
     // rows of a KV unit beyond 48 go to further workgroups (grid z)
     const int row0 = blockIdx.z * kMaxRows;
@@ -117,7 +128,6 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
     for (int i = 0; i < a.q_rows; ++i)
         lmax = max(lmax, len_s[i]);
 
-    const int tps = a.split_by_length ? split_span(lmax, a.num_splits) : a.tokens_per_split;
     const int lo = split * tps;
     int hi = min(lo + tps, a.list_len);
     if (MODE == kModeDense)
@@ -194,18 +204,22 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
         __syncthreads();
     }
 
-    const int64_t ws_base = (int64_t)split * a.total_rows;
+    // workspace rows: (b, i, h) of the output, or [split][row of the unit]
+    const int64_t ws_base =
+        a.ragged ? (int64_t)blockIdx.x * a.rows : (int64_t)split * a.total_rows;
 #pragma unroll
     for (int r = 0; r < kMaxRows; ++r) {
         if (r < R && tid < D) {
             int i = (row0 + r) / G, h = g * G + (row0 + r - i * G);
-            int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
+            int64_t orow = a.ragged ? (int64_t)(row0 + r)
+                                    : ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             a.ws_acc[(ws_base + orow) * D + tid] = acc[r];
         }
     }
     if (tid < R) {
         int i = (row0 + tid) / G, h = g * G + (row0 + tid - i * G);
-        int64_t orow = ((int64_t)b * a.q_rows + i) * a.num_heads + h;
+        int64_t orow = a.ragged ? (int64_t)(row0 + tid)
+                                : ((int64_t)b * a.q_rows + i) * a.num_heads + h;
         a.ws_max[ws_base + orow] = m_s[tid];
         a.ws_sum[ws_base + orow] = l_s[tid];
     }
@@ -216,7 +230,8 @@ __global__ __launch_bounds__(kThreads) void verify_simple_kernel(VerifyArgs a)
 hipError_t launch_verify_simple(const VerifyArgs &a, int head_dim, VerifyMode mode,
                                 hipStream_t stream, const hipEvent_t *ev)
 {
-    dim3 grid(a.num_splits, a.batch * a.num_kv_heads, (a.rows + kMaxRows - 1) / kMaxRows);
+    dim3 grid(a.num_splits, a.ragged ? 1 : a.batch * a.num_kv_heads,
+              (a.rows + kMaxRows - 1) / kMaxRows);
     dim3 block(kThreads);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
 #define PA_SIMPLE(D, M)                                                                        \

@@ -114,9 +114,10 @@ enum pa_kernel {
 
 /* What a list position of a KV unit names (the entry point a plan is for). */
 enum pa_selection {
-    PA_SEL_DENSE = 0,              /* paged_attn_verify_e4m3, paged_attn_verify_batch_e4m3 */
+    PA_SEL_DENSE = 0,              /* paged_attn_verify_e4m3 (and its allocation-free form) */
     PA_SEL_BLOCKS = 1,             /* qsa_sparse_verify_e4m3 */
-    PA_SEL_TOKENS = 2              /* qsa_sparse_verify_tokens_e4m3 */
+    PA_SEL_TOKENS = 2,             /* qsa_sparse_verify_tokens_e4m3 */
+    PA_SEL_BATCH = 3               /* paged_attn_verify_batch_e4m3: splits shared by a batch */
 };
 
 /* (host) Split plan: the token axis of each KV unit (one KV head of one
@@ -138,6 +139,7 @@ typedef struct pa_plan {
     int32_t selection;             /* enum pa_selection */
     int64_t ws_acc_bytes;          /* FP32 [num_splits][rows][head_dim] */
     int64_t ws_stat_bytes;         /* FP32 [num_splits][rows], each of max and sum */
+    int64_t ws_index_bytes;        /* int32 [num_kv_units + 1] (PA_SEL_BATCH), else 0 */
 } pa_plan;
 
 /* (host) FP32 split workspace written by the verify entry points and read by
@@ -147,13 +149,18 @@ typedef struct pa_plan {
  *     max[s][r]    = m = max_t y_t            (-inf when the split is empty)
  *     sum[s][r]    = l = sum_t 2^(y_t - m)    (0 when empty)
  *     acc[s][r][d] = sum_t 2^(y_t - m) * V_t[g][d]   (0 when empty; no v_scale)
- * Rows are numbered like the output, so the combine works row by row. */
+ * Rows are numbered like the output (rows = (i, h), or (b, i, h) for a batch
+ * of requests), so the combine works row by row; a ragged batch
+ * (paged_attn_verify_batch_e4m3) numbers them per KV unit instead. */
 typedef struct pa_workspace {
     float *acc;
     float *max;
     float *sum;
     int64_t acc_bytes;             /* capacity of acc */
     int64_t stat_bytes;            /* capacity of each of max and sum */
+    int32_t *index;                /* split index of a ragged batch (PA_SEL_BATCH plans);
+                                      NULL elsewhere */
+    int64_t index_bytes;           /* capacity of index */
 } pa_workspace;
 
 /* (host, integer) Choose the split of max_tokens list positions (tokens for
@@ -171,7 +178,12 @@ typedef struct pa_workspace {
  * clamped to what the token count allows and raised where a split would
  * otherwise cover more pages (token ids: entries) than the MFMA kernel keeps
  * per workgroup, 1,024 at head_dim 256 and 2,048 at 128, so that every plan
- * it returns runs on that kernel.  Returns PA_EINVAL for non-positive sizes or
+ * it returns runs on that kernel.  PA_SEL_BATCH plans a ragged batch instead:
+ * num_splits counts the splits of all num_kv_units units together (one
+ * workgroup per compute unit and 48-row chunk, or as requested), raised to
+ * num_kv_units * ceil(max_tokens / T) so that every unit fits at full length,
+ * with T (tokens_per_split) the longest split the MFMA kernel takes for the
+ * page size; the kernels shorten the span from the row lengths.  Returns PA_EINVAL for non-positive sizes or
  * an unknown selection, PA_EUNSUPPORTED when the count would pass 65,535. */
 int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t num_kv_units,
                         int32_t head_dim, int32_t page_size, int32_t selection,
@@ -216,7 +228,7 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
 /* Dense verify of a batch of independent requests ([DN] first section: shapes
  * outside the single-request q2-8 route -- independent-request batches, q16,
  * other grouped shapes -- take a path with FP32 accumulation and the FP32
- * split workspace), writing split partials.
+ * split workspace), writing split partials for paged_attn_combine_batch_fp32.
  *   q_fp16       [batch][q_rows][num_heads][head_dim] FP16, contiguous, 16-byte aligned
  *   block_table  [batch][max_blocks_per_req] int32: request b's logical page ->
  *                physical page; entries up to the longest row of each request
@@ -228,13 +240,22 @@ int32_t paged_attn_verify_e4m3(const void *q_fp16, const pa_kv_pool *kv,
  *   the unit's K/V); batch*num_kv_heads <= 65535; head_dim 128 or 256
  *   plan         (host) from paged_attn_plan(max_blocks_per_req*page_size,
  *                q_rows*num_heads/num_kv_heads, batch*num_kv_heads, head_dim,
- *                page_size, PA_SEL_DENSE, ...)
- *   rows of the workspace and of the combined output: (b, i, h).
- * Splits follow each request's own length: with L_b its longest row length
- * (after the clamp) and S = plan->num_splits, split s of request b covers
- * tokens [s*T_b, (s+1)*T_b), T_b = ceil(L_b / S) rounded up to a multiple of
- * 64 (never more than plan->tokens_per_split), so a short request's work is
- * spread over all S splits instead of leaving most of them empty.
+ *                page_size, PA_SEL_BATCH, ...)
+ *   ws           (host) acc [num_splits][rows_per_unit][head_dim], max and sum
+ *                [num_splits][rows_per_unit] with rows_per_unit =
+ *                q_rows*num_heads/num_kv_heads (unit row i*G + h%G for query
+ *                row i, head h), and index [batch*num_kv_heads + 1]
+ * Splits follow the lengths over the whole batch (a ragged plan): with U =
+ * batch*num_kv_heads units, L_u the longest row length of unit u (after the
+ * clamp; the KV heads of a request share it) and S = plan->num_splits, every
+ * split spans T = ceil(sum_u L_u / (S - U)) positions on the 64-token tile
+ * (plan->tokens_per_split when that is smaller or S <= U), unit u takes
+ * S_u = ceil(L_u / T) consecutive splits, unit 0 first, and its split k covers
+ * tokens [k*T, (k+1)*T).  index[u] is unit u's first split and index[U] the
+ * splits used; splits past it write nothing.  A long request thus gets more
+ * workgroups than a short one, and every working workgroup reads about T
+ * tokens.  This is computed on the device from row_lens, so a captured call
+ * replays with new lengths.
  * Other arguments, masking and errors as for paged_attn_verify_e4m3. */
 int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                      const int32_t *block_table, int32_t max_blocks_per_req,
@@ -272,6 +293,16 @@ int32_t paged_attn_verify_noalloc_e4m3(const void *q_fp16, const pa_kv_pool *kv,
                                        int32_t head_dim, float sm_scale, float k_scale,
                                        float v_scale, const pa_plan *plan, void *out_fp16,
                                        void *stream);
+
+/* The FP32 combination (as paged_attn_combine_fp32) of the partials that
+ * paged_attn_verify_batch_e4m3 wrote with the same plan and workspace: row
+ * (b, i, h) merges the splits index[u] .. index[u+1]-1 of its unit u = b*Hkv
+ * + h/G into out_fp16 [batch][q_rows][num_heads][head_dim] (8-byte aligned).
+ * PA_EPLAN for a plan not made for this shape with PA_SEL_BATCH. */
+int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *plan,
+                                      int32_t batch, int32_t q_rows, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, float out_scale,
+                                      void *out_fp16, void *stream);
 
 /* FP32 combination of split partials into FP16 rows ([DN] first section):
  *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),

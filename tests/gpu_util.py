@@ -83,7 +83,7 @@ def run_batch(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     G = w.num_heads // w.num_kv_heads
     s = w.num_splits if splits is None else splits
     p = pa.plan(w.cap, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, w.page_size,
-                splits=s, kernel=kernel)
+                "batch", splits=s, kernel=kernel)
     ws = pa.make_workspace(p, w.batch * w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                           v_scale=w.v_scale, p=p, ws=ws)
@@ -91,6 +91,21 @@ def run_batch(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     if return_ws:
         return out.cpu().numpy(), p, tuple(t.cpu().numpy() for t in ws)
     return out.cpu().numpy()
+
+
+def ragged_plan(row_lens, cap: int, num_kv_heads: int, num_splits: int, tcap: int):
+    """The split layout a ragged batch's kernels derive on the device, worked
+    out on the host from the same rule: span T and split index [units + 1]."""
+    L = np.clip(np.asarray(row_lens, np.int64), 0, cap).max(axis=1)
+    U = L.size * num_kv_heads
+    total = int(L.sum()) * num_kv_heads
+    T = tcap
+    if num_splits > U:
+        t = -(-total // (num_splits - U))
+        T = max(64, min(-(-t // 64) * 64, tcap))
+    per_unit = np.repeat(-(-L // T), num_kv_heads)
+    index = np.concatenate([[0], np.cumsum(per_unit)]).astype(np.int64)
+    return T, index
 
 
 def oracle_batch(orc, w, nthreads=1) -> np.ndarray:

@@ -130,10 +130,55 @@ def test_plan_rejects(L):
     assert f(10, 4, 0, 256, 16, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL
     assert f(10, 4, 1, 256, 16, 0, 0, -2, ctypes.byref(out)) == PA_EINVAL
     assert f(10, 4, 1, 256, 0, 0, 0, 0, ctypes.byref(out)) == PA_EINVAL      # page size
-    assert f(10, 4, 1, 256, 16, 3, 0, 0, ctypes.byref(out)) == PA_EINVAL     # selection
+    assert f(10, 4, 1, 256, 16, 4, 0, 0, ctypes.byref(out)) == PA_EINVAL     # selection
     assert f(10, 4, 1, 256, 16, 0, 0, 0, None) == PA_EINVAL
     # a count past 65,535 splits: two billion tokens in one-token pages
     assert f(2 ** 31 - 1, 4, 1, 256, 1, 0, 0, 0, ctypes.byref(out)) == PA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("cap,rows,units,D,page,cus,req", [
+    (32 * 1024, 96, 8, 256, 3296, 256, 0), (32 * 1024, 48, 8, 256, 3296, 256, 0),
+    (512, 96, 4, 256, 64, 0, 0), (4096, 96, 300, 256, 64, 256, 0), (1 << 20, 12, 2, 256, 1, 256, 0),
+    (700, 6, 1, 128, 16, 256, 5), (0, 6, 3, 256, 16, 256, 0),
+])
+def test_plan_batch_rules(L, cap, rows, units, D, page, cus, req):
+    """A batch plan: num_splits counts the splits of all units (one workgroup per
+    compute unit and 48-row chunk, or as requested), at least enough for every
+    unit at full length at the longest span the MFMA kernel takes."""
+    p = pa.plan(cap, rows, units, D, page, "batch", num_cus=cus, splits=req)
+    S, T = p.num_splits, p.tokens_per_split
+    slots = 1024 if D == 256 else 2048
+    assert T % 64 == 0 and T >= 64
+    assert T == min((slots - 1) * page // 64 * 64, max(1, -(-cap // 64)) * 64)
+    assert mfma_slots_fit(p)
+    chunks = -(-rows // 48)
+    want = req if req else -(-(cus or 256) // chunks)
+    assert S == max(want, units * -(-cap // T), 1)
+    assert p.ws_acc_bytes == S * rows * D * 4 and p.ws_stat_bytes == S * rows * 4
+    assert p.ws_index_bytes == (units + 1) * 4
+
+
+def test_ragged_plan_rule_covers_every_length():
+    """The device's ragged rule (re-derived on the host) always fits the splits:
+    sum_u ceil(L_u / T) <= S for any lengths up to the capacity, with T on the
+    tile and at most the plan's span."""
+    from tests import gpu_util as gu
+
+    rng = np.random.default_rng(0x5A7)
+    for _ in range(400):
+        B = int(rng.integers(1, 40))
+        Hkv = int(rng.integers(1, 4))
+        q = int(rng.integers(1, 17))
+        cap = int(rng.integers(1, 200000))
+        tcap = int(rng.choice([64, 960, 1024, 4096, 65472]))
+        S = B * Hkv * -(-cap // tcap) + int(rng.integers(0, 300))
+        lens = rng.integers(-5, cap + 50, size=(B, q))
+        lens[rng.random((B, q)) < 0.2] = 0
+        T, index = gu.ragged_plan(lens, cap, Hkv, S, tcap)
+        assert T % 64 == 0 and 64 <= T <= max(tcap, 64)
+        assert index[-1] <= S and np.all(np.diff(index) >= 0)
+        L = np.repeat(np.clip(lens, 0, cap).max(axis=1), Hkv)
+        assert np.all(np.diff(index) * T >= L), "a unit's splits cover its length"
 
 
 def test_build_id_matches_sources(L):
@@ -345,9 +390,9 @@ def test_verify_batch_rejects_bad_arguments(L):
     pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
                        head_stride=256, num_pages=64, page_size=64)
     p = pa.PaPlan()
-    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 0, 0, 0, ctypes.byref(p)) == PA_OK
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 3, 0, 0, ctypes.byref(p)) == PA_OK
     ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
-                        stat_bytes=1 << 40)
+                        stat_bytes=1 << 40, index=0x70000, index_bytes=1 << 20)
     A = ctypes.c_void_p(0x60000)
     f = L.paged_attn_verify_batch_e4m3
 
@@ -368,8 +413,22 @@ def test_verify_batch_rejects_bad_arguments(L):
     assert call(sm=-1.0) == PA_EINVAL
     assert call(mb=9) == PA_EPLAN                              # plan made for 8 blocks
     assert call(B=3) == PA_EPLAN                               # plan made for 4 units
-    small = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=16, stat_bytes=16)
+    small = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=16, stat_bytes=16,
+                           index=0x70000, index_bytes=1 << 20)
     assert call(w=small) == PA_EWORKSPACE
+    noidx = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
+                           stat_bytes=1 << 40)
+    assert call(w=noidx) == PA_EINVAL                           # the split index is missing
+    shortidx = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
+                              stat_bytes=1 << 40, index=0x70000, index_bytes=16)
+    assert call(w=shortidx) == PA_EWORKSPACE                    # 4 units need 5 entries
+    dense = pa.PaPlan()
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 0, 0, 0, ctypes.byref(dense)) == PA_OK
+    assert call(plan=dense) == PA_EPLAN                         # not a batch plan
+    few = pa.PaPlan()
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 3, 0, 0, ctypes.byref(few)) == PA_OK
+    few.num_splits = 3
+    assert call(plan=few) == PA_EPLAN                           # fewer splits than units
 
 
 @no_device
@@ -377,10 +436,12 @@ def test_verify_batch_without_device_reports_edevice(L):
     pool = pa.PaKvPool(k_pool=0x10000, v_pool=0x20000, page_stride=256 * 64, token_stride=256,
                        head_stride=256, num_pages=64, page_size=64)
     p = pa.PaPlan()
-    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 0, 0, 0, ctypes.byref(p)) == PA_OK
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 3, 0, 0, ctypes.byref(p)) == PA_OK
     ws = pa.PaWorkspace(acc=0x30000, max=0x40000, sum=0x50000, acc_bytes=1 << 40,
-                        stat_bytes=1 << 40)
+                        stat_bytes=1 << 40, index=0x70000, index_bytes=1 << 20)
     A = ctypes.c_void_p(0x60000)
+    assert L.paged_attn_combine_batch_fp32(ctypes.byref(ws), ctypes.byref(p), 4, 16, 6, 1, 256,
+                                           1.0, A, None) == PA_EDEVICE
     assert L.paged_attn_verify_batch_e4m3(A, ctypes.byref(pool), A, 8, A, 4, 16, 6, 1, 256,
                                           0.0625, 1.0, ctypes.byref(p), ctypes.byref(ws),
                                           None) == PA_EDEVICE

@@ -628,7 +628,7 @@ def test_graph_replay_sparse_and_batch_entries():
                                               k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
                                               out=out)
         else:
-            p = pa.plan(w.cap, qr * G, B * w.num_kv_heads, D, w.page_size, splits=4)
+            p = pa.plan(w.cap, qr * G, B * w.num_kv_heads, D, w.page_size, "batch", splits=4)
             fn = lambda: pa.verify_batch(q, k, v, bt, lens, sm_scale=w.sm_scale,
                                          k_scale=w.k_scale, v_scale=w.v_scale, p=p, ws=ws,
                                          out=out)
@@ -826,24 +826,25 @@ def test_batch_small(orc, case, kernel):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_batch_matches_single_requests(kernel):
-    """The batch entry splits each request by its own longest row: split s of
-    request b covers [s*T_b, (s+1)*T_b), T_b = ceil(L_b / S) rounded up to 64.
-    Its partials for request b are bit-identical to the single-request
-    entry's with those boundaries (whose further splits are empty)."""
+    """The batch entry shares its splits over the requests by length: one span
+    T for the batch, request b's unit taking ceil(L_b / T) consecutive splits.
+    The split index it writes equals the host's re-derivation of that rule,
+    and each unit's partials are bit-identical to the single-request entry's
+    with splits of T tokens (whose further splits are empty)."""
     w = wl.make_dense_batch("bsingle", 0xB51, ctxs=[1000, 300, 770], q_rows=8, num_heads=6,
                             num_kv_heads=1, head_dim=256, page_size=96, sigma=1.0,
                             k_scale=0.5, v_scale=1.5, max_blocks=12)
     lens = w.row_lens.copy()
     lens[2] = [770, 700, 0, 3, 770, 500, 769, 1]
     w = dataclasses.replace(w, row_lens=lens)
-    S = 4
+    S = 9
     announce("batch vs single", kernel)
-    _, _, (bacc, bmx, bsm) = gu.run_batch(w, kernel, splits=S, return_ws=True)
+    _, bp, (bacc, bmx, bsm, bidx) = gu.run_batch(w, kernel, splits=S, return_ws=True)
+    T, index = gu.ragged_plan(w.row_lens, w.cap, w.num_kv_heads, bp.num_splits,
+                              bp.tokens_per_split)
+    assert np.array_equal(bidx, index), (bidx, index)
     R = w.q_rows * w.num_heads
     for b in range(w.batch):
-        L = int(np.clip(w.row_lens[b], 0, w.cap).max())
-        T = -(-L // S)
-        T = -(-T // 64) * 64 if T > 0 else 64
         r = dataclasses.replace(w.request(b), max_tokens=w.cap)
         d = gu.dense_to_dev(r)
         p = pa.plan(w.cap, R // w.num_kv_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -855,10 +856,11 @@ def test_batch_matches_single_requests(kernel):
                                   w.k_scale, p, ws)
         torch.cuda.synchronize()
         acc, mx, sm = (t.cpu().numpy() for t in ws)
-        rows = slice(b * R, (b + 1) * R)
-        assert np.array_equal(bacc[:, rows], acc[:S]), b
-        assert np.array_equal(bmx[:, rows], mx[:S]) and np.array_equal(bsm[:, rows], sm[:S]), b
-        assert np.all(mx[S:] == -np.inf) and not sm[S:].any() and not acc[S:].any(), b
+        s0, s1 = index[b], index[b + 1]
+        n = s1 - s0
+        assert np.array_equal(bacc[s0:s1], acc[:n]), b
+        assert np.array_equal(bmx[s0:s1], mx[:n]) and np.array_equal(bsm[s0:s1], sm[:n]), b
+        assert np.all(mx[n:] == -np.inf) and not sm[n:].any() and not acc[n:].any(), b
 
 
 def test_batch_config(orc):
