@@ -115,8 +115,10 @@ class DenseBench:
         out32 = torch.empty(self.rows * D, dtype=torch.float32, device="cuda:0")
         lse = torch.empty(self.rows, dtype=torch.float32, device="cuda:0")
         res = {}
-        for name, fn in (("combine_us", self.combine),
-                         ("combine_lse_us", lambda: self.combine_lse(out32, lse))):
+        fns = [("combine_us", self.combine)]
+        if self.plan.selection != self.pa.PA_SELECTION["batch"]:
+            fns.append(("combine_lse_us", lambda: self.combine_lse(out32, lse)))
+        for name, fn in fns:
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
@@ -296,6 +298,19 @@ class QsaTokensBench(QsaBench):
                                               w.sm_scale, w.k_scale, self.plan, self.ws)
 
 
+def bench_for(name: str, w, kernel: str, splits: int = 0):
+    """The resident bench of a named workload (dense, sparse over blocks or token
+    ids, or a batch of independent requests)."""
+    n = copies_for(2 * w.k_pool.size)
+    if hasattr(w, "sel_tokens"):
+        return QsaTokensBench(w, n, kernel)
+    if hasattr(w, "sel_blocks"):
+        return QsaBench(w, n, kernel)
+    if hasattr(w, "request"):
+        return BatchBench(w, n, kernel)
+    return DenseBench(w, n, kernel, splits)
+
+
 def measure(b, steps: int, warmup: int) -> dict:
     """Cold (rotating pool copies) and hot (one copy) timings of one workload:
     per-call time from graph replays, verify-kernel time from the eager,
@@ -314,6 +329,7 @@ def measure(b, steps: int, warmup: int) -> dict:
 def sweep_entry(name: str, kv_bytes: int, plan, m: dict, **extra) -> dict:
     gb = lambda us: round(kv_bytes / (us * 1e-6) / 1e9, 1)
     return {"workload": name, **extra, "kv_bytes": kv_bytes, "splits": plan.num_splits,
+            "tokens_per_split": plan.tokens_per_split,
             "us_per_call": round(m["us"], 3), "gbs": gb(m["us"]),
             "us_per_call_pcts": m["pcts"],
             "verify_us": round(m["verify_us"], 3), "verify_gbs": gb(m["verify_us"]),
@@ -535,16 +551,17 @@ def cpu_baseline(w, outputs: dict, max_seconds: float = 20.0):
 
 
 def traffic_from_profile(src_hash: str, workload: str):
-    """HBM bytes per verify launch from the committed rocprofv3 counter runs,
-    or None when they were taken on another kernel source or workload."""
+    """HBM bytes per verify launch for `workload` from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when the
+    kernel sources have changed since the counters were taken."""
     try:
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != src_hash or d.get("workload") != workload:
+    if d.get("source_hash") != src_hash:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
 
 
 def main():
@@ -592,7 +609,17 @@ def main():
     w = wl.cached(args.workload)
     n_copies = copies_for(2 * w.k_pool.size)
     log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
-    b = DenseBench(w, n_copies, args.kernel, args.splits)
+    b = bench_for(args.workload, w, args.kernel, args.splits)
+    if not isinstance(w, wl.DenseWorkload):
+        # a sparse or batch workload on its own (counter and trace runs): its
+        # timings, without the headline record, which is a dense figure
+        m = measure(b, args.steps, args.warmup)
+        m.pop("out")
+        e = sweep_entry(w.name, b.kv_bytes, b.plan, m, units=w.batch * w.num_kv_heads)
+        e["traffic"] = traffic_from_profile(src_hash, w.name)
+        print(json.dumps({"workload_only": e, "source_hash": src_hash,
+                          "build_id": pa.build_id()}), flush=True)
+        return
     m = measure(b, args.steps, args.warmup)
     log(f"[bench] cold: {m['us']:.2f} us/call (graph), {m['eager_us']:.2f} eager, "
         f"verify {m['verify_us']:.2f} us; hot: {m['hot_us']:.2f} us/call, "
@@ -646,6 +673,8 @@ def main():
         del bb
         torch.cuda.empty_cache()
         sweep.append(sweep_entry(w.name, w.kv_bytes(), plan, m, ctx=w.max_tokens))
+        for e in sweep:
+            e["traffic"] = traffic_from_profile(src_hash, e["workload"])
 
     cache_write = None
     if not args.no_sweep:

@@ -217,12 +217,31 @@ __device__ __forceinline__ void swap16(float v, float &x0, float &x1)
     x1 = __builtin_bit_cast(float, r1);
 }
 
+// Maxima of scores as plain v_max_f32 / v_max3_f32.  fmaxf makes the compiler
+// quiet each operand it cannot prove quiet (MFMA results, lane swaps) with a
+// v_max(x, x) first, which doubles the softmax's maxima.  The instructions
+// drop a quiet NaN operand as maxnum does; the scores never hold a signalling
+// NaN (they come out of the MFMA), so the result is the same.
+__device__ __forceinline__ float max2(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float max_over_groups(float v)
 {
     float a, b;
     swap32(v, a, b);
-    swap16(fmaxf(a, b), a, b);
-    return fmaxf(a, b);
+    swap16(max2(a, b), a, b);
+    return max2(a, b);
 }
 
 __device__ __forceinline__ float sum_over_groups(float v)
@@ -832,9 +851,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                         sv[jj] = ((vis >> jj) & 1u) ? sv[jj] : -INFINITY;
                 }
                 // c > 0, so the largest logit comes from the largest raw score
-                const float mloc = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-                const float mt = fmaxf(m_true[rb], max_over_groups(mloc) * c);
+                const float mloc = max2(max3(sv[0], sv[1], sv[2]),
+                                        max3(sv[3], sv[4], max3(sv[5], sv[6], sv[7])));
+                const float mt = max2(m_true[rb], max_over_groups(mloc) * c);
                 m_true[rb] = mt;
                 if (__any(mt > m_ref[rb] + kLazy)) {
                     // rare: move the reference and rescale what was accumulated.
