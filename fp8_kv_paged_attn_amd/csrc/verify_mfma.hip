@@ -236,6 +236,20 @@ __device__ __forceinline__ float max3(float a, float b, float c)
     return r;
 }
 
+// p - h[i] for the FP16 pair h, in one v_fma_mix_f32 (p * 1 - h[i], one
+// rounding): the FP16 operand is read in place, where a conversion to FP32
+// and a subtraction would take two instructions.
+__device__ __forceinline__ float sub_half(float p, half2v h, int i)
+{
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    float r;
+    if (i == 0)
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(r) : "v"(p), "v"(hb));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "=v"(r) : "v"(p), "v"(hb));
+    return r;
+}
+
 __device__ __forceinline__ float max_over_groups(float v)
 {
     float a, b;
@@ -751,6 +765,27 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         else
             wait_vmcnt<0>();
     };
+    // The page reference of block j of this wave from that of its block j - 1
+    // (dense lists): with both blocks whole inside one page, block j is the
+    // same page 128 positions on, and its base moves by 128 token strides
+    // (a few scalar operations instead of the slot-cache reads, their wait and
+    // the 64-bit address arithmetic of a lookup).  Otherwise the full lookup.
+    auto next_ref = [&](const BlockRef &prev, int j) __attribute__((always_inline)) -> BlockRef {
+        if (!SPARSE && two_slot) {
+            const int pos0 = lo + (j * kWaves + w) * kSub;
+            if (prev.na == kSub && prev.end_a == kSub && prev.ua + kMacro + kSub <= ps &&
+                pos0 + kSub <= hi) {
+                BlockRef br = prev;       // same page: phys, first tokens and na stay
+                br.ua = prev.ua + kMacro;
+                br.base_a = prev.base_a + (int64_t)kMacro * a.token_stride;
+                br.end_a = kSub;
+                br.end_b = hi - pos0;
+                return br;
+            }
+        }
+        return lookup(j);
+    };
+    BlockRef bcur = {};   // the reference of this wave's current block
     auto step = [&](auto nrb_c, int j) __attribute__((always_inline)) {
         constexpr int NRB = decltype(nrb_c)::value;
         const int st = j & 1;
@@ -801,7 +836,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         }
         BlockRef bnext = {};
         if (j + 1 < nms) {
-            bnext = lookup(j + 1);
+            bnext = next_ref(bcur, j + 1);
             issue_plane(bnext, j + 1, a.k_pool, k_st + (st ^ 1) * (kWaves * C::BLOCK), nullptr);
         }
 
@@ -874,12 +909,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[jj], c, bias));
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[jj + 1], c, bias));
                     lsum += p0 + p1;
-                    // hi = p with the low 13 mantissa bits cleared (exact in FP16),
-                    // lo = the rest, rounded toward zero
-                    const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p0) & 0xFFFFE000u);
-                    const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p1) & 0xFFFFE000u);
-                    const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(h0, h1));
-                    const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
+                    // hi = p rounded toward zero to FP16 (its first 11 bits), lo =
+                    // p - hi, exact in FP32, rounded toward zero to FP16
+                    const half2v hh = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+                    const float l0 = sub_half(p0, hh, 0), l1 = sub_half(p1, hh, 1);
+                    const half2v ll = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(l0, l1));
                     hh8[jj] = hh.x;
                     hh8[jj + 1] = hh.y;
                     ll8[jj] = ll.x;
@@ -979,6 +1013,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         if (j + 1 < nms)
             issue_plane(bnext, j + 1, a.v_pool, v_st + (st ^ 1) * (kWaves * C::BLOCK),
                         &tok_s[w][st ^ 1][0]);
+        bcur = bnext;
     };
 
     auto main_loop = [&](auto nrb_c) __attribute__((always_inline)) {
@@ -987,9 +1022,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     };
 
     if (nms > 0) {
-        const BlockRef br0 = lookup(0);
-        issue_plane(br0, 0, a.k_pool, k_st, nullptr);
-        issue_plane(br0, 0, a.v_pool, v_st, &tok_s[w][0][0]);
+        bcur = lookup(0);
+        issue_plane(bcur, 0, a.k_pool, k_st, nullptr);
+        issue_plane(bcur, 0, a.v_pool, v_st, &tok_s[w][0][0]);
         if (nrb == 1)
             main_loop(std::integral_constant<int, 1>());
         else if (nrb == 2)
