@@ -81,8 +81,11 @@ __device__ inline RaggedPos ragged_locate(const VerifyArgs &a, int s, int lane, 
 {
     const int B = a.batch, Hkv = a.num_kv_heads, S = a.num_splits;
     const int64_t U = (int64_t)B * Hkv;
-    int64_t total = 0;
-    for (int b0 = 0; b0 < B; b0 += 64)
+    // the first 64 requests' lengths are kept for the second pass (one round
+    // trip for a batch of up to 64 requests)
+    const int L0 = lane < B ? request_len(a, lane) : 0;
+    int64_t total = L0;
+    for (int b0 = 64; b0 < B; b0 += 64)
         total += (b0 + lane < B) ? request_len(a, b0 + lane) : 0;
     for (int o = 32; o >= 1; o >>= 1)
         total += __shfl_xor(total, o, 64);
@@ -97,8 +100,9 @@ __device__ inline RaggedPos ragged_locate(const VerifyArgs &a, int s, int lane, 
     int base = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int b = b0 + lane;
-        const int L = b < B ? request_len(a, b) : 0;
-        const int sb = (int)((L + T - 1) / T);
+        const int L = b0 == 0 ? L0 : (b < B ? request_len(a, b) : 0);
+        // L + T - 1 < 2^31: a batch plan keeps the capacity plus its span in int32
+        const int sb = (int)((uint32_t)(L + (int)T - 1) / (uint32_t)T);
         const int cnt = Hkv * sb;
         int incl = cnt;                               // inclusive scan over lanes
         for (int o = 1; o < 64; o <<= 1) {
