@@ -71,6 +71,15 @@ SMALL = [
     (2, 24, 1, 256, 200, 16, None, 2),
     (5, 8, 4, 256, 333, 1, None, 4),
     (8, 6, 1, 256, 4100, 1728, None, 64),
+    # a wave's next block 128 positions on in the same page (reference moved in
+    # place) or past it (looked up): pages of 288 (wave 0's third block still
+    # fits, the others cross), 1000 (not a multiple of 32: blocks straddle two
+    # pages), 160 (only the first step of wave 0 stays) and 2048 with lengths
+    # and a split end inside a page
+    (8, 6, 1, 256, 3000, 288, None, 2),
+    (4, 6, 1, 256, 2100, 1000, [2095, 2096, 2097, 2100], 3),
+    (8, 6, 1, 256, 5000, 160, None, 4),
+    (8, 6, 1, 256, 4000, 2048, [3990, 3991, 3992, 3993, 3994, 3995, 3996, 3997], 3),
 ]
 
 
@@ -808,6 +817,9 @@ BATCHES = [
                                                 [517, 500, 1, 2], [0, 0, 0, 0]], 3),
     ([2500, 900], 12, 4, 1, 256, 848, None, 5),
     ([129, 64, 200], 16, 6, 2, 256, 1, None, 2),
+    # long splits over pages of 1000 (span 1728: block references moved in place
+    # inside a page and looked up across page edges)
+    ([5000, 2900, 640], 8, 6, 1, 256, 1000, None, 8),
 ]
 
 
