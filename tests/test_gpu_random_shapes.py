@@ -5,7 +5,7 @@ Each case draws a shape the boundary accepts -- grouped heads, head dim 128 or
 contexts up to a few thousand tokens, causal or arbitrary row lengths (zero,
 past the capacity, negative), planner-chosen or requested split counts -- for
 the dense verify of one request, the ragged batch of independent requests and
-the sparse verify over selected blocks, and checks the output against the FP64
+the sparse verify over selected blocks and over selected token ids, and checks the output against the FP64
 oracle at the usual bar (rel-L2 <= 5e-4, max-abs <= 4x the FP16 rounding
 floor).  The draws are fixed by their seeds, so a failing case is reproduced by
 its index.
@@ -98,7 +98,28 @@ def qsa_case(i: int):
                 v_scale=float(rng.uniform(0.2, 3.0)), num_splits=splits, row_lens=lens)
 
 
-N_DENSE, N_BATCH, N_QSA = 40, 20, 20
+def tokens_case(i: int):
+    rng = np.random.default_rng(0x70C0 + i)
+    D = int(rng.choice([128, 256]))
+    Hkv = int(rng.choice([1, 2]))
+    G, q_rows = _group_and_rows(rng, 48, 8)
+    page = int(rng.choice([16, 32, 48, 64, 100, 333]))
+    ctx = int(rng.integers(q_rows + 8, 3000))
+    num_empty = int(rng.integers(0, 5))
+    num_sel = int(rng.integers(q_rows + num_empty + 1, min(ctx, 2500) + 1))
+    B = int(rng.integers(1, 4))
+    lens = None
+    if rng.random() < 0.5:
+        lens = np.stack([np.array(_lens(rng, q_rows, ctx) or [ctx] * q_rows, np.int64)
+                         for _ in range(B)])
+    splits = 0 if rng.random() < 0.4 else int(rng.integers(1, 9))
+    return dict(batch=B, q_rows=q_rows, num_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                ctx=ctx, page_size=page, num_sel=num_sel, k_scale=float(rng.uniform(0.2, 3.0)),
+                v_scale=float(rng.uniform(0.2, 3.0)), num_empty=num_empty, num_splits=splits,
+                row_lens=lens)
+
+
+N_DENSE, N_BATCH, N_QSA, N_TOKENS = 40, 20, 20, 12
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -132,3 +153,15 @@ def test_random_qsa(orc, i, kernel):
     w = wl.make_qsa(f"rnd_qsa{i}", 0x05A000 + i, **args)
     got = gu.run_qsa(w, kernel)
     gu.assert_parity(got, orc.qsa_workload(w), f"random qsa {i}/{kernel}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("i", range(N_TOKENS))
+def test_random_qsa_tokens(orc, i, kernel):
+    args = tokens_case(i)
+    announce("random qsa tokens", i, kernel,
+             {k: v for k, v in args.items() if k != "row_lens"},
+             "lens", None if args["row_lens"] is None else args["row_lens"].tolist())
+    w = wl.make_qsa_tokens(f"rnd_tok{i}", 0x70C000 + i, **args)
+    got = gu.run_qsa_tokens(w, kernel)
+    gu.assert_parity(got, orc.qsa_tokens_workload(w), f"random qsa tokens {i}/{kernel}")
