@@ -11,10 +11,11 @@ from the 256 MB Infinity Cache ("cold"); the same loop on one copy ("hot",
 identical inputs back to back) is reported beside it, with the other contexts
 of the range (8K, 64K, 128K) and the sparse (QSA) batch.
 
-Per-call time is measured on a HIP graph of 10 consecutive verify + combine
-calls, replayed (the pages time their kernels from CUDA-graph samples), so that
-Python launch overhead does not set the pace; the eager per-call time is
-reported beside it.  Throughput counts algorithmic bytes only: the longest
+Per-call time is measured on a HIP graph of consecutive verify + combine calls,
+replayed (the pages time their kernels from CUDA-graph samples), so that Python
+launch overhead does not set the pace: exactly --steps calls are timed, and the
+percentiles come from a separate sample of 60 replays; the eager per-call time
+is reported beside it.  Throughput counts algorithmic bytes only: the longest
 visible prefix x 512 B (K and V, one KV head, D = 256, one byte per element).
 The verify kernel's own duration comes from the library's kernel timer (HIP
 events passed with each verify dispatch, on the stream it runs on) over an
@@ -24,7 +25,9 @@ device's practical read ceiling beside the published peak.  The FP64 CPU
 oracle is timed on the host's cores on the same workload as a reported
 baseline.
 
-Prints ONE JSON line on stdout; progress goes to stderr.
+Prints ONE JSON line on stdout; progress goes to stderr.  With --workload
+naming a sparse or batch workload (c4, c4tok, batch) the line holds that
+workload's timings alone ("workload_only"): the form the counter runs take.
 """
 
 from __future__ import annotations
