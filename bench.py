@@ -301,7 +301,7 @@ class QsaTokensBench(QsaBench):
                                               w.sm_scale, w.k_scale, self.plan, self.ws)
 
 
-def bench_for(name: str, w, kernel: str, splits: int = 0):
+def bench_for(w, kernel: str, splits: int = 0):
     """The resident bench of a named workload (dense, sparse over blocks or token
     ids, or a batch of independent requests)."""
     n = copies_for(2 * w.k_pool.size)
@@ -612,7 +612,7 @@ def main():
     w = wl.cached(args.workload)
     n_copies = copies_for(2 * w.k_pool.size)
     log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
-    b = bench_for(args.workload, w, args.kernel, args.splits)
+    b = bench_for(w, args.kernel, args.splits)
     if not isinstance(w, wl.DenseWorkload):
         # a sparse or batch workload on its own (counter and trace runs): its
         # timings, without the headline record, which is a dense figure
