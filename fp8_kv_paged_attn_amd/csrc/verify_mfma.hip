@@ -893,11 +893,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 if (__any(mt > m_ref[rb] + kLazy)) {
                     // rare: move the reference and rescale what was accumulated.
                     // A row that has seen nothing keeps -inf (and zero state).
-                    const float alpha = (mt == -INFINITY) ? 1.0f : exp2f(m_ref[rb] - mt);
-                    l_part[rb] *= alpha;
+                    // While no row of the row block has a reference yet (its first
+                    // block: every accumulator and sum is still exactly zero) the
+                    // rescale is skipped; it would multiply 16 x D zeros.
+                    if (__any(m_ref[rb] != -INFINITY)) {
+                        const float alpha = (mt == -INFINITY) ? 1.0f : exp2f(m_ref[rb] - mt);
+                        l_part[rb] *= alpha;
 #pragma unroll
-                    for (int d = 0; d < C::DB; ++d)
-                        scale_in_place(acc[rb][d], alpha);
+                        for (int d = 0; d < C::DB; ++d)
+                            scale_in_place(acc[rb][d], alpha);
+                    }
                     m_ref[rb] = mt;
                 }
                 // p = 2^(logit - m_ref + 6) = exp2(fma(s, c, 6 - m_ref)): P carries 2^6
