@@ -415,6 +415,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // takes rows row0 .. row0 + R - 1 of the unit
     const int row0 = blockIdx.z * (16 * kRowBlocks);
     const int R = min(a.rows - row0, 16 * kRowBlocks), G = a.group;
+    // row / G for a row of the KV unit (row < rows <= 96, G <= rows, so
+    // row * G < 2^16): (row * ceil(2^16 / G)) >> 16 is exact, one 24-bit
+    // multiply and a shift where a division takes about twenty instructions,
+    // several of them at quarter rate.
+    const uint32_t g_magic = (65536u + (uint32_t)G - 1u) / (uint32_t)G;
+    auto div_g = [&](int row) __attribute__((always_inline)) {
+        return (int)(__umul24((uint32_t)row, g_magic) >> 16);
+    };
     const int ps = a.page_size;
 
     uint8_t *const k_st = smem;                               // [2][kWaves][BLOCK]
@@ -428,19 +436,22 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // Q is fetched once per workgroup with direct-to-LDS loads into the K0
     // stage (free until the first K/V loads), rows of 2D bytes with their
     // 16-byte chunks XOR-swizzled by row, and read into registers from there.
-    // Q row r of this KV unit is query row r / G, head kvh*G + r % G.
+    // Q row r of this KV unit is query row r / G, head kvh*G + r % G: it lies
+    // r + (r / G)(H - G) rows past the unit's first Q row.
     uint8_t *const q_st = k_st;
     constexpr int kQRowsPerDma = 1024 / (2 * D);
     constexpr int kQLanesPerRow = 2 * D / 16;
     {
         const int nq = (R * 2 * D + 1023) / 1024;          // 1 KB loads for R rows
         const int r_in = lane / kQLanesPerRow, c = lane % kQLanesPerRow;
+        const uint8_t *qb =
+            (const uint8_t *)(a.q + ((int64_t)b * a.q_rows * a.num_heads + (int64_t)kvh * G) * D);
         for (int i = w; i < nq; i += kWaves) {
             const int r = i * kQRowsPerDma + r_in;
             if (r < R) {
-                const int qi = (row0 + r) / G, h = kvh * G + (row0 + r - qi * G);
-                const uint16_t *qrow = a.q + (((int64_t)b * a.q_rows + qi) * a.num_heads + h) * D;
-                dma16((const uint8_t *)qrow + 16 * (c ^ (r & 15)),
+                const int row = row0 + r;
+                const int qrow = row + div_g(row) * (a.num_heads - G);
+                dma16(qb + (int64_t)qrow * (2 * D) + 16 * (c ^ (r & 15)),
                       __builtin_amdgcn_readfirstlane(lds_addr(q_st + i * 1024)));
             }
         }
@@ -634,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
         const int r = rb * 16 + n;
-        const int lr = __shfl(lmine, r < R ? (row0 + r) / G : 0, 64);
+        const int lr = __shfl(lmine, r < R ? div_g(row0 + r) : 0, 64);
         lrow[rb] = r < R ? lr : 0;
     }
     // row blocks up to the last one with a row that sees a token
@@ -1141,7 +1152,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 L += lv[v] * f;
                 fv[v] = f * kPUnscale;
             }
-            const int i = (row0 + r) / G, h = kvh * G + (row0 + r - i * G);
+            const int i = div_g(row0 + r), h = kvh * G + (row0 + r - i * G);
             const int64_t orow =
                 a.ragged ? (int64_t)(row0 + r) : ((int64_t)b * a.q_rows + i) * a.num_heads + h;
             float *dst = a.ws_acc + (ws_base + orow) * D;
