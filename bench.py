@@ -241,12 +241,13 @@ PCT_REPLAYS = 60     # graph replays behind the per-call percentiles
 
 
 def percentiles(xs, calls_per_sample: int):
-    """p10/p50/p90 (us) of per-call times given in ms."""
+    """p10/p50/p90, mean and max (us) of per-call times given in ms."""
     if not xs:
         return None
     ys = sorted(x * 1e3 for x in xs)
     pick = lambda q: ys[min(len(ys) - 1, int(round(q * (len(ys) - 1))))]
     return {"p10": round(pick(0.1), 3), "p50": round(pick(0.5), 3), "p90": round(pick(0.9), 3),
+            "mean": round(sum(ys) / len(ys), 3), "max": round(ys[-1], 3),
             "samples": len(ys), "calls_per_sample": calls_per_sample}
 
 
