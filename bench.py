@@ -572,7 +572,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--kernel", default="mfma", choices=["auto", "simple", "mfma"])
     ap.add_argument("--splits", type=int, default=0)
