@@ -25,6 +25,9 @@ namespace {
 constexpr int kTileTokens = 64;
 constexpr int kMaxRowsPerUnit = 48;
 constexpr int kMaxQRows = 8;
+// the verify kernel stores a KV unit's partial rows by 32-bit byte offsets from
+// the unit's first row: q_rows * num_heads * head_dim * 4 must stay below 2^31
+constexpr int kMaxHeads = 65536;
 // the batched entry: up to 16 query rows, up to 96 rows per KV unit (two
 // 48-row chunks, one workgroup each)
 constexpr int kMaxRowsPerUnitBatch = 96;
@@ -101,7 +104,7 @@ int32_t check_shape(int32_t q_rows, int32_t num_heads, int32_t num_kv_heads, int
 {
     if (q_rows < 1 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads != 0)
         return PA_EINVAL;
-    if (q_rows > max_q_rows)
+    if (q_rows > max_q_rows || num_heads > kMaxHeads)
         return PA_EUNSUPPORTED;
     if (head_dim != 128 && head_dim != 256)
         return PA_EUNSUPPORTED;

@@ -153,6 +153,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// Stores of the split partials at device scope (the SC1 cache-policy bit).
+// Each XCD of the chip has its own L2, so such a store is written through to
+// memory when it is issued.  An ordinary store stays dirty in the L2 until
+// the write-back that ends the kernel, and every workgroup writes its
+// partials in its last microseconds, so that write-back would delay the end
+// of the kernel.  The stores go through a raw buffer resource: a uniform
+// base, a 32-bit byte offset below 2^31 per lane, and the 32-bit data format.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kStoreDeviceScope = 16;      // cache-policy operand: SC1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(float *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ void store_ws(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0,
+                                           kStoreDeviceScope);
+}
+
+__device__ __forceinline__ void store_ws(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0,
+                                          kStoreDeviceScope);
+}
+
 template <bool BF16>
 struct Frag;
 template <>
@@ -1111,9 +1138,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __syncthreads();
     // Every wave derives all four weights 2^(m_ref_v - M) itself, so that one
     // barrier separates the exchange from its use.
-    // workspace rows: (b, i, h) of the output, or [split][row of the unit]
+    // workspace rows: (b, i, h) of the output, or [split][row of the unit].
+    // Row r of the unit is output row unit_row + r + (r / G)(H - G), so the
+    // stores are addressed from the unit's first row.
     const int64_t ws_base =
-        a.ragged ? (int64_t)blockIdx.x * a.rows : (int64_t)split * a.total_rows;
+        a.ragged ? (int64_t)blockIdx.x * a.rows
+                 : (int64_t)split * a.total_rows +
+                       ((int64_t)b * a.q_rows * a.num_heads + (int64_t)kvh * G);
+    const __amdgpu_buffer_rsrc_t rs_acc = ws_rsrc(a.ws_acc + ws_base * D);
+    const __amdgpu_buffer_rsrc_t rs_max = ws_rsrc(a.ws_max + ws_base);
+    const __amdgpu_buffer_rsrc_t rs_sum = ws_rsrc(a.ws_sum + ws_base);
 #pragma unroll
     for (int q = 0; q < kWaves; ++q) {
         if (q != w)
@@ -1152,10 +1186,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 L += lv[v] * f;
                 fv[v] = f * kPUnscale;
             }
-            const int i = div_g(row0 + r), h = kvh * G + (row0 + r - i * G);
-            const int64_t orow =
-                a.ragged ? (int64_t)(row0 + r) : ((int64_t)b * a.q_rows + i) * a.num_heads + h;
-            float *dst = a.ws_acc + (ws_base + orow) * D;
+            const int orow = a.ragged ? row0 + r : row0 + r + div_g(row0 + r) * (a.num_heads - G);
 #pragma unroll
             for (int d = 0; d < C::DQ; ++d) {
                 f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1165,18 +1196,16 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     for (int vi = 0; vi < kWaves - 1; ++vi)
                         o += xs[vi][d] * fv[vi < q ? vi : vi + 1];
                 }
-                // a row that sees nothing of the split writes zeros, whatever
-                // its accumulators took up unmasked (the weights are 0, but
-                // 0 x NaN is not)
-                if (L == 0.0f)
-                    o = f32x4{0.f, 0.f, 0.f, 0.f};
-                // lane (n, g) of d-block db holds d = 16 db + 4 g + k
-                if (r < R)
-                    *(f32x4 *)(dst + 16 * (q * C::DQ + d) + 4 * g) = o;
+                // lane (n, g) of d-block db holds d = 16 db + 4 g + k.  A row
+                // that sees nothing of the split (sum 0) writes no numerator:
+                // the combine never uses an empty split's numerator, and what
+                // its accumulators took up unmasked is not part of it.
+                if (r < R && L != 0.0f)
+                    store_ws(rs_acc, (uint32_t)(orow * D + 16 * (q * C::DQ + d) + 4 * g) * 4u, o);
             }
             if (q == 0 && g == 0 && r < R) {
-                a.ws_max[ws_base + orow] = M;
-                a.ws_sum[ws_base + orow] = L * kPUnscale;
+                store_ws(rs_max, (uint32_t)orow * 4u, M);
+                store_ws(rs_sum, (uint32_t)orow * 4u, L * kPUnscale);
             }
         }
     }
@@ -1216,6 +1245,10 @@ hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, VerifyMode mode
                               hipStream_t stream, const hipEvent_t *ev)
 {
     if (a.rows < 1 || a.rows > 65535 * 16 * kRowBlocks)
+        return hipErrorNotSupported;
+    // the partial stores' byte offsets from a KV unit's first row are 32-bit
+    const int64_t span = a.ragged ? a.rows : (int64_t)a.q_rows * a.num_heads;
+    if (span * head_dim * 4 >= ((int64_t)1 << 31))
         return hipErrorNotSupported;
     switch (head_dim * 4 + mode) {
     case 256 * 4 + kModeDense: return launch_t<256, kModeDense>(a, stream, ev);

@@ -64,7 +64,8 @@ extern "C" {
 enum pa_status {
     PA_OK = 0,
     PA_EINVAL = -1,        /* null pointer, bad shape or count, bad scale */
-    PA_EUNSUPPORTED = -2,  /* valid but not built: head_dim, rows per KV head */
+    PA_EUNSUPPORTED = -2,  /* valid but not built: head_dim, rows per KV head,
+                              more than 65,536 heads */
     PA_EWORKSPACE = -3,    /* workspace smaller than the plan needs */
     PA_EALIGN = -4,        /* pointer or stride not 16-byte aligned */
     PA_EDEVICE = -5,       /* no HIP device, or not gfx950 */
@@ -148,7 +149,9 @@ typedef struct pa_plan {
  * a separate FP32 max and sum), with y_t = s_t * log2(e):
  *     max[s][r]    = m = max_t y_t            (-inf when the split is empty)
  *     sum[s][r]    = l = sum_t 2^(y_t - m)    (0 when empty)
- *     acc[s][r][d] = sum_t 2^(y_t - m) * V_t[g][d]   (0 when empty; no v_scale)
+ *     acc[s][r][d] = sum_t 2^(y_t - m) * V_t[g][d]   (no v_scale; the MFMA kernel
+ *                    leaves it unwritten when the split is empty, since the
+ *                    combine never uses an empty split's numerator)
  * Rows are numbered like the output (rows = (i, h), or (b, i, h) for a batch
  * of requests), so the combine works row by row; a ragged batch
  * (paged_attn_verify_batch_e4m3) numbers them per KV unit instead. */

@@ -258,6 +258,9 @@ def test_verify_rejects_bad_arguments(L):
     _spoil(L, "q_rows", 0, PA_EINVAL)
     _spoil(L, "Hkv", 4, PA_EINVAL)                 # 6 % 4 != 0
     _spoil(L, "H", 12, PA_EUNSUPPORTED)            # 8 x 12 rows per KV head > 48
+    c = Call()                                     # more than 65,536 heads
+    c.H, c.Hkv = 6 * 16384, 16384
+    assert c(L) == PA_EUNSUPPORTED
     _spoil(L, "q", A + 8, PA_EALIGN)
     _spoil(L, "k_pool", A * 2 + 4, PA_EALIGN, sub="pool")
     _spoil(L, "token_stride", 264 - 4, PA_EALIGN, sub="pool")
