@@ -8,7 +8,7 @@
 // goes to page slot / page_size, row slot % page_size of both planes.
 //
 // One thread per 16 elements of a token: two 16-byte FP16 loads and one
-// 16-byte store per plane.  The quotient is the correctly rounded FP32
+// 16-byte device-scope store per plane.  The quotient is the correctly rounded FP32
 // division, formed from the scale's reciprocal with one FMA correction; the
 // hardware FP8 conversion rounds it to nearest even after a clamp to the
 // largest finite code.
@@ -90,6 +90,22 @@ __device__ __forceinline__ uint4 encode16(uint4 in0, uint4 in1, float scale, flo
                       nan_to_7f((uint32_t)out[2]), nan_to_7f((uint32_t)out[3]));
 }
 
+// A 16-byte store at device scope (SC1).  Each XCD of the chip has its own
+// L2, and such a store is written through to memory as it is issued; an
+// ordinary store stays dirty in the L2 until the write-back that ends the
+// kernel, which then holds the kernel's completion (up to the L2 capacity of
+// the written bytes).  The compiler offers no device-scope 16-byte store, so
+// it is inline asm with a 64-bit address.  The compiler's hazard checks do not
+// see into the asm: a VALU write of the VGPRs holding the data of a store of
+// more than 8 bytes needs two wait states after it, which the s_nop provides.
+// Nothing in the kernel reads what it stores, so no wait for it is needed.
+__device__ __forceinline__ void store16_device(uint8_t *p, uint4 v)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(x) : "memory");
+}
+
 // Thread layout: a token's chunks (num_kv_heads x head_dim/16 of them) are
 // consecutive threads; a workgroup covers 256 / chunks tokens per iteration
 // (chunks <= 256), and loops over chunks itself when a token has more.
@@ -123,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
             const uint4 *vs = (const uint4 *)(v + src);
             const uint4 k0 = ks[0], k1 = ks[1], v0 = vs[0], v1 = vs[1];
             const int64_t dst = base + g * head_stride + e;
-            *(uint4 *)(kp + dst) = encode16<FAST>(k0, k1, k_scale, ky);
-            *(uint4 *)(vp + dst) = encode16<FAST>(v0, v1, v_scale, vy);
+            store16_device(kp + dst, encode16<FAST>(k0, k1, k_scale, ky));
+            store16_device(vp + dst, encode16<FAST>(v0, v1, v_scale, vy));
         }
     }
 }
