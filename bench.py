@@ -149,52 +149,61 @@ class DenseBench:
         return res
 
     def run_graph(self, steps: int, warmup: int, rotate: bool):
-        """Per-call time of verify + combine replayed from a HIP graph.
+        """Per-call time of verify + combine replayed from HIP graphs.
 
-        A graph of c = gcd(steps, GRAPH_CALLS) consecutive calls (rotating over
-        the pool copies when rotate) is captured once.  After at least `warmup`
-        untimed calls, exactly `steps` calls (steps / c replays) are timed
-        between two synchronisations; that gives ms per call.  A separate
-        sample of PCT_REPLAYS replays, an event after each, sets self.pcts (the
-        per-call percentiles), so that they rest on at least 50 samples
-        whatever `steps` is."""
+        Graphs of c = gcd(steps, GRAPH_CALLS) consecutive calls are captured
+        once: one on the first pool copy, or (rotate) enough of them that their
+        calls read every pool copy in turn.  After at least `warmup` untimed
+        calls, exactly `steps` calls (steps / c replays, cycling through the
+        graphs) are timed between two synchronisations; that gives ms per call.
+        A separate sample of PCT_REPLAYS replays, an event after each, sets
+        self.pcts (the per-call percentiles), so that they rest on at least 50
+        samples whatever `steps` is."""
         torch = self.torch
         calls = math.gcd(max(1, steps), GRAPH_CALLS)
+        # rotating: graph q holds the calls on copies q*calls .. q*calls + calls - 1
+        # (mod the copy count), and the replays cycle through the graphs, so
+        # that consecutive calls read every copy in turn
+        ngraphs = -(-len(self.pools) // calls) if rotate else 1
+        copy = lambda q, i: (q * calls + i) % len(self.pools) if rotate else 0
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(calls):
-                self.verify(i if rotate else 0)
+                self.verify(copy(0, i))
                 self.combine()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(calls):
-                self.verify(i if rotate else 0)
-                self.combine()
+        graphs = []
+        for q in range(ngraphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    self.verify(copy(q, i))
+                    self.combine()
+            graphs.append(g)
         torch.cuda.synchronize()
-        for _ in range(max(1, -(-warmup // calls))):
-            g.replay()
+        for r in range(max(ngraphs, -(-warmup // calls))):
+            graphs[r % ngraphs].replay()
         torch.cuda.synchronize()
         reps = max(1, steps // calls)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            g.replay()
+        for r in range(reps):
+            graphs[r % ngraphs].replay()
         e1.record()
         torch.cuda.synchronize()
         total_ms = e0.elapsed_time(e1)
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(PCT_REPLAYS + 1)]
         marks[0].record()
         for k in range(PCT_REPLAYS):
-            g.replay()
+            graphs[k % ngraphs].replay()
             marks[k + 1].record()
         torch.cuda.synchronize()
         self.pcts = percentiles([marks[k].elapsed_time(marks[k + 1]) / calls
                                  for k in range(PCT_REPLAYS)], calls)
-        del g
+        del graphs
         return total_ms / (reps * calls)
 
     def output(self):
@@ -305,7 +314,7 @@ class QsaTokensBench(QsaBench):
 def bench_for(w, kernel: str, splits: int = 0):
     """The resident bench of a named workload (dense, sparse over blocks or token
     ids, or a batch of independent requests)."""
-    n = copies_for(2 * w.k_pool.size)
+    n = copies_for(w.kv_bytes())
     if hasattr(w, "sel_tokens"):
         return QsaTokensBench(w, n, kernel)
     if hasattr(w, "sel_blocks"):
@@ -511,9 +520,10 @@ def read_ceiling_at(torch, pa, nbytes: int, reps: int = 20) -> dict:
     return {"bytes": nbytes, "us": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
-def copies_for(pool_bytes: int) -> int:
-    """Enough pool copies that one rotation exceeds twice the Infinity Cache."""
-    return max(2, math.ceil(2 * MALL_BYTES / max(pool_bytes, 1)) + 1)
+def copies_for(touched_bytes: int) -> int:
+    """Enough pool copies that the bytes one rotation reads (touched_bytes per
+    call) exceed twice the Infinity Cache."""
+    return max(2, math.ceil(2 * MALL_BYTES / max(touched_bytes, 1)) + 1)
 
 
 def cpu_baseline(w, outputs: dict, max_seconds: float = 20.0):
@@ -611,7 +621,7 @@ def main():
 
     log(f"[bench] generating {args.workload}")
     w = wl.cached(args.workload)
-    n_copies = copies_for(2 * w.k_pool.size)
+    n_copies = copies_for(w.kv_bytes())
     log(f"[bench] {w.name}: {n_copies} pool copies, kernel={args.kernel}")
     b = bench_for(w, args.kernel, args.splits)
     if not isinstance(w, wl.DenseWorkload):
@@ -643,7 +653,7 @@ def main():
         for name in ["c1", "c2_64k", "c2_128k"]:
             log(f"[bench] sweep {name}")
             ws = wl.cached(name)
-            bs = DenseBench(ws, copies_for(2 * ws.k_pool.size), args.kernel, 0)
+            bs = DenseBench(ws, copies_for(ws.kv_bytes()), args.kernel, 0)
             ms = measure(bs, steps, args.warmup)
             outputs[ws.name] = (ws, ms.pop("out"))
             sweep.append(sweep_entry(ws.name, bs.kv_bytes, bs.plan, ms, ctx=ws.max_tokens))
@@ -651,7 +661,7 @@ def main():
             torch.cuda.empty_cache()
         log("[bench] sweep c4 (QSA)")
         wq = wl.cached("c4")
-        bq = QsaBench(wq, copies_for(2 * wq.k_pool.size), args.kernel)
+        bq = QsaBench(wq, copies_for(wq.kv_bytes()), args.kernel)
         mq = measure(bq, steps, args.warmup)
         outputs[wq.name] = (wq, mq.pop("out"))
         sweep.append(sweep_entry(wq.name, bq.kv_bytes, bq.plan, mq,
@@ -660,7 +670,7 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] sweep c4tok (QSA over token ids)")
         wt = wl.cached("c4tok")
-        bt = QsaTokensBench(wt, copies_for(2 * wt.k_pool.size), args.kernel)
+        bt = QsaTokensBench(wt, copies_for(wt.kv_bytes()), args.kernel)
         mt = measure(bt, steps, args.warmup)
         outputs[wt.name] = (wt, mt.pop("out"))
         sweep.append(sweep_entry(wt.name, bt.kv_bytes, bt.plan, mt,
@@ -669,7 +679,7 @@ def main():
         torch.cuda.empty_cache()
         log("[bench] sweep batch (independent requests)")
         wb = wl.cached("batch")
-        bb = BatchBench(wb, copies_for(2 * wb.k_pool.size), args.kernel)
+        bb = BatchBench(wb, copies_for(wb.kv_bytes()), args.kernel)
         mb = measure(bb, steps, args.warmup)
         outputs[wb.name] = (wb, mb.pop("out"))
         sweep.append(sweep_entry(wb.name, bb.kv_bytes, bb.plan, mb,
