@@ -396,7 +396,8 @@ constexpr int max_slots()
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, DivMagic dm)
+__global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, DivMagic dm,
+                                                                   DivMagic hm, uint32_t g_magic)
 {
     // SPARSE: bf16 queries and a selection list (blocks or token ids); TOK:
     // the list holds token ids, one slot per position, and dm divides by the
@@ -436,17 +437,18 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         unit = __builtin_amdgcn_readfirstlane(rp.unit);
         tps = __builtin_amdgcn_readfirstlane(rp.span);
     }
-    const int b = unit / a.num_kv_heads;
+    const int b = divp(unit, hm);              // unit / num_kv_heads
     const int kvh = unit - b * a.num_kv_heads;
     // rows of a KV unit beyond 48 go to further workgroups (grid z): this one
     // takes rows row0 .. row0 + R - 1 of the unit
     const int row0 = blockIdx.z * (16 * kRowBlocks);
     const int R = min(a.rows - row0, 16 * kRowBlocks), G = a.group;
     // row / G for a row of the KV unit (row < rows <= 96, G <= rows, so
-    // row * G < 2^16): (row * ceil(2^16 / G)) >> 16 is exact, one 24-bit
-    // multiply and a shift where a division takes about twenty instructions,
-    // several of them at quarter rate.
-    const uint32_t g_magic = (65536u + (uint32_t)G - 1u) / (uint32_t)G;
+    // row * G < 2^16): (row * g_magic) >> 16 with g_magic = ceil(2^16 / G)
+    // (from the host) is exact, one 24-bit multiply and a shift where a
+    // division takes about twenty instructions, several of them at quarter
+    // rate.  The divisions by the page size and by the KV head count are
+    // multiply-shifts from the host too (dm, hm).
     auto div_g = [&](int row) __attribute__((always_inline)) {
         return (int)(__umul24((uint32_t)row, g_magic) >> 16);
     };
@@ -1233,9 +1235,10 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
     // (a ragged batch's splits are shared by its units: grid y is 1)
     dim3 grid(a.num_splits, a.ragged ? 1 : a.batch * a.num_kv_heads,
               (a.rows + 16 * kRowBlocks - 1) / (16 * kRowBlocks));
+    const uint32_t g_magic = (65536u + (uint32_t)a.group - 1u) / (uint32_t)a.group;
     hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
-                          make_magic(a.page_size));
+                          make_magic(a.page_size), make_magic(a.num_kv_heads), g_magic);
     return hipGetLastError();
 }
 
