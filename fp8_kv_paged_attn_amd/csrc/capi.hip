@@ -31,7 +31,7 @@ constexpr int kMaxHeads = 65536;
 // the batched entry: up to 16 query rows, up to 96 rows per KV unit (two
 // 48-row chunks, one workgroup each)
 constexpr int kMaxRowsPerUnitBatch = 96;
-constexpr int kMaxQRowsBatch = 16;
+constexpr int kMaxQRowsBatch = pa::kRaggedMaxQRows;
 constexpr int kDefaultCUs = 256;
 // Fewest tokens a split should read, so that the FP32 partial it writes
 // (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.

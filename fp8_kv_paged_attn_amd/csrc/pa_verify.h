@@ -50,13 +50,23 @@ struct VerifyArgs {
     int32_t *split_index;
 };
 
+// Query rows per request of a ragged batch (the batched entry's limit).
+constexpr int kRaggedMaxQRows = 16;
+
 // Longest clamped row length of request b (all its KV heads see the same).
+// The loop is unrolled to the row limit, so that every length load is issued
+// before the first is waited for: one memory round trip, not one per row.
 __device__ inline int request_len(const VerifyArgs &a, int b)
 {
+    const int32_t *lens = a.row_lens + (int64_t)b * a.q_rows;
+    int raw[kRaggedMaxQRows];
+#pragma unroll
+    for (int i = 0; i < kRaggedMaxQRows; ++i)
+        raw[i] = i < a.q_rows ? lens[i] : 0;
     int L = 0;
-    for (int i = 0; i < a.q_rows; ++i) {
-        int l = a.row_lens[(int64_t)b * a.q_rows + i];
-        l = l < 0 ? 0 : (l > a.len_cap ? a.len_cap : l);
+#pragma unroll
+    for (int i = 0; i < kRaggedMaxQRows; ++i) {
+        const int l = raw[i] < 0 ? 0 : (raw[i] > a.len_cap ? a.len_cap : raw[i]);
         L = l > L ? l : L;
     }
     return L;
@@ -92,7 +102,15 @@ __device__ inline RaggedPos ragged_locate(const VerifyArgs &a, int s, int lane, 
     total *= Hkv;
     int64_t T = a.tokens_per_split;
     if (S > U) {
-        int64_t t = (total + (S - U) - 1) / (S - U);
+        // the span ceil(total / (S - U)): a 32-bit division when the sum of
+        // the lengths allows (a 64-bit one takes several times as many
+        // instructions), both on wave-uniform values
+        const int64_t d = S - U;
+        int64_t t;
+        if (total + d <= (int64_t)INT32_MAX)
+            t = (int64_t)(((uint32_t)total + (uint32_t)d - 1u) / (uint32_t)d);
+        else
+            t = (total + d - 1) / d;
         t = (t + 63) / 64 * 64;
         T = t < 64 ? 64 : (t < T ? t : T);
     }
