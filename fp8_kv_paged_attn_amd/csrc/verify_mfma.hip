@@ -387,6 +387,13 @@ struct Cfg {
     static constexpr int QUARTER = kRowBlocks * DQ * 64 * 16;       // bytes per (wave, quarter)
     static constexpr int MERGE = kWaves * (kWaves - 1) * QUARTER;
     static constexpr int SHARED = STAGES > MERGE ? STAGES : MERGE;
+    // Each wave leaves its quarters in a private area: its own four stage
+    // slots (K and V of both stages: no other wave's loads target them) and a
+    // 1/kWaves share of the space past the stages, in 1 KB chunks.
+    static constexpr int SLOT_CHUNKS = BLOCK / 1024;
+    static constexpr int EXTRA = (SHARED - STAGES) / kWaves;
+    static_assert((kWaves - 1) * QUARTER == 4 * BLOCK + EXTRA && EXTRA % 1024 == 0,
+                  "a wave's three quarters fill its stage slots and its extra share");
 };
 
 template <int D>
@@ -1080,10 +1087,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 
     // ---- merge the four waves' states and write the split's partial --------
     // Wave w owns output quarter w: d-blocks [w*DQ, (w+1)*DQ).  Every wave
-    // leaves its accumulators of the three other quarters in LDS (the stages'
-    // space), scaled to its own reference; the owner adds them with weights
+    // leaves its accumulators of the three other quarters in its private part
+    // of LDS, relative to its own reference; the owner adds them with weights
     // 2^(m_ref - M), M the exact row max over the split.
-    wait_vmcnt<0>();   // nothing may still target the stages (the merge area)
+    wait_vmcnt<0>();   // this wave's loads no longer target its stage slots
     // rows that see no token of this split may have accumulated values in
     // blocks processed without masks: they get the empty state
 #pragma unroll
@@ -1115,7 +1122,15 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb)
         lw[rb] = sum_over_groups(l_part[rb]);
-    __syncthreads();   // every wave is done with the stages
+    // Chunk c (1 KB) of wave v's private merge area.  The wave's own loads
+    // are done (the wait above), and no other wave writes there, so it
+    // exports without waiting for the others to finish their blocks.
+    auto xchunk = [&](int v, int c) __attribute__((always_inline)) -> uint8_t * {
+        return c < 4 * C::SLOT_CHUNKS
+                   ? smem + ((c / C::SLOT_CHUNKS) * kWaves + v) * C::BLOCK +
+                         (c % C::SLOT_CHUNKS) * 1024
+                   : smem + C::STAGES + v * C::EXTRA + (c - 4 * C::SLOT_CHUNKS) * 1024;
+    };
     // per wave and row: running max, accumulator reference and row sum
     if (g == 0) {
 #pragma unroll
@@ -1129,13 +1144,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     for (int q = 0; q < kWaves; ++q) {
         if (q == w)
             continue;
-        uint8_t *dstq = smem + (w * (kWaves - 1) + (q < w ? q : q - 1)) * C::QUARTER;
+        const int qi = q < w ? q : q - 1;    // this quarter among the wave's three
 #pragma unroll
         for (int rb = 0; rb < kRowBlocks; ++rb)
             if (rb < nrb)     // row blocks past nrb were never accumulated: zero
 #pragma unroll
                 for (int d = 0; d < C::DQ; ++d)
-                    *(f32x4 *)(dstq + ((rb * C::DQ + d) * 64 + lane) * 16) = acc[rb][q * C::DQ + d];
+                    *(f32x4 *)(xchunk(w, (qi * kRowBlocks + rb) * C::DQ + d) + lane * 16) =
+                        acc[rb][q * C::DQ + d];
     }
     __syncthreads();
     // Every wave derives all four weights 2^(m_ref_v - M) itself, so that one
@@ -1163,10 +1179,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                 for (int vi = 0; vi < kWaves - 1; ++vi) {
                     const int v = vi < q ? vi : vi + 1;
-                    const uint8_t *srcq = smem + (v * (kWaves - 1) + (q < v ? q : q - 1)) * C::QUARTER;
+                    const int qi = q < v ? q : q - 1;   // quarter q among wave v's three
 #pragma unroll
                     for (int d = 0; d < C::DQ; ++d)
-                        xs[vi][d] = *(const f32x4 *)(srcq + ((rb * C::DQ + d) * 64 + lane) * 16);
+                        xs[vi][d] = *(const f32x4 *)(
+                            xchunk(v, (qi * kRowBlocks + rb) * C::DQ + d) + lane * 16);
                 }
             }
             float mv[kWaves], rv[kWaves], lv[kWaves];
@@ -1184,7 +1201,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             float L = 0.0f;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) {
-                const float f = (rv[v] == -INFINITY) ? 0.0f : exp2f(rv[v] - M);
+                // rv <= M: the hardware exp2 (a weight below 2^-126 may
+                // flush to zero, a negligible contribution)
+                const float f = (rv[v] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(rv[v] - M);
                 L += lv[v] * f;
                 fv[v] = f * kPUnscale;
             }
