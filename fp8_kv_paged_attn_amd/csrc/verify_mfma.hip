@@ -844,10 +844,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         wait_groups(1);                              // K(j); V(j) may be in flight
 
         // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
+        // (the first k-block's MFMAs take a zero accumulator operand, so the
+        // scores need no initialisation; they are only read when any)
         f32x4 s[NRB][2];
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-            s[rb][0] = s[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (any) {
             const uint32_t kbase = lds_addr(kst + w * C::BLOCK);
             // all K reads of the block first, so that their latencies overlap
@@ -874,7 +873,8 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                     }
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
-                        s[rb][bb] = mfma_qk(k0, qf[rb][2 * t], s[rb][bb]);
+                        s[rb][bb] = mfma_qk(k0, qf[rb][2 * t],
+                                            t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[rb][bb]);
 #pragma unroll
                     for (int rb = 0; rb < NRB; ++rb)
                         s[rb][bb] = mfma_qk(k1, qf[rb][2 * t + 1], s[rb][bb]);
