@@ -841,7 +841,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         int32_t *tok = &tok_s[w][st][0];
         const int pos0 = lo + (j * kWaves + w) * kSub;
         const bool any = pos0 < hi;                  // wave-uniform
-        wait_groups(1);                              // K(j); V(j) may be in flight
+        // block 0's V is issued once its K is in: the first burst of the grid
+        // carries K alone, so that the first QK can start sooner
+        if (j == 0) {
+            wait_groups(0);                          // K(0)
+            issue_plane(bcur, 0, a.v_pool, v_st, &tok_s[w][0][0]);
+        } else {
+            wait_groups(1);                          // K(j); V(j) may be in flight
+        }
 
         // ---- S^T = K Q^T on this wave's 32 tokens --------------------------
         // (the first k-block's MFMAs take a zero accumulator operand, so the
@@ -1076,7 +1083,6 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     if (nms > 0) {
         bcur = lookup(0);
         issue_plane(bcur, 0, a.k_pool, k_st, nullptr);
-        issue_plane(bcur, 0, a.v_pool, v_st, &tok_s[w][0][0]);
         if (nrb == 1)
             main_loop(std::integral_constant<int, 1>());
         else if (nrb == 2)
