@@ -426,6 +426,14 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave row sum
     __shared__ float xr[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator reference
 
+    // The argument block spans four 64-byte scalar-cache lines; one word of
+    // each, read at entry, brings them all in with one miss, where reading the
+    // fields as they are needed takes a miss per line, in sequence.
+    {
+        const uint32_t *kp = (const uint32_t *)__builtin_amdgcn_kernarg_segment_ptr();
+        const uint32_t t0 = kp[0], t1 = kp[16], t2 = kp[32], t3 = kp[48];
+        asm volatile("" : : "s"(t0), "s"(t1), "s"(t2), "s"(t3));
+    }
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
