@@ -531,8 +531,8 @@ def cpu_baseline(w, outputs: dict, max_seconds: float = 20.0):
     on every workload the bench measured, whose outputs (`outputs`: name ->
     (workload, GPU output)) it is compared with (the accuracy figures).
 
-    Threads: the CPUs this process may use, at most 16 (the host CPUs a GPU machine
-    allots to one GPU); the host's CPU count is reported beside it."""
+    Threads: the CPUs this process may use, at most 16 (a host's share of CPUs
+    per GPU on an 8-GPU MI355X node); the host's CPU count is reported beside it."""
     import oracle
 
     orc = oracle.get()
