@@ -119,7 +119,7 @@ def tokens_case(i: int):
                 row_lens=lens)
 
 
-N_DENSE, N_BATCH, N_QSA, N_TOKENS = 40, 20, 20, 12
+N_DENSE, N_BATCH, N_QSA, N_TOKENS = 80, 40, 40, 24
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
