@@ -32,6 +32,8 @@ CODEGEN_FLAGS = [
 
 # sources whose kernels issue direct-to-LDS loads as inline asm
 ASM_DMA_SOURCES = ["verify_mfma.hip"]
+# sources whose kernels issue wide (more than 8-byte) stores as inline asm
+ASM_STORE_SOURCES = ["cache_write.hip"]
 
 
 def source_files():
@@ -52,14 +54,15 @@ def source_hash() -> str:
 
 
 def check_hazards(extra_flags=()) -> None:
-    """Compile the inline-asm DMA sources to gfx950 assembly and reject the
-    build if a load lacks the wait states gfx9 requires before it."""
+    """Compile the inline-asm sources to gfx950 assembly and reject the build
+    if a direct-to-LDS load lacks the wait states gfx9 requires before it, or
+    a wide asm store the wait states a VALU write of its data needs after it."""
     try:
         from . import asm_hazards
     except ImportError:          # run as a script
         import asm_hazards
 
-    for name in ASM_DMA_SOURCES:
+    def assembly(name):
         src = os.path.join(CSRC, name)
         asm = os.path.join(HERE, name + ".s.tmp")
         cmd = [hipcc(), *CODEGEN_FLAGS, "--cuda-device-only", "-S",
@@ -68,12 +71,22 @@ def check_hazards(extra_flags=()) -> None:
         if r.returncode != 0:
             raise RuntimeError("hipcc -S failed:\n" + r.stdout + r.stderr)
         with open(asm) as f:
-            found = asm_hazards.check(f.read())
+            text = f.read()
         os.remove(asm)
+        return text
+
+    for name in ASM_DMA_SOURCES:
+        found = asm_hazards.check(assembly(name))
         if found:
             lines = "\n".join(f"  {k}: {p}  ->  {t}" for k, p, t in found[:10])
             raise RuntimeError(f"{name}: {len(found)} unprotected hazards before "
                                f"direct-to-LDS loads:\n{lines}")
+    for name in ASM_STORE_SOURCES:
+        found = asm_hazards.check_stores(assembly(name))
+        if found:
+            lines = "\n".join(f"  {t}" for t in found[:10])
+            raise RuntimeError(f"{name}: {len(found)} asm stores without the wait states "
+                               f"after them:\n{lines}")
 
 
 def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:

@@ -63,3 +63,34 @@ def test_vgpr_addressed_load_only_needs_m0_spacing():
     assert asm_hazards.check(VGPR_ADDRESS) == []
     assert [k for k, _, _ in asm_hazards.check(VGPR_ADDRESS.replace(
         "\tv_mov_b32_e32 v5, v9\n", ""))] == ["m0"]
+
+
+# The cache writer's device-scope stores, as the compiler lays out an asm block:
+# a 16-byte store must be followed in its block by s_nop 1 or more (two wait
+# states before a VALU write of its data VGPRs).
+STORE_PROTECTED = """
+	v_cvt_pk_fp8_f32 v13, v10, v11
+	;;#ASMSTART
+	global_store_dwordx4 v[26:27], v[10:13], off sc1
+	s_nop 1
+	;;#ASMEND
+	v_mov_b32_e32 v10, 0
+"""
+
+
+def test_asm_store_with_wait_states_is_clean():
+    assert asm_hazards.check_stores(STORE_PROTECTED) == []
+
+
+def test_asm_store_without_wait_states_is_flagged():
+    bare = STORE_PROTECTED.replace("\ts_nop 1\n", "")
+    assert asm_hazards.check_stores(bare) == ["global_store_dwordx4 v[26:27], v[10:13], off sc1"]
+    one = STORE_PROTECTED.replace("s_nop 1", "s_nop 0")       # one wait state only
+    assert len(asm_hazards.check_stores(one)) == 1
+
+
+def test_narrow_and_compiler_stores_are_not_asm_hazards():
+    narrow = STORE_PROTECTED.replace("dwordx4 v[26:27], v[10:13]", "dwordx2 v[26:27], v[10:11]")
+    assert asm_hazards.check_stores(narrow.replace("\ts_nop 1\n", "")) == []
+    outside = "\tglobal_store_dwordx4 v[26:27], v[10:13], off\n\tv_mov_b32_e32 v10, 0\n"
+    assert asm_hazards.check_stores(outside) == []
