@@ -64,7 +64,8 @@ EXPORTS = ("paged_attn_abi_version", "paged_attn_build_id", "paged_attn_status_s
            "paged_attn_timer_arm", "paged_attn_timer_read", "paged_attn_stream_read_probe",
            "paged_attn_combine_fp32_lse", "paged_attn_verify_batch_e4m3",
            "paged_attn_cache_write_e4m3", "qsa_sparse_verify_tokens_e4m3",
-           "paged_attn_verify_noalloc_e4m3", "paged_attn_combine_batch_fp32")
+           "paged_attn_verify_noalloc_e4m3", "paged_attn_combine_batch_fp32",
+           "paged_attn_combine_batch_fp32_lse")
 
 _LIB = None
 
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(PaPlan), i32, i32, i32, i32, i32,
                                                 f32, p, p]
     L.paged_attn_combine_batch_fp32.restype = i32
+    L.paged_attn_combine_batch_fp32_lse.argtypes = [ctypes.POINTER(PaWorkspace),
+                                                    ctypes.POINTER(PaPlan), i32, i32, i32, i32,
+                                                    i32, f32, p, p, p, p]
+    L.paged_attn_combine_batch_fp32_lse.restype = i32
     L.paged_attn_cache_write_e4m3.argtypes = [p, p, i64, i32, i32, p, ctypes.POINTER(PaKvPool),
                                               f32, f32, p]
     L.paged_attn_cache_write_e4m3.restype = i32
@@ -393,6 +398,33 @@ def paged_attn_combine_batch_fp32(ws, p: PaPlan, batch: int, q_rows: int, num_he
                                              int(head_dim), _scale(out_scale, "out_scale"),
                                              out.data_ptr(), _stream(out.device))
     _check(rc, "paged_attn_combine_batch_fp32")
+
+
+def paged_attn_combine_batch_fp32_lse(ws, p: PaPlan, batch: int, q_rows: int,
+                                      num_heads: int, num_kv_heads: int, head_dim: int,
+                                      out_scale, out=None, out32=None, lse=None) -> None:
+    """The batch combine writing any of: out (float16), out32 (float32), both
+    [batch][q_rows][heads][head_dim] elements, and lse (float32,
+    [batch][q_rows][heads]): the base-2 LSE of each row, for a merge across ranks."""
+    torch = _torch()
+    if len(ws) != 4:
+        raise ValueError("a batch workspace is (acc, max, sum, index)")
+    if out is None and out32 is None and lse is None:
+        raise ValueError("give at least one of out, out32, lse")
+    rows = batch * q_rows * num_heads
+    dev = ws[0].device
+    for t, dt, n in ((out, torch.float16, rows * head_dim), (out32, torch.float32, rows * head_dim),
+                     (lse, torch.float32, rows)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous() or t.numel() < n
+                              or t.device != dev):
+            raise ValueError(f"outputs must be contiguous {dt} tensors of {n} elements on {dev}")
+    ptr = lambda t: None if t is None else t.data_ptr()
+    rc = lib().paged_attn_combine_batch_fp32_lse(ctypes.byref(_ws(*ws)), ctypes.byref(p),
+                                                 int(batch), int(q_rows), int(num_heads),
+                                                 int(num_kv_heads), int(head_dim),
+                                                 _scale(out_scale, "out_scale"), ptr(out),
+                                                 ptr(out32), ptr(lse), _stream(dev))
+    _check(rc, "paged_attn_combine_batch_fp32_lse")
 
 
 def paged_attn_combine_fp32(ws, num_splits: int, num_rows: int, head_dim: int, out_scale,

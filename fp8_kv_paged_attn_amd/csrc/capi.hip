@@ -668,13 +668,16 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     return dispatch(a, plan, head_dim, pa::kModeDense, static_cast<hipStream_t>(stream));
 }
 
-int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *plan,
-                                      int32_t batch, int32_t q_rows, int32_t num_heads,
-                                      int32_t num_kv_heads, int32_t head_dim, float out_scale,
-                                      void *out_fp16, void *stream)
+namespace {
+
+// The batch combine's checks and launch, writing any of the three outputs.
+int32_t combine_batch_checked(const pa_workspace *ws, const pa_plan *plan, int32_t batch,
+                              int32_t q_rows, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float out_scale, void *out_fp16,
+                              float *out_fp32, float *lse, void *stream)
 {
     int32_t rc, rows_per_unit = 0;
-    if (!plan || !out_fp16)
+    if (!plan || (!out_fp16 && !out_fp32 && !lse))
         return PA_EINVAL;
     if ((rc = check_shape(q_rows, num_heads, num_kv_heads, head_dim, &rows_per_unit,
                           kMaxQRowsBatch, kMaxRowsPerUnitBatch)) != PA_OK)
@@ -690,15 +693,39 @@ int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *pla
     if ((rc = check_ws(ws, plan, rows_per_unit, head_dim,
                        (int64_t)batch * num_kv_heads + 1)) != PA_OK)
         return rc;
-    if (!aligned16(ws->acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0)
+    if (!aligned16(ws->acc) || (reinterpret_cast<uintptr_t>(out_fp16) & 7u) != 0 ||
+        !aligned16(out_fp32) || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
         return PA_EALIGN;
     if ((rc = check_device()) != PA_OK)
         return rc;
     const hipError_t err = pa::launch_combine_ragged(
         ws->acc, ws->max, ws->sum, ws->index, plan->num_splits, batch, q_rows, num_heads,
-        num_kv_heads, head_dim, out_scale, static_cast<uint16_t *>(out_fp16),
+        num_kv_heads, head_dim, out_scale, static_cast<uint16_t *>(out_fp16), out_fp32, lse,
         static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+}  // namespace
+
+int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *plan,
+                                      int32_t batch, int32_t q_rows, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, float out_scale,
+                                      void *out_fp16, void *stream)
+{
+    if (!out_fp16)
+        return PA_EINVAL;
+    return combine_batch_checked(ws, plan, batch, q_rows, num_heads, num_kv_heads, head_dim,
+                                 out_scale, out_fp16, nullptr, nullptr, stream);
+}
+
+int32_t paged_attn_combine_batch_fp32_lse(const pa_workspace *ws, const pa_plan *plan,
+                                          int32_t batch, int32_t q_rows, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          float out_scale, void *out_fp16, float *out_fp32,
+                                          float *lse, void *stream)
+{
+    return combine_batch_checked(ws, plan, batch, q_rows, num_heads, num_kv_heads, head_dim,
+                                 out_scale, out_fp16, out_fp32, lse, stream);
 }
 
 int32_t paged_attn_combine_fp32(const float *ws_acc, const float *ws_max, const float *ws_sum,

@@ -236,13 +236,13 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
 hipError_t launch_combine_ragged(const float *acc, const float *mx, const float *sm,
                                  const int32_t *index, int num_splits, int batch, int q_rows,
                                  int num_heads, int num_kv_heads, int head_dim, float out_scale,
-                                 uint16_t *out, hipStream_t stream)
+                                 uint16_t *out, float *out32, float *lse, hipStream_t stream)
 {
     const int64_t rows = (int64_t)batch * q_rows * num_heads;
     const int64_t units = (int64_t)batch * num_kv_heads;
     const int per_row = (int)((num_splits + units - 1) / units);
     return launch_any(acc, mx, sm, num_splits, per_row < 1 ? 1 : per_row, (int)rows, head_dim,
-                      out_scale, out, nullptr, nullptr,
+                      out_scale, out, out32, lse,
                       RaggedRows{index, q_rows, num_heads, num_heads / num_kv_heads, num_kv_heads},
                       stream);
 }

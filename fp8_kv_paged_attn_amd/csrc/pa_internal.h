@@ -24,6 +24,6 @@ hipError_t launch_combine(const float *acc, const float *mx, const float *sm, in
 hipError_t launch_combine_ragged(const float *acc, const float *mx, const float *sm,
                                  const int32_t *index, int num_splits, int batch, int q_rows,
                                  int num_heads, int num_kv_heads, int head_dim, float out_scale,
-                                 uint16_t *out, hipStream_t stream);
+                                 uint16_t *out, float *out32, float *lse, hipStream_t stream);
 
 }  // namespace pa

@@ -307,6 +307,24 @@ int32_t paged_attn_combine_batch_fp32(const pa_workspace *ws, const pa_plan *pla
                                       int32_t num_kv_heads, int32_t head_dim, float out_scale,
                                       void *out_fp16, void *stream);
 
+/* The batch combine for a merge across ranks ([NB] commit exposing an optional
+ * base-2 LSE and FP32 partial output for cross-rank merging): the combination
+ * of paged_attn_combine_batch_fp32, writing any of
+ *   out_fp16 [batch][q_rows][num_heads][head_dim]  as paged_attn_combine_batch_fp32
+ *   out_fp32 the same shape                        the values before FP16 rounding
+ *   lse      [batch][q_rows][num_heads]            the base-2 log of each row's whole
+ *                                                  softmax sum, -inf for a row whose
+ *                                                  splits are all empty
+ * with the meanings of paged_attn_combine_fp32_lse.  Null outputs are skipped; at
+ * least one must be given (PA_EINVAL otherwise); out_fp16 8-byte, out_fp32
+ * 16-byte, lse 4-byte aligned (PA_EALIGN otherwise).  Other arguments and errors
+ * as for paged_attn_combine_batch_fp32. */
+int32_t paged_attn_combine_batch_fp32_lse(const pa_workspace *ws, const pa_plan *plan,
+                                          int32_t batch, int32_t q_rows, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          float out_scale, void *out_fp16, float *out_fp32,
+                                          float *lse, void *stream);
+
 /* FP32 combination of split partials into FP16 rows ([DN] first section):
  *   M = max over non-empty splits of max[s][r],  w_s = 2^(max[s][r] - M),
  *   out[r][d] = fp16_rne(out_scale * sum_s w_s acc[s][r][d] / sum_s w_s sum[s][r]),

@@ -448,6 +448,14 @@ def test_verify_batch_without_device_reports_edevice(L):
     assert L.paged_attn_verify_batch_e4m3(A, ctypes.byref(pool), A, 8, A, 4, 16, 6, 1, 256,
                                           0.0625, 1.0, ctypes.byref(p), ctypes.byref(ws),
                                           None) == PA_EDEVICE
+    lse = L.paged_attn_combine_batch_fp32_lse
+    args = (ctypes.byref(ws), ctypes.byref(p), 4, 16, 6, 1, 256, 1.0)
+    assert lse(*args, A, None, None, None) == PA_EDEVICE
+    assert lse(*args, None, ctypes.c_void_p(0x80000), ctypes.c_void_p(0x90000), None) == PA_EDEVICE
+    assert lse(*args, None, None, None, None) == PA_EINVAL             # no output
+    assert lse(*args, None, ctypes.c_void_p(0x80008), None, None) == PA_EALIGN   # out_fp32
+    assert lse(*args, None, None, ctypes.c_void_p(0x90002), None) == PA_EALIGN   # lse
+    assert lse(*args[:2], 4, 16, 6, 1, 64, 1.0, A, None, None, None) == PA_EUNSUPPORTED
 
 
 def test_cache_write_rejects_bad_arguments(L):

@@ -907,6 +907,53 @@ def test_batch_matches_single_requests(kernel):
         assert np.all(mx[n:] == -np.inf) and not sm[n:].any(), b
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_batch_combine_lse(orc, kernel):
+    """The batch combine for a merge across ranks: its FP16 output is
+    bit-identical to the plain batch combine's; its FP32 output and base-2 LSE
+    match the FP64 oracle merge of each unit's own FP32 partials (the split
+    index the verify wrote); rows of length zero give LSE -inf and zeros."""
+    w = wl.make_dense_batch("blse", 0xB15E, ctxs=[1000, 300, 770], q_rows=4, num_heads=12,
+                            num_kv_heads=2, head_dim=128, page_size=96, sigma=1.0,
+                            k_scale=0.5, v_scale=1.5, max_blocks=12)
+    lens = w.row_lens.copy()
+    lens[1] = [300, 0, 250, 1]
+    w = dataclasses.replace(w, row_lens=lens)
+    announce("batch combine lse", kernel)
+    _, p, ws = gu.run_batch(w, kernel, splits=11, return_ws=True)
+    dev_ws = tuple(torch.from_numpy(x).to(gu.DEV) for x in ws)
+    B, Q, H, Hkv, D = w.batch, w.q_rows, w.num_heads, w.num_kv_heads, w.head_dim
+    G = H // Hkv
+    rows = B * Q * H
+    out16 = torch.empty(rows * D, dtype=torch.float16, device=gu.DEV)
+    ref16 = torch.empty(rows * D, dtype=torch.float16, device=gu.DEV)
+    out32 = torch.empty(rows * D, dtype=torch.float32, device=gu.DEV)
+    lse = torch.empty(rows, dtype=torch.float32, device=gu.DEV)
+    pa.paged_attn_combine_batch_fp32(dev_ws, p, B, Q, H, Hkv, D, w.v_scale, ref16)
+    pa.paged_attn_combine_batch_fp32_lse(dev_ws, p, B, Q, H, Hkv, D, w.v_scale, out=out16,
+                                         out32=out32, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, ref16)
+    acc, mx, sm, index = ws
+    got = out32.cpu().numpy().astype(np.float64).reshape(B, Q, H, D)
+    gl = lse.cpu().numpy().astype(np.float64).reshape(B, Q, H)
+    for b in range(B):
+        for g in range(Hkv):
+            u = b * Hkv + g
+            s0, s1 = int(index[u]), int(index[u + 1])
+            ref_out, ref_lse = orc.combine(acc[s0:s1], mx[s0:s1], sm[s0:s1], w.v_scale,
+                                           with_lse=True)
+            for ru in range(Q * G):
+                i, h = ru // G, g * G + ru % G
+                if not np.isfinite(ref_lse[ru]):
+                    assert gl[b, i, h] == -np.inf and not got[b, i, h].any(), (b, i, h)
+                    continue
+                scale = max(np.abs(ref_out[ru]).max(), 1e-30)
+                assert np.abs(got[b, i, h] - ref_out[ru]).max() <= 2e-6 * scale, (b, i, h)
+                assert abs(gl[b, i, h] - ref_lse[ru]) <= 2e-6 * max(1.0, abs(ref_lse[ru])), (b, i, h)
+    assert np.isinf(gl[1, 1]).all() and not got[1, 1].any()      # the zero-length row
+
+
 def test_batch_config(orc):
     """The named batch configuration (8 requests, q16, contexts 4K-32K) at full
     size, the MFMA kernel in the benchmark's plan."""
