@@ -25,7 +25,7 @@ from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpaged_attn_e4m3.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 PA_KERNEL = {"auto": 0, "simple": 1, "mfma": 2}
 PA_SELECTION = {"dense": 0, "blocks": 1, "tokens": 2, "batch": 3}
@@ -44,12 +44,14 @@ class PaPlan(ctypes.Structure):
                 ("rows_per_kv_unit", ctypes.c_int32), ("num_kv_units", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("selection", ctypes.c_int32), ("ws_acc_bytes", ctypes.c_int64),
-                ("ws_stat_bytes", ctypes.c_int64), ("ws_index_bytes", ctypes.c_int64)]
+                ("ws_stat_bytes", ctypes.c_int64), ("ws_index_bytes", ctypes.c_int64),
+                ("rows_per_workgroup", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"PaPlan(splits={self.num_splits}, tokens_per_split={self.tokens_per_split}, "
                 f"kernel={self.kernel}, max_tokens={self.max_tokens}, "
-                f"rows={self.rows_per_kv_unit}, units={self.num_kv_units})")
+                f"rows={self.rows_per_kv_unit}, units={self.num_kv_units}, "
+                f"rows_per_workgroup={self.rows_per_workgroup})")
 
 
 class PaWorkspace(ctypes.Structure):

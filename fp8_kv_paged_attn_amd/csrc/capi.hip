@@ -36,6 +36,8 @@ constexpr int kDefaultCUs = 256;
 // Fewest tokens a split should read, so that the FP32 partial it writes
 // (rows x (head_dim + 2) x 4 bytes) stays small against its K/V bytes.
 constexpr int kMinTokensPerSplit = 128;
+// Tokens of one step of an MFMA workgroup (four waves of 32-token blocks).
+constexpr int kChunkStepTokens = 128;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned16(int64_t v) { return (v & 15) == 0; }
@@ -128,6 +130,12 @@ int32_t check_scales(float sm_scale, float k_scale)
     return PA_OK;
 }
 
+// Rows of a KV unit one MFMA workgroup takes (a plan's 0 reads as 48).
+int32_t chunk_rows(const pa_plan *plan)
+{
+    return plan->rows_per_workgroup == 0 ? kMaxRowsPerUnit : plan->rows_per_workgroup;
+}
+
 // A plan fits a call when it was made for the call's sizes, page size and
 // selection, its splits cover the list without a split wholly past it and
 // without 32-bit overflow of a split's bounds, and -- for the MFMA kernel --
@@ -145,6 +153,11 @@ int32_t check_plan(const pa_plan *plan, int32_t list_len, int32_t rows_per_unit,
         plan->tokens_per_split % kTileTokens != 0 || plan->num_splits > 65535)
         return PA_EPLAN;
     if (plan->kernel < PA_KERNEL_AUTO || plan->kernel > PA_KERNEL_MFMA)
+        return PA_EPLAN;
+    const int32_t ch = chunk_rows(plan);
+    if (ch != 16 && ch != 32 && ch != kMaxRowsPerUnit)
+        return PA_EPLAN;
+    if (selection == PA_SEL_BATCH && ch != kMaxRowsPerUnit)
         return PA_EPLAN;
     if (plan->kernel != PA_KERNEL_SIMPLE &&
         pa::mfma_slots_needed(plan->tokens_per_split, page_size, selection == PA_SEL_TOKENS) >
@@ -320,6 +333,7 @@ int32_t sparse_verify(pa::VerifyMode mode, const void *q_bf16, const pa_kv_pool 
     a.num_kv_heads = num_kv_heads;
     a.group = num_heads / num_kv_heads;
     a.rows = rows_per_unit;
+    a.chunk_rows = chunk_rows(plan);
     a.num_splits = plan->num_splits;
     a.tokens_per_split = plan->tokens_per_split;
     a.total_rows = (int32_t)total_rows;
@@ -380,6 +394,7 @@ int32_t dense_args(const void *q_fp16, const pa_kv_pool *kv, const int32_t *bloc
     a.num_kv_heads = num_kv_heads;
     a.group = num_heads / num_kv_heads;
     a.rows = rows_per_unit;
+    a.chunk_rows = chunk_rows(plan);
     a.num_splits = plan->num_splits;
     a.tokens_per_split = plan->tokens_per_split;
     a.total_rows = q_rows * num_heads;
@@ -481,37 +496,73 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
         out->ws_acc_bytes = splits * rows_per_kv_unit * head_dim * 4;
         out->ws_stat_bytes = splits * rows_per_kv_unit * 4;
         out->ws_index_bytes = ((int64_t)num_kv_units + 1) * 4;
+        out->rows_per_workgroup = kMaxRowsPerUnit;
         return PA_OK;
     }
-    int64_t splits;
-    if (requested_splits > 0) {
-        splits = requested_splits;
-    } else {
-        // one workgroup per compute unit over all units, a unit of more than
-        // 48 rows taking one workgroup per 48-row chunk ...
-        const int64_t chunks = ((int64_t)rows_per_kv_unit + 47) / 48;
-        const int64_t wgs = (int64_t)num_kv_units * chunks;
-        splits = (cus + wgs - 1) / wgs;
-        // ... but no split shorter than kMinTokensPerSplit tokens
-        int64_t cap = ((int64_t)max_tokens + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
-        if (cap < 1)
-            cap = 1;
-        if (splits > cap)
-            splits = cap;
-    }
-    if (splits > tiles)
-        splits = tiles;
-    if (splits > 65535)
-        splits = 65535;
-    const int64_t tiles_per_split = (tiles + splits - 1) / splits;
-    int64_t tps = tiles_per_split * kTileTokens;
     // longest split whose page slots (token ids: entries) fit the MFMA
     // kernel's cache: (T - 1) / page + 2 <= slots, i.e. T <= (slots - 1) * page
     int64_t tcap = selection == PA_SEL_TOKENS ? slots : (slots - 1) * (int64_t)page_size;
     tcap = tcap / kTileTokens * kTileTokens;
-    if (tps > tcap)
-        tps = tcap;
-    splits = max_tokens > 0 ? ((int64_t)max_tokens + tps - 1) / tps : 1;
+    // the split length for a wanted split count: whole tiles, within the
+    // cache, and the count that length needs
+    struct Shape {
+        int64_t splits, tps;
+    };
+    auto shape_for = [&](int64_t want) -> Shape {
+        if (want > tiles)
+            want = tiles;
+        if (want > 65535)
+            want = 65535;
+        int64_t tps = (tiles + want - 1) / want * kTileTokens;
+        if (tps > tcap)
+            tps = tcap;
+        return {max_tokens > 0 ? ((int64_t)max_tokens + tps - 1) / tps : 1, tps};
+    };
+    // no split shorter than kMinTokensPerSplit tokens
+    int64_t min_cap = ((int64_t)max_tokens + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
+    if (min_cap < 1)
+        min_cap = 1;
+    Shape sh;
+    int64_t chunk = kMaxRowsPerUnit;
+    if (requested_splits > 0) {
+        sh = shape_for(requested_splits);
+    } else {
+        // one workgroup per compute unit over all units, a unit of more than
+        // 48 rows taking one workgroup per 48-row chunk ...
+        const int64_t wgs = (int64_t)num_kv_units * (((int64_t)rows_per_kv_unit + 47) / 48);
+        int64_t want = (cus + wgs - 1) / wgs;
+        // ... but no split shorter than kMinTokensPerSplit tokens
+        sh = shape_for(want < min_cap ? want : min_cap);
+        // A short list leaves each workgroup one 128-token step (one block
+        // per wave) and a fixed cost of the same order.  Smaller row chunks
+        // then put more compute units on the list, with longer splits and
+        // less work per token each (the chunks of a split read the same K/V,
+        // mostly from L2): 16 rows, else 32, when that fills at most every
+        // compute unit with splits of at most 256 tokens.  (MI355X, q8 rows
+        // of six heads: at 8K tokens 48-row chunks took 14.8 us per call, 16
+        // rows 11.6; at 32K 20.7 against 16.3 with 32 rows; at 64K and up,
+        // where a 48-row workgroup already has two steps or more, smaller
+        // chunks were slower.)
+        if (sh.tps <= kChunkStepTokens) {
+            for (int64_t c : {(int64_t)16, (int64_t)32}) {
+                if (rows_per_kv_unit <= c)
+                    continue;   // one chunk of the unit either way
+                const int64_t per = (int64_t)num_kv_units * (((int64_t)rows_per_kv_unit + c - 1) / c);
+                int64_t w = cus / per;
+                if (w > min_cap)
+                    w = min_cap;
+                if (w < 1)
+                    continue;
+                const Shape sc = shape_for(w);
+                if (sc.splits * per <= cus && sc.tps <= 2 * kChunkStepTokens) {
+                    sh = sc;
+                    chunk = c;
+                    break;
+                }
+            }
+        }
+    }
+    const int64_t splits = sh.splits, tps = sh.tps;
     if (splits > 65535 || splits * tps > INT32_MAX)
         return PA_EUNSUPPORTED;
     const int64_t rows = (int64_t)rows_per_kv_unit * num_kv_units;
@@ -527,6 +578,7 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     out->selection = selection;
     out->ws_acc_bytes = splits * rows * head_dim * 4;
     out->ws_stat_bytes = splits * rows * 4;
+    out->rows_per_workgroup = (int32_t)chunk;
     return PA_OK;
 }
 
@@ -656,6 +708,7 @@ int32_t paged_attn_verify_batch_e4m3(const void *q_fp16, const pa_kv_pool *kv,
     a.num_kv_heads = num_kv_heads;
     a.group = num_heads / num_kv_heads;
     a.rows = rows_per_unit;
+    a.chunk_rows = chunk_rows(plan);
     a.num_splits = plan->num_splits;
     a.tokens_per_split = plan->tokens_per_split;
     a.total_rows = (int32_t)total_rows;

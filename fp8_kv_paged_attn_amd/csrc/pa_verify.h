@@ -35,6 +35,8 @@ struct VerifyArgs {
                                 // topk*page; tokens: topk)
     int32_t batch, q_rows, num_heads, num_kv_heads, group;  // group = H / Hkv
     int32_t rows;               // rows per KV unit = q_rows * group
+    int32_t chunk_rows;         // rows of a KV unit one MFMA workgroup takes: 16, 32
+                                // or 48 (grid z counts the chunks; ragged: 48)
     int32_t num_splits, tokens_per_split;
     int32_t total_rows;         // rows of the workspace = B * q_rows * H
     float logit_scale;          // sm_scale * k_scale * log2(e)

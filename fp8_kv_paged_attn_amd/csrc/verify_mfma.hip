@@ -454,10 +454,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     const int b = divp(unit, hm);              // unit / num_kv_heads
     const int kvh = unit - b * a.num_kv_heads;
-    // rows of a KV unit beyond 48 go to further workgroups (grid z): this one
-    // takes rows row0 .. row0 + R - 1 of the unit
-    const int row0 = blockIdx.z * (16 * kRowBlocks);
-    const int R = min(a.rows - row0, 16 * kRowBlocks), G = a.group;
+    // the rows of a KV unit are taken in chunks of 16, 32 or 48 (one workgroup
+    // each, grid z): this one takes rows row0 .. row0 + R - 1 of the unit
+    const int row0 = blockIdx.z * a.chunk_rows;
+    const int R = min(a.rows - row0, a.chunk_rows), G = a.group;
     // row / G for a row of the KV unit (row < rows <= 96, G <= rows, so
     // row * G < 2^16): (row * g_magic) >> 16 with g_magic = ceil(2^16 / G)
     // (from the host) is exact, one 24-bit multiply and a shift where a
@@ -1264,10 +1264,10 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
     // every split's page slots (token ids: positions) must fit the LDS slot cache
     if (mfma_slots_needed(a.tokens_per_split, a.page_size, MODE == kModeTokens) > max_slots<D>())
         return hipErrorNotSupported;
-    // grid z: chunks of 48 rows of a KV unit (one chunk up to 48 rows)
+    // grid z: the row chunks of a KV unit
     // (a ragged batch's splits are shared by its units: grid y is 1)
     dim3 grid(a.num_splits, a.ragged ? 1 : a.batch * a.num_kv_heads,
-              (a.rows + 16 * kRowBlocks - 1) / (16 * kRowBlocks));
+              (a.rows + a.chunk_rows - 1) / a.chunk_rows);
     const uint32_t g_magic = (65536u + (uint32_t)a.group - 1u) / (uint32_t)a.group;
     hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
@@ -1280,7 +1280,11 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
 hipError_t launch_verify_mfma(const VerifyArgs &a, int head_dim, VerifyMode mode,
                               hipStream_t stream, const hipEvent_t *ev)
 {
-    if (a.rows < 1 || a.rows > 65535 * 16 * kRowBlocks)
+    if (a.chunk_rows != 16 && a.chunk_rows != 32 && a.chunk_rows != 16 * kRowBlocks)
+        return hipErrorNotSupported;
+    if (a.ragged && a.chunk_rows != 16 * kRowBlocks)
+        return hipErrorNotSupported;
+    if (a.rows < 1 || a.rows > 65535 * a.chunk_rows)
         return hipErrorNotSupported;
     // the partial stores' byte offsets from a KV unit's first row are 32-bit
     const int64_t span = a.ragged ? a.rows : (int64_t)a.q_rows * a.num_heads;

@@ -59,7 +59,7 @@ extern "C" {
  * requires the revision it was written for, so new workspace layouts never
  * reach an older binary).  Revision 2: the planner takes the page size and
  * the selection kind, and plans carry them. */
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 enum pa_status {
     PA_OK = 0,
@@ -141,6 +141,10 @@ typedef struct pa_plan {
     int64_t ws_acc_bytes;          /* FP32 [num_splits][rows][head_dim] */
     int64_t ws_stat_bytes;         /* FP32 [num_splits][rows], each of max and sum */
     int64_t ws_index_bytes;        /* int32 [num_kv_units + 1] (PA_SEL_BATCH), else 0 */
+    int32_t rows_per_workgroup;    /* rows of a KV unit one MFMA workgroup takes: 16, 32
+                                      or 48 (0 reads as 48); PA_SEL_BATCH: 48.  The
+                                      workspace and the results do not depend on it;
+                                      the plain kernel always takes 48 */
 } pa_plan;
 
 /* (host) FP32 split workspace written by the verify entry points and read by
@@ -177,7 +181,12 @@ typedef struct pa_workspace {
  * than 48 rows counts once per 48-row chunk, each chunk being a workgroup),
  * but no split shorter than 128 tokens, so that the FP32 partial each split
  * writes stays small against its K/V bytes (the pages tune split counts per
- * device and region, [QSA] sm_120 retune commit).  Either count is then
+ * device and region, [QSA] sm_120 retune commit).  When that leaves each
+ * workgroup a single 128-token step (short lists), the rows of a unit are cut
+ * finer (rows_per_workgroup 16, else 32) if that still fills at most num_cus
+ * workgroups with splits of at most 256 tokens: more compute units read the
+ * list, and each does less per token.  A requested count keeps 48-row chunks.
+ * Either count is then
  * clamped to what the token count allows and raised where a split would
  * otherwise cover more pages (token ids: entries) than the MFMA kernel keeps
  * per workgroup, 1,024 at head_dim 256 and 2,048 at 128, so that every plan

@@ -59,9 +59,11 @@ def dense_plan(w, kernel="auto", splits: Optional[int] = None):
 
 
 def run_dense(w, kernel="auto", splits: Optional[int] = None, d: Optional[DenseDev] = None,
-              k=None, v=None, return_ws=False):
+              k=None, v=None, return_ws=False, rows_per_workgroup: Optional[int] = None):
     d = d or dense_to_dev(w)
     p = dense_plan(w, kernel, splits)
+    if rows_per_workgroup is not None:
+        p.rows_per_workgroup = rows_per_workgroup
     ws = pa.make_workspace(p, w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.verify(d.q, d.k if k is None else k, d.v if v is None else v, d.table, d.lens,
                     w.max_tokens, sm_scale=w.sm_scale, k_scale=w.k_scale, v_scale=w.v_scale,
@@ -115,7 +117,8 @@ def oracle_batch(orc, w, nthreads=1) -> np.ndarray:
                      for b in range(w.batch)])
 
 
-def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
+def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False,
+            rows_per_workgroup: Optional[int] = None):
     q = bf16_tensor(w.q_bits).to(DEV)
     k = torch.from_numpy(w.k_pool).to(DEV)
     v = torch.from_numpy(w.v_pool).to(DEV)
@@ -126,6 +129,8 @@ def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False):
     s = w.num_splits if splits is None else splits
     p = pa.plan(w.topk * w.page_size, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim,
                 w.page_size, "blocks", splits=s, kernel=kernel)
+    if rows_per_workgroup is not None:
+        p.rows_per_workgroup = rows_per_workgroup
     ws = pa.make_workspace(p, w.batch * w.q_rows * w.num_heads, w.head_dim, DEV)
     out = pa.qsa_verify(q, k, v, bt, sel, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                         v_scale=w.v_scale, p=p, ws=ws)

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_and_status(L):
-    assert L.paged_attn_abi_version() == pa.ABI_VERSION == 2
+    assert L.paged_attn_abi_version() == pa.ABI_VERSION == 3
     for rc in (PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EALIGN, PA_EDEVICE, PA_EHIP,
                PA_EPLAN, PA_ESCRATCH, 12345):
         s = L.paged_attn_status_string(rc)
@@ -69,6 +69,9 @@ def mfma_slots_fit(p) -> bool:
     (2048, 48, 32, 128, 64, "tokens", 0, 0), (4096, 48, 256, 256, 64, "tokens", 0, 0),
     (262144, 48, 1, 256, 1, "dense", 0, 0), (262144, 48, 1, 256, 1, "dense", 0, 1),
     (20000, 48, 1, 128, 1, "blocks", 0, 1), (70000, 12, 1, 256, 2, "dense", 0, 0),
+    (16384, 48, 1, 256, 3296, "dense", 0, 0), (32768, 48, 1, 256, 3296, "dense", 0, 0),
+    (8192, 40, 1, 256, 3296, "dense", 0, 0), (8192, 20, 2, 256, 64, "dense", 0, 0),
+    (4096, 48, 2, 128, 64, "blocks", 0, 0), (512, 48, 4, 256, 16, "tokens", 0, 0),
 ])
 def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
     p = pa.plan(max_tokens, rows, units, D, page, sel, num_cus=cus, splits=req)
@@ -79,6 +82,20 @@ def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
     if max_tokens > 0:
         assert (S - 1) * T < max_tokens, "no split may lie wholly past max_tokens"
     assert mfma_slots_fit(p), "every plan runs on the MFMA kernel"
+    ch = p.rows_per_workgroup
+    assert ch in (16, 32, 48)
+    if ch != 48:
+        # finer row chunks only for short lists (one 128-token step per
+        # 48-row workgroup), at most one workgroup per compute unit, splits of
+        # at most 256 tokens, and only where they cut a unit into more chunks
+        c = cus if cus > 0 else 256
+        assert not req and rows > ch
+        assert S * units * -(-rows // ch) <= c and T <= 256
+        p48 = -(-tiles // min(max(1, -(-c // (units * -(-rows // 48)))),
+                              max(1, -(-max_tokens // 128)))) * 64
+        assert p48 <= 128
+        assert (p.ws_acc_bytes, p.ws_stat_bytes) == (S * rows * units * D * 4, S * rows * units * 4)
+        return
     # the slot cap only ever raises the count: the uncapped rule's count is a lower bound
     if req:
         want = min(req, tiles)
@@ -108,6 +125,23 @@ def test_plan_counts_row_chunks(L):
     assert pa.plan(32960, 96, 8, 256, 1600, num_cus=256).num_splits == 16
     # 8 units of 48 rows: 32 splits wanted; 1,088 tokens each cover 32,960 in 31
     assert pa.plan(32960, 48, 8, 256, 1600, num_cus=256).num_splits == 31
+
+
+@pytest.mark.parametrize("max_tokens,rows,units,req,expect", [
+    (8192, 48, 1, 0, (64, 128, 16)),      # 3 chunks x 64 splits = 192 workgroups
+    (16384, 48, 1, 0, (64, 256, 16)),     # 16-row chunks with two steps per split
+    (32768, 48, 1, 0, (128, 256, 32)),    # 16 rows would need 448-token splits
+    (49152, 48, 1, 0, (256, 192, 48)),    # finer chunks would need splits of 384+
+    (65536, 48, 1, 0, (256, 256, 48)),    # two steps per 48-row workgroup already
+    (8192, 48, 1, 64, (64, 128, 48)),     # a requested count keeps 48-row chunks
+    (8192, 12, 1, 0, (64, 128, 48)),      # one chunk of 16 rows either way
+    (8192, 20, 1, 0, (64, 128, 16)),      # 16 + 4 rows
+    (8192, 48, 2, 0, (32, 256, 16)),      # 2 units x 3 chunks x 32 splits of 256 tokens
+])
+def test_plan_row_chunks_for_short_lists(L, max_tokens, rows, units, req, expect):
+    p = pa.plan(max_tokens, rows, units, 256, 3296, num_cus=256, splits=req)
+    assert (p.num_splits, p.tokens_per_split, p.rows_per_workgroup) == expect
+    assert pa.plan(max_tokens, rows, units, 256, 3296, "batch", num_cus=256).rows_per_workgroup == 48
 
 
 def test_plan_raises_splits_to_fit_the_slot_cache(L):
@@ -281,6 +315,10 @@ def test_verify_rejects_bad_arguments(L):
     _spoil(L, "selection", 1, PA_EPLAN, sub="plan")                # made for blocks
     _spoil(L, "tokens_per_split", 1 << 30, PA_EPLAN, sub="plan")   # S*T past INT32_MAX
     _spoil(L, "num_splits", 200, PA_EPLAN, sub="plan")              # splits wholly past the end
+    _spoil(L, "rows_per_workgroup", 24, PA_EPLAN, sub="plan")       # chunks of 16, 32 or 48 rows
+    _spoil(L, "rows_per_workgroup", 64, PA_EPLAN, sub="plan")
+    for ch in (0, 16, 32, 48):                                      # 0 reads as 48
+        _spoil(L, "rows_per_workgroup", ch, PA_EDEVICE, sub="plan")
     _spoil(L, "acc_bytes", 1024, PA_EWORKSPACE, sub="ws")
     _spoil(L, "stat_bytes", 4, PA_EWORKSPACE, sub="ws")
     _spoil(L, "sum", None, PA_EINVAL, sub="ws")
@@ -432,6 +470,10 @@ def test_verify_batch_rejects_bad_arguments(L):
     assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 3, 0, 0, ctypes.byref(few)) == PA_OK
     few.num_splits = 3
     assert call(plan=few) == PA_EPLAN                           # fewer splits than units
+    fine = pa.PaPlan()
+    assert L.paged_attn_plan(64 * 8, 96, 4, 256, 64, 3, 0, 0, ctypes.byref(fine)) == PA_OK
+    fine.rows_per_workgroup = 16
+    assert call(plan=fine) == PA_EPLAN                          # a batch takes 48-row chunks
 
 
 @no_device
@@ -542,3 +584,30 @@ def test_python_binding_rejects_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(pa, "_LIB", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         pa.lib()
+
+
+@pytest.mark.parametrize("cname,pyname", [("pa_plan", "PaPlan"), ("pa_workspace", "PaWorkspace"),
+                                          ("pa_kv_pool", "PaKvPool")])
+def test_struct_layout_matches_header(tmp_path, cname, pyname):
+    """The binding's ctypes structs have the header's size and field offsets
+    (a C program built against the header prints them)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    cls = getattr(pa, pyname)
+    fields = [f[0] for f in cls._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'    printf("{f} %zu\\n", offsetof({cname}, {f}));\n' for f in fields)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "paged_attn_e4m3.h"\n'
+                   "int main(void) {\n"
+                   f'    printf("sizeof %zu\\n", sizeof({cname}));\n{body}    return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                      text=True).stdout.splitlines())
+    assert int(got["sizeof"]) == ctypes.sizeof(cls)
+    for f in fields:
+        assert int(got[f]) == getattr(cls, f).offset, f

@@ -98,6 +98,47 @@ def test_dense_small(orc, case, kernel):
     gu.assert_parity(got, ref, f"small{case}/{kernel}")
 
 
+# the MFMA kernel's row chunks: a unit's rows cut into workgroups of 16, 32 or
+# 48 rows (ragged last chunks included) give the same function
+CHUNKED = [
+    # (q_rows, H, Hkv, D, ctx, page, lens, splits)
+    (8, 6, 1, 256, 1000, 800, None, 3),                                    # 48 rows
+    (7, 6, 1, 256, 2100, 1000, [2090, 2091, 2092, 2093, 2094, 2095, 2096], 2),   # 42
+    (5, 4, 1, 128, 600, 64, [0, 100, 300, 599, 600], 4),                  # 20 rows
+    (8, 6, 1, 256, 2500, 848, [2493, 2494, 2495, 2496, 2497, 0, 0, 0], 0),  # empty chunk
+]
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 48])
+@pytest.mark.parametrize("case", range(len(CHUNKED)))
+def test_dense_row_chunks(orc, case, chunk):
+    qr, H, Hkv, D, ctx, page, lens, splits = CHUNKED[case]
+    w = wl.make_dense(f"chunk{case}", 0x5EED40 + case, q_rows=qr, num_heads=H, num_kv_heads=Hkv,
+                      head_dim=D, ctx=ctx, page_size=page, pool_pages=-(-ctx // page) + 2,
+                      sigma=1.2, k_scale=0.45, v_scale=1.6, row_lens=lens, num_splits=splits,
+                      poison_tail=True)
+    announce("row_chunks", case, CHUNKED[case], chunk)
+    got = gu.run_dense(w, "mfma", rows_per_workgroup=chunk)
+    gu.assert_parity(got, orc.dense_workload(w), f"chunk{case}/{chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_qsa_row_chunks(orc, chunk):
+    w = wl.make_qsa("qsa_chunk", 0x5EED51, batch=3, q_rows=4, num_heads=12, num_kv_heads=2,
+                    head_dim=128, ctx=1024, page_size=64, topk=6, k_scale=0.5, v_scale=2.0,
+                    num_splits=3)
+    announce("qsa_row_chunks", chunk)
+    got = gu.run_qsa(w, "mfma", rows_per_workgroup=chunk)
+    gu.assert_parity(got, orc.qsa_workload(w), f"qsa_chunk/{chunk}")
+
+
+def test_plan_picks_row_chunks_c1():
+    """The full-size 8K workload runs with 16-row chunks (its parity test above
+    goes through this plan)."""
+    w = wl.cached("c1")
+    assert gu.dense_plan(w, "auto", None).rows_per_workgroup == 16
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_qsa_small_edges(orc, kernel):
     w = wl.make_qsa("qsa_small", 0x5EED50, batch=3, q_rows=4, num_heads=12, num_kv_heads=2,
