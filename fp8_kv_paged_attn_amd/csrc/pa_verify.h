@@ -25,6 +25,10 @@ struct VerifyArgs {
     int64_t token_stride;
     int64_t head_stride;
     int32_t page_size;
+    int32_t chunk_rows;         // rows of a KV unit one MFMA workgroup takes: 16, 32
+                                // or 48 (grid z counts the chunks; ragged: 48); it
+                                // sits in the alignment gap before the table pointer,
+                                // so the other fields keep their offsets
     const int32_t *block_table; // [B][table_stride] (one request: [entries])
     int32_t table_stride;       // entries per request (one dense request: 0)
     const int32_t *sel;         // sparse: [B][Hkv][topk] blocks or token ids; dense: nullptr
@@ -35,8 +39,6 @@ struct VerifyArgs {
                                 // topk*page; tokens: topk)
     int32_t batch, q_rows, num_heads, num_kv_heads, group;  // group = H / Hkv
     int32_t rows;               // rows per KV unit = q_rows * group
-    int32_t chunk_rows;         // rows of a KV unit one MFMA workgroup takes: 16, 32
-                                // or 48 (grid z counts the chunks; ragged: 48)
     int32_t num_splits, tokens_per_split;
     int32_t total_rows;         // rows of the workspace = B * q_rows * H
     float logit_scale;          // sm_scale * k_scale * log2(e)

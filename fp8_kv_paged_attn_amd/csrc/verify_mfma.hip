@@ -30,9 +30,11 @@
 //  * O^T += V^T P^T: V^T fragments come straight from LDS with ds_read_tr8_b64
 //    (the transposing read).  P is split into FP16 hi + lo parts and both are
 //    multiplied ("compensated probabilities", design note first section);
-//    every product is exact in FP32.  A wave's FP32 accumulator is 48 rows x D.
+//    every product is exact in FP32.  A wave's FP32 accumulator is 16 RB rows x
+//    D, RB = 1, 2 or 3 the row blocks of the workgroup's chunk of the unit's
+//    rows (a kernel instance per chunk size: 16, 32 or 48 rows).
 //  * Row blocks (16 rows) in which no row sees any token are skipped: the main
-//    loop is instantiated for 1, 2 or 3 row blocks.
+//    loop is instantiated for 1 .. RB row blocks.
 //  * The running reference max of a row moves only when a block exceeds it by
 //    more than 2^8, so P <= 2^14 in FP16 and accumulator rescales are rare;
 //    the partial written out uses the exact row max.
@@ -402,7 +404,7 @@ constexpr int max_slots()
     return mfma_max_slots(D);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int RB>
 __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, DivMagic dm,
                                                                    DivMagic hm, uint32_t g_magic)
 {
@@ -422,9 +424,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     __shared__ int2v slots[kSlots];                 // (physical page, first token) per slot
     __shared__ __attribute__((aligned(16))) int32_t tok_s[kWaves][2][kSub];   // sparse tokens
     __shared__ int32_t blk_tmax[kWaves][2];         // sparse: last token of an all-valid block
-    __shared__ float xm[kWaves][16 * kRowBlocks];   // merge: per-wave row max
-    __shared__ float xl[kWaves][16 * kRowBlocks];   // merge: per-wave row sum
-    __shared__ float xr[kWaves][16 * kRowBlocks];   // merge: per-wave accumulator reference
+    __shared__ float xm[kWaves][16 * RB];   // merge: per-wave row max
+    __shared__ float xl[kWaves][16 * RB];   // merge: per-wave row sum
+    __shared__ float xr[kWaves][16 * RB];   // merge: per-wave accumulator reference
 
     // The argument block spans four 64-byte scalar-cache lines; one word of
     // each, read at entry, brings them all in with one miss, where reading the
@@ -454,10 +456,10 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     }
     const int b = divp(unit, hm);              // unit / num_kv_heads
     const int kvh = unit - b * a.num_kv_heads;
-    // the rows of a KV unit are taken in chunks of 16, 32 or 48 (one workgroup
+    // the rows of a KV unit are taken in chunks of 16 RB rows (one workgroup
     // each, grid z): this one takes rows row0 .. row0 + R - 1 of the unit
-    const int row0 = blockIdx.z * a.chunk_rows;
-    const int R = min(a.rows - row0, a.chunk_rows), G = a.group;
+    const int row0 = blockIdx.z * (16 * RB);
+    const int R = min(a.rows - row0, 16 * RB), G = a.group;
     // row / G for a row of the KV unit (row < rows <= 96, G <= rows, so
     // row * G < 2^16): (row * g_magic) >> 16 with g_magic = ceil(2^16 / G)
     // (from the host) is exact, one 24-bit multiply and a shift where a
@@ -685,9 +687,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     asm volatile("" : "+v"(lraw));
     const int lmine = clamp_len(lraw);
     lmax = max16_broadcast(lmine);
-    int lrow[kRowBlocks];
+    int lrow[RB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int r = rb * 16 + n;
         const int lr = __shfl(lmine, r < R ? div_g(row0 + r) : 0, 64);
         lrow[rb] = r < R ? lr : 0;
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // row blocks up to the last one with a row that sees a token
     int nrb = 1;
 #pragma unroll
-    for (int rb = 1; rb < kRowBlocks; ++rb)
+    for (int rb = 1; rb < RB; ++rb)
         if (__any(lrow[rb] > 0))
             nrb = rb + 1;
     if (!SPARSE)
@@ -706,9 +708,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // is processed without masks; rows that see nothing of the split are reset
     // to the empty state at the end.
     // Dense blocks are never unmasked past hi, where the K bytes may be NaN.
-    int minl[kRowBlocks];
+    int minl[RB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         int v = SPARSE ? INT32_MAX : hi;
         if (rb * 16 + n < R && lrow[rb] > (SPARSE ? 0 : lo))
             v = SPARSE ? lrow[rb] : min(lrow[rb], hi);
@@ -749,9 +751,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // 64t + 16g + 8e .. +7 (16-byte chunk 8t + 2g + e of the row), so that one
     // 16-byte LDS chunk of K (dims 64t + 16g .. +15) feeds two consecutive
     // k-blocks.
-    QFrag qf[kRowBlocks][C::KB];
+    QFrag qf[RB][C::KB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const int r = rb * 16 + n;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
@@ -769,17 +771,17 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     const int nms = hi > lo ? (hi - lo + kMacro - 1) / kMacro : 0;
 
     // ---- per-wave state ------------------------------------------------------
-    f32x4 acc[kRowBlocks][C::DB];
+    f32x4 acc[RB][C::DB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int d = 0; d < C::DB; ++d)
             acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_true[kRowBlocks], m_ref[kRowBlocks], l_part[kRowBlocks];
+    float m_true[RB], m_ref[RB], l_part[RB];
     // per row block, (d-block, k) pairs of this lane whose row saw a NaN V byte
-    uint64_t nan_hit[kRowBlocks];
+    uint64_t nan_hit[RB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         m_true[rb] = -INFINITY;
         m_ref[rb] = -INFINITY;
         l_part[rb] = 0.0f;
@@ -1091,12 +1093,21 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     if (nms > 0) {
         bcur = lookup(0);
         issue_plane(bcur, 0, a.k_pool, k_st, nullptr);
-        if (nrb == 1)
+        if constexpr (RB == 1) {
             main_loop(std::integral_constant<int, 1>());
-        else if (nrb == 2)
-            main_loop(std::integral_constant<int, 2>());
-        else
-            main_loop(std::integral_constant<int, 3>());
+        } else if constexpr (RB == 2) {
+            if (nrb == 1)
+                main_loop(std::integral_constant<int, 1>());
+            else
+                main_loop(std::integral_constant<int, 2>());
+        } else {
+            if (nrb == 1)
+                main_loop(std::integral_constant<int, 1>());
+            else if (nrb == 2)
+                main_loop(std::integral_constant<int, 2>());
+            else
+                main_loop(std::integral_constant<int, 3>());
+        }
     }
 
     // ---- merge the four waves' states and write the split's partial --------
@@ -1108,7 +1119,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // rows that see no token of this split may have accumulated values in
     // blocks processed without masks: they get the empty state
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         if (lrow[rb] <= (SPARSE ? 0 : lo)) {
             m_true[rb] = -INFINITY;
             m_ref[rb] = -INFINITY;
@@ -1118,11 +1129,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // NaN V bytes seen by a row (rare; only blocks not seen whole record them)
     bool any_nan = false;
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
         any_nan = any_nan || nan_hit[rb] != 0;
     if (__builtin_expect(__any(any_nan), 0)) {
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int d = 0; d < C::DB; ++d) {
                 f32x4 x = acc[rb][d];
@@ -1132,9 +1143,9 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
                 acc[rb][d] = x;
             }
     }
-    float lw[kRowBlocks];
+    float lw[RB];
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
         lw[rb] = sum_over_groups(l_part[rb]);
     // Chunk c (1 KB) of wave v's private merge area.  The wave's own loads
     // are done (the wait above), and no other wave writes there, so it
@@ -1148,7 +1159,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
     // per wave and row: running max, accumulator reference and row sum
     if (g == 0) {
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             xm[w][rb * 16 + n] = m_true[rb];
             xr[w][rb * 16 + n] = m_ref[rb];
             xl[w][rb * 16 + n] = lw[rb];
@@ -1160,11 +1171,11 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
             continue;
         const int qi = q < w ? q : q - 1;    // this quarter among the wave's three
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
             if (rb < nrb)     // row blocks past nrb were never accumulated: zero
 #pragma unroll
                 for (int d = 0; d < C::DQ; ++d)
-                    *(f32x4 *)(xchunk(w, (qi * kRowBlocks + rb) * C::DQ + d) + lane * 16) =
+                    *(f32x4 *)(xchunk(w, (qi * RB + rb) * C::DQ + d) + lane * 16) =
                         acc[rb][q * C::DQ + d];
     }
     __syncthreads();
@@ -1185,7 +1196,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
         if (q != w)
             continue;
 #pragma unroll
-        for (int rb = 0; rb < kRowBlocks; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             const int r = rb * 16 + n;
             // the three foreign partials of this quarter: all LDS reads first
             f32x4 xs[kWaves - 1][C::DQ];
@@ -1197,7 +1208,7 @@ __global__ __launch_bounds__(kThreads, 1) void verify_mfma_kernel(VerifyArgs a, 
 #pragma unroll
                     for (int d = 0; d < C::DQ; ++d)
                         xs[vi][d] = *(const f32x4 *)(
-                            xchunk(v, (qi * kRowBlocks + rb) * C::DQ + d) + lane * 16);
+                            xchunk(v, (qi * RB + rb) * C::DQ + d) + lane * 16);
                 }
             }
             float mv[kWaves], rv[kWaves], lv[kWaves];
@@ -1258,8 +1269,8 @@ DivMagic make_magic(int d)
     return dm;
 }
 
-template <int D, int MODE>
-hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
+template <int D, int MODE, int RB>
+hipError_t launch_rb(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
 {
     // every split's page slots (token ids: positions) must fit the LDS slot cache
     if (mfma_slots_needed(a.tokens_per_split, a.page_size, MODE == kModeTokens) > max_slots<D>())
@@ -1269,10 +1280,23 @@ hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *e
     dim3 grid(a.num_splits, a.ragged ? 1 : a.batch * a.num_kv_heads,
               (a.rows + a.chunk_rows - 1) / a.chunk_rows);
     const uint32_t g_magic = (65536u + (uint32_t)a.group - 1u) / (uint32_t)a.group;
-    hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream,
+    hipExtLaunchKernelGGL((verify_mfma_kernel<D, MODE, RB>), grid, dim3(kThreads), 0, stream,
                           ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, 0, a,
                           make_magic(a.page_size), make_magic(a.num_kv_heads), g_magic);
     return hipGetLastError();
+}
+
+// One instance per row-chunk size, so that a chunk of 16 or 32 rows carries
+// no code or registers for the row blocks it never has.
+template <int D, int MODE>
+hipError_t launch_t(const VerifyArgs &a, hipStream_t stream, const hipEvent_t *ev)
+{
+    switch (a.chunk_rows) {
+    case 16: return launch_rb<D, MODE, 1>(a, stream, ev);
+    case 32: return launch_rb<D, MODE, 2>(a, stream, ev);
+    case 16 * kRowBlocks: return launch_rb<D, MODE, kRowBlocks>(a, stream, ev);
+    default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace
