@@ -343,6 +343,7 @@ def sweep_entry(name: str, kv_bytes: int, plan, m: dict, **extra) -> dict:
     gb = lambda us: round(kv_bytes / (us * 1e-6) / 1e9, 1)
     return {"workload": name, **extra, "kv_bytes": kv_bytes, "splits": plan.num_splits,
             "tokens_per_split": plan.tokens_per_split,
+            "rows_per_workgroup": plan.rows_per_workgroup,
             "us_per_call": round(m["us"], 3), "gbs": gb(m["us"]),
             "us_per_call_pcts": m["pcts"],
             "verify_us": round(m["verify_us"], 3), "verify_gbs": gb(m["verify_us"]),
@@ -726,7 +727,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "ctx": w.max_tokens, "page_size": w.page_size, "kv_bytes": w.kv_bytes(),
                    "splits": plan.num_splits, "tokens_per_split": plan.tokens_per_split,
-                   "kernel": kernel_name, "cache": f"cold: {n_copies} rotating pool copies",
+                   "rows_per_workgroup": plan.rows_per_workgroup, "kernel": kernel_name, "cache": f"cold: {n_copies} rotating pool copies",
                    "us_per_call": round(m["us"], 3), "timing": "HIP graph of 10 verify + combine calls, replayed",
                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
         "hot": {"us_per_call": round(m["hot_us"], 3),
