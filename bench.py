@@ -651,7 +651,7 @@ def main():
     sweep = []
     if not args.no_sweep:
         steps = max(20, args.steps // 2)
-        for name in ["c1", "c2_64k", "c2_128k"]:
+        for name in ["c1", "c2_16k", "c2_32k", "c2_64k", "c2_128k"]:
             log(f"[bench] sweep {name}")
             ws = wl.cached(name)
             bs = DenseBench(ws, copies_for(ws.kv_bytes()), args.kernel, 0)

@@ -576,7 +576,7 @@ def config_c1() -> DenseWorkload:
 
 
 def config_c2(ctx: int) -> DenseWorkload:
-    """C1's shape at 64K/128K; pool of 2x pages; 3 K channels x8 larger."""
+    """C1's shape at 16K-128K; pool of 2x pages; 3 K channels x8 larger."""
     n_log = -(-ctx // 3296)
     return make_dense(f"c2_q8_ctx{ctx}_page3296", BASE_SEED + 2, q_rows=8, num_heads=6,
                       num_kv_heads=1, head_dim=256, ctx=ctx, page_size=3296,
@@ -625,6 +625,8 @@ def cached(name: str):
 CONFIGS: Dict[str, object] = {
     "c0": config_c0,
     "c1": config_c1,
+    "c2_16k": lambda: config_c2(16384),
+    "c2_32k": lambda: config_c2(32768),
     "c2_64k": lambda: config_c2(65536),
     "c2_128k": lambda: config_c2(131072),
     "c3": config_c3,

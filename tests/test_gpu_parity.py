@@ -36,7 +36,7 @@ def announce(*what):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("kernel", KERNELS)
-@pytest.mark.parametrize("name", ["c0", "c1", "c2_64k", "c2_128k", "c3"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2_16k", "c2_32k", "c2_64k", "c2_128k", "c3"])
 def test_dense_config(orc, name, kernel):
     w = wl.cached(name)
     announce(name, kernel)
