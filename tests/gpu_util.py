@@ -141,7 +141,8 @@ def run_qsa(w, kernel="auto", splits: Optional[int] = None, return_ws=False,
     return res
 
 
-def run_qsa_tokens(w, kernel="auto", splits: Optional[int] = None, k_pool=None, v_pool=None):
+def run_qsa_tokens(w, kernel="auto", splits: Optional[int] = None, k_pool=None, v_pool=None,
+                   rows_per_workgroup: Optional[int] = None):
     """Token-id selection batch through qsa_sparse_verify_tokens_e4m3 + combine."""
     q = bf16_tensor(w.q_bits).to(DEV)
     k = torch.from_numpy(w.k_pool if k_pool is None else k_pool).to(DEV)
@@ -153,6 +154,8 @@ def run_qsa_tokens(w, kernel="auto", splits: Optional[int] = None, k_pool=None, 
     s = w.num_splits if splits is None else splits
     p = pa.plan(w.num_sel, w.q_rows * G, w.batch * w.num_kv_heads, w.head_dim, w.page_size,
                 "tokens", splits=s, kernel=kernel)
+    if rows_per_workgroup is not None:
+        p.rows_per_workgroup = rows_per_workgroup
     out = pa.qsa_verify_tokens(q, k, v, bt, sel, lens, sm_scale=w.sm_scale, k_scale=w.k_scale,
                                v_scale=w.v_scale, p=p)
     torch.cuda.synchronize()

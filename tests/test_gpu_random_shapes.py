@@ -3,7 +3,8 @@
 Each case draws a shape the boundary accepts -- grouped heads, head dim 128 or
 256, page sizes from 1 token to several thousand (multiples of 32 and not),
 contexts up to a few thousand tokens, causal or arbitrary row lengths (zero,
-past the capacity, negative), planner-chosen or requested split counts -- for
+past the capacity, negative), planner-chosen or requested split counts, and
+for the MFMA kernel the plan's row chunk or a forced one of 16, 32 or 48 rows -- for
 the dense verify of one request, the ragged batch of independent requests and
 the sparse verify over selected blocks and over selected token ids, and checks the output against the FP64
 oracle at the usual bar (rel-L2 <= 5e-4, max-abs <= 4x the FP16 rounding
@@ -122,6 +123,15 @@ def tokens_case(i: int):
 N_DENSE, N_BATCH, N_QSA, N_TOKENS = 80, 40, 40, 24
 
 
+def row_chunk(kind: int, i: int, kernel: str):
+    """Rows per MFMA workgroup for case i: the plan's (None) or 16, 32 or 48
+    forced (drawn from a stream of its own, so the shapes do not change)."""
+    if kernel != "mfma":
+        return None
+    r = int(np.random.default_rng(0xC4C0 + 1000 * kind + i).choice([0, 16, 32, 48]))
+    return r or None
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("i", range(N_DENSE))
 def test_random_dense(orc, i, kernel):
@@ -129,7 +139,9 @@ def test_random_dense(orc, i, kernel):
     announce("random dense", i, kernel, {k: v for k, v in args.items() if k != "row_lens"},
              "lens", args["row_lens"])
     w = wl.make_dense(f"rnd_dense{i}", 0xD5E000 + i, **args)
-    got = gu.run_dense(w, kernel)
+    rpw = row_chunk(0, i, kernel)
+    announce("rows per workgroup", rpw)
+    got = gu.run_dense(w, kernel, rows_per_workgroup=rpw)
     gu.assert_parity(got, orc.dense_workload(w), f"random dense {i}/{kernel}")
 
 
@@ -151,7 +163,9 @@ def test_random_qsa(orc, i, kernel):
     announce("random qsa", i, kernel, {k: v for k, v in args.items() if k != "row_lens"},
              "lens", None if args["row_lens"] is None else args["row_lens"].tolist())
     w = wl.make_qsa(f"rnd_qsa{i}", 0x05A000 + i, **args)
-    got = gu.run_qsa(w, kernel)
+    rpw = row_chunk(1, i, kernel)
+    announce("rows per workgroup", rpw)
+    got = gu.run_qsa(w, kernel, rows_per_workgroup=rpw)
     gu.assert_parity(got, orc.qsa_workload(w), f"random qsa {i}/{kernel}")
 
 
@@ -163,5 +177,7 @@ def test_random_qsa_tokens(orc, i, kernel):
              {k: v for k, v in args.items() if k != "row_lens"},
              "lens", None if args["row_lens"] is None else args["row_lens"].tolist())
     w = wl.make_qsa_tokens(f"rnd_tok{i}", 0x70C000 + i, **args)
-    got = gu.run_qsa_tokens(w, kernel)
+    rpw = row_chunk(2, i, kernel)
+    announce("rows per workgroup", rpw)
+    got = gu.run_qsa_tokens(w, kernel, rows_per_workgroup=rpw)
     gu.assert_parity(got, orc.qsa_tokens_workload(w), f"random qsa tokens {i}/{kernel}")
