@@ -533,31 +533,42 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
         int64_t want = (cus + wgs - 1) / wgs;
         // ... but no split shorter than kMinTokensPerSplit tokens
         sh = shape_for(want < min_cap ? want : min_cap);
-        // A short list leaves each workgroup one 128-token step (one block
-        // per wave) and a fixed cost of the same order.  Smaller row chunks
-        // then put more compute units on the list, with longer splits and
-        // less work per token each (the chunks of a split read the same K/V,
-        // mostly from L2): 16 rows, else 32, when that fills at most every
-        // compute unit with splits of at most 256 tokens.  (MI355X, q8 rows
-        // of six heads: at 8K tokens 48-row chunks took 14.8 us per call, 16
-        // rows 11.6; at 32K 20.7 against 16.3 with 32 rows; at 64K and up,
-        // where a 48-row workgroup already has two steps or more, smaller
-        // chunks were slower.)
-        if (sh.tps <= kChunkStepTokens) {
-            for (int64_t c : {(int64_t)16, (int64_t)32}) {
+        // A short list leaves each 48-row workgroup fewer than two 128-token
+        // steps (at most one block per wave, some waves idle) beside a fixed
+        // cost of the same order.  Smaller row chunks then put more compute
+        // units on the list, with longer splits and less work per token each
+        // (the chunks of a split read the same K/V, mostly from L2): 16 rows
+        // with splits of at most three steps, else 32 rows with at most four,
+        // within one workgroup per compute unit.  (MI355X, q8 rows of six
+        // heads, per call: 8K 14.8 us at 48 rows against 11.5 at 16; 24K 18.8
+        // against 14.7 at 16; 48K 21.4 against 17.7 at 32.  From two steps
+        // on, at 64K and up, 48 rows gave the faster verify kernel.)  The
+        // count of (split, unit) pairs is kept a multiple of 8, so that the
+        // chunks of a pair, whose workgroup ids differ by a multiple of it,
+        // run on one XCD and share its L2 (79 splits instead of 64 at 64K
+        // took 23.8 against 21.6 us per call).
+        if (sh.tps < 2 * kChunkStepTokens) {
+            const int64_t chunk_rows[2] = {16, 32}, max_steps[2] = {3, 4};
+            bool found = false;
+            for (int k = 0; k < 2 && !found; ++k) {
+                const int64_t c = chunk_rows[k];
                 if (rows_per_kv_unit <= c)
                     continue;   // one chunk of the unit either way
                 const int64_t per = (int64_t)num_kv_units * (((int64_t)rows_per_kv_unit + c - 1) / c);
                 int64_t w = cus / per;
                 if (w > min_cap)
                     w = min_cap;
-                if (w < 1)
-                    continue;
-                const Shape sc = shape_for(w);
-                if (sc.splits * per <= cus && sc.tps <= 2 * kChunkStepTokens) {
-                    sh = sc;
-                    chunk = c;
-                    break;
+                for (; w >= 1; --w) {
+                    const Shape sc = shape_for(w);
+                    if (sc.tps > max_steps[k] * kChunkStepTokens)
+                        break;   // fewer splits only make them longer
+                    const int64_t pairs = sc.splits * num_kv_units;
+                    if (sc.splits * per <= cus && (pairs % 8 == 0 || pairs < 8)) {
+                        sh = sc;
+                        chunk = c;
+                        found = true;
+                        break;
+                    }
                 }
             }
         }

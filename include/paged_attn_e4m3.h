@@ -182,10 +182,12 @@ typedef struct pa_workspace {
  * but no split shorter than 128 tokens, so that the FP32 partial each split
  * writes stays small against its K/V bytes (the pages tune split counts per
  * device and region, [QSA] sm_120 retune commit).  When that leaves each
- * workgroup a single 128-token step (short lists), the rows of a unit are cut
- * finer (rows_per_workgroup 16, else 32) if that still fills at most num_cus
- * workgroups with splits of at most 256 tokens: more compute units read the
- * list, and each does less per token.  A requested count keeps 48-row chunks.
+ * workgroup fewer than two 128-token steps (short lists), the rows of a unit
+ * are cut finer (rows_per_workgroup 16, else 32) if that still fills at most
+ * num_cus workgroups, with splits of at most 3 steps (16 rows) or 4 (32 rows)
+ * and a count of (split, unit) pairs that is a multiple of 8: more compute
+ * units read the list, each does less per token, and the chunks of a split
+ * run on one XCD.  A requested count keeps 48-row chunks.
  * Either count is then
  * clamped to what the token count allows and raised where a split would
  * otherwise cover more pages (token ids: entries) than the MFMA kernel keeps

@@ -85,15 +85,18 @@ def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
     ch = p.rows_per_workgroup
     assert ch in (16, 32, 48)
     if ch != 48:
-        # finer row chunks only for short lists (one 128-token step per
-        # 48-row workgroup), at most one workgroup per compute unit, splits of
-        # at most 256 tokens, and only where they cut a unit into more chunks
+        # finer row chunks only for short lists (fewer than two 128-token
+        # steps per 48-row workgroup), at most one workgroup per compute unit,
+        # splits of at most 3 steps (16 rows) or 4 (32 rows), a split count
+        # that keeps the (split, unit) pairs a multiple of 8 (or below 8), and
+        # only where they cut a unit into more chunks
         c = cus if cus > 0 else 256
         assert not req and rows > ch
-        assert S * units * -(-rows // ch) <= c and T <= 256
+        assert S * units * -(-rows // ch) <= c and T <= (384 if ch == 16 else 512)
+        assert (S * units) % 8 == 0 or S * units < 8
         p48 = -(-tiles // min(max(1, -(-c // (units * -(-rows // 48)))),
                               max(1, -(-max_tokens // 128)))) * 64
-        assert p48 <= 128
+        assert p48 < 256
         assert (p.ws_acc_bytes, p.ws_stat_bytes) == (S * rows * units * D * 4, S * rows * units * 4)
         return
     # the slot cap only ever raises the count: the uncapped rule's count is a lower bound
@@ -130,8 +133,10 @@ def test_plan_counts_row_chunks(L):
 @pytest.mark.parametrize("max_tokens,rows,units,req,expect", [
     (8192, 48, 1, 0, (64, 128, 16)),      # 3 chunks x 64 splits = 192 workgroups
     (16384, 48, 1, 0, (64, 256, 16)),     # 16-row chunks with two steps per split
+    (24576, 48, 1, 0, (64, 384, 16)),     # 77 splits of 320 would split pairs over XCDs
     (32768, 48, 1, 0, (128, 256, 32)),    # 16 rows would need 448-token splits
-    (49152, 48, 1, 0, (256, 192, 48)),    # finer chunks would need splits of 384+
+    (49152, 48, 1, 0, (128, 384, 32)),    # 48 rows: 192-token splits, under two steps
+    (53248, 48, 1, 0, (208, 256, 48)),    # two steps per 48-row workgroup
     (65536, 48, 1, 0, (256, 256, 48)),    # two steps per 48-row workgroup already
     (8192, 48, 1, 64, (64, 128, 48)),     # a requested count keeps 48-row chunks
     (8192, 12, 1, 0, (64, 128, 48)),      # one chunk of 16 rows either way
