@@ -143,8 +143,10 @@ typedef struct pa_plan {
     int64_t ws_index_bytes;        /* int32 [num_kv_units + 1] (PA_SEL_BATCH), else 0 */
     int32_t rows_per_workgroup;    /* rows of a KV unit one MFMA workgroup takes: 16, 32
                                       or 48 (0 reads as 48); PA_SEL_BATCH: 48.  The
-                                      workspace and the results do not depend on it;
-                                      the plain kernel always takes 48 */
+                                      workspace layout does not depend on it; the values
+                                      may differ in FP32 rounding (a row block's lazy
+                                      reference max follows all of its rows).  The plain
+                                      kernel always takes 48 */
 } pa_plan;
 
 /* (host) FP32 split workspace written by the verify entry points and read by
