@@ -527,10 +527,13 @@ int32_t paged_attn_plan(int32_t max_tokens, int32_t rows_per_kv_unit, int32_t nu
     if (requested_splits > 0) {
         sh = shape_for(requested_splits);
     } else {
-        // one workgroup per compute unit over all units, a unit of more than
-        // 48 rows taking one workgroup per 48-row chunk ...
+        // at most one workgroup per compute unit over all units, a unit of
+        // more than 48 rows taking one workgroup per 48-row chunk (a count
+        // rounded up would leave a few workgroups for a second round: three
+        // KV heads at 64K with 86 splits, 258 workgroups, took 49.8 us per
+        // call against 32.4 with 79) ...
         const int64_t wgs = (int64_t)num_kv_units * (((int64_t)rows_per_kv_unit + 47) / 48);
-        int64_t want = (cus + wgs - 1) / wgs;
+        int64_t want = cus / wgs > 1 ? cus / wgs : 1;
         // ... but no split shorter than kMinTokensPerSplit tokens
         sh = shape_for(want < min_cap ? want : min_cap);
         // A short list leaves each 48-row workgroup fewer than two 128-token

@@ -179,7 +179,7 @@ typedef struct pa_workspace {
  * num_cus = compute units to fill; <= 0 takes the current device's count
  * (queried once per device and kept), or 256 (the MI355X count) when no
  * device can be queried.  requested_splits > 0 asks for that split count; 0
- * picks one: one workgroup per compute unit over all units (a unit of more
+ * picks one: at most one workgroup per compute unit over all units (a unit of more
  * than 48 rows counts once per 48-row chunk, each chunk being a workgroup),
  * but no split shorter than 128 tokens, so that the FP32 partial each split
  * writes stays small against its K/V bytes (the pages tune split counts per

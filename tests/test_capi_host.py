@@ -94,7 +94,7 @@ def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
         assert not req and rows > ch
         assert S * units * -(-rows // ch) <= c and T <= (384 if ch == 16 else 512)
         assert (S * units) % 8 == 0 or S * units < 8
-        p48 = -(-tiles // min(max(1, -(-c // (units * -(-rows // 48)))),
+        p48 = -(-tiles // min(max(1, c // (units * -(-rows // 48))),
                               max(1, -(-max_tokens // 128)))) * 64
         assert p48 < 256
         assert (p.ws_acc_bytes, p.ws_stat_bytes) == (S * rows * units * D * 4, S * rows * units * 4)
@@ -104,7 +104,7 @@ def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
         want = min(req, tiles)
     else:
         c = cus if cus > 0 else 256
-        want = min(max(1, -(-c // (units * -(-rows // 48)))), max(1, -(-max_tokens // 128)))
+        want = min(max(1, c // (units * -(-rows // 48))), max(1, -(-max_tokens // 128)))
     T0 = -(-tiles // want) * 64
     S0 = max(1, -(-max_tokens // T0))
     assert S >= S0
@@ -121,6 +121,17 @@ def test_plan_rules(L, max_tokens, rows, units, D, page, sel, cus, req):
     assert p.ws_acc_bytes == S * rows * units * D * 4
     assert p.ws_stat_bytes == S * rows * units * 4
     assert p.kernel == 0
+
+
+@pytest.mark.parametrize("units", [1, 2, 3, 5, 6, 7, 8, 32, 255, 256])
+def test_plan_fills_at_most_one_round(L, units):
+    """Planner-chosen counts never put more workgroups than compute units
+    (while one split per unit fits): a few left over would run as a second
+    round and double the call."""
+    for ctx in (8192, 65536, 131072, 262144):
+        p = pa.plan(ctx, 48, units, 256, 3296, num_cus=256)
+        chunks = -(-48 // p.rows_per_workgroup)
+        assert p.num_splits * units * chunks <= 256, (ctx, units, p)
 
 
 def test_plan_counts_row_chunks(L):
